@@ -1,0 +1,251 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * Three calls make one decode step (or one prefill) of DeepSeek Sparse
+ * Attention, as the method is described on the pages
+ *   "DeepSeek fixes RoPE mismatch in the V3.2-Exp inference demo"
+ *   "DeepSeek-V3.2-Exp . RoPE coefficients"
+ *   "DeepSeek-V3.2-Exp -- Sparse latent attention"
+ *   "DeepSeek-V3.2-Exp . Rotate first features"
+ *   "DeepSeek-V3.2-Exp . Similarities"
+ *
+ *   dsa_indexer     lightning-indexer score on block-FP8 q and k with
+ *                   non-interleaved RoPE (also appends the new keys)
+ *   dsa_topk        per-query causal top-k selection (up to 2048 positions)
+ *   dsa_sparse_mla  sparse latent attention in absorbed (MQA) form
+ *
+ * plus dsa_rope_table, which builds the rotary table the indexer reads.
+ *
+ * Conventions shared by every call:
+ *  - Every pointer in an args struct is a DEVICE pointer unless stated.
+ *    The caller owns every buffer; the library allocates nothing, frees
+ *    nothing, keeps no state between calls and never synchronises.
+ *  - Work is enqueued on `stream` in order; results are ready when the
+ *    stream reaches the end of the call's work. Calls on one stream see each
+ *    other's results in order.
+ *  - All arguments are validated on the host before anything is launched;
+ *    on any error nothing is launched and no memory is touched. Values that
+ *    live in device memory (positions, indices) cannot be checked on the
+ *    host: the kernels bound-check them instead and treat an out-of-range
+ *    position as an empty row and an out-of-range index as "not selected".
+ *  - dsa_status 0 means success. A failed launch reports DSA_ERR_HIP.
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  - bf16 data is passed as uint16 bit patterns.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* Fixed head geometry (page "Sparse latent attention": 64 indexer heads of
+ * 128 features, one shared 128-feature key per position, a 512-feature
+ * latent plus a 64-feature rotary key cached per position). */
+#define DSA_INDEX_DIM 128     /* indexer head dim; also the FP8 block size */
+#define DSA_INDEX_ROPE 64     /* rotated features of an indexer row */
+#define DSA_MAX_INDEX_HEADS 64
+#define DSA_LATENT_DIM 512
+#define DSA_ROPE_DIM 64
+#define DSA_MAX_ATTN_HEADS 128
+#define DSA_MAX_TOPK 2048
+
+typedef enum dsa_status {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    DSA_ERR_SHAPE = 2,       /* a size or stride is out of its range */
+    DSA_ERR_UNSUPPORTED = 3, /* unknown dtype or flag */
+    DSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    DSA_ERR_ALIGN = 5,       /* a pointer or stride is not 16-byte aligned */
+    DSA_ERR_HIP = 6          /* a HIP launch failed */
+} dsa_status;
+
+enum { DSA_DTYPE_F32 = 0, DSA_DTYPE_BF16 = 1 };
+
+/* dsa_indexer_args.flags */
+#define DSA_INDEXER_APPEND_ONLY 1u  /* run step 1 only: append keys, no scores */
+
+/* ------------------------------------------------------------------------
+ * Rotary table. Page "RoPE coefficients" (precompute_freqs_cis excerpt):
+ * theta_i = theta^(-2i/64) for i < 32 in float32; with yarn != 0 the YaRN
+ * blend theta_i/factor*(1-smooth_i) + theta_i*smooth_i, smooth = 1 - ramp,
+ * with the ramp and correction range of the YaRN paper (Peng et al. 2023)
+ * over [low, high] from beta_fast/beta_slow and orig_len. Entry [p][i] is
+ * (cos, sin) of the float32 product p*theta_i, rounded to float32.
+ * Output: cos_out, sin_out float32 [P][32], row-major.
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_rope_table_args {
+    int32_t P;          /* positions, >= 1 */
+    int32_t yarn;       /* 0: plain frequencies, 1: YaRN blend */
+    int32_t orig_len;   /* original training length (YaRN only), >= 1 */
+    float theta;        /* rotary base, > 1 */
+    float factor;       /* YaRN interpolation factor, >= 1 */
+    float beta_fast;    /* YaRN ramp bounds, beta_fast > beta_slow > 0 */
+    float beta_slow;
+    float* cos_out;     /* [P][32] */
+    float* sin_out;     /* [P][32] */
+} dsa_rope_table_args;
+
+dsa_status dsa_rope_table(const dsa_rope_table_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Call 1: lightning-indexer score.
+ * Pages: the aipricedb digest's indexer formula
+ *   I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]);
+ * "Sparse latent attention", equation S^I; "Rotate first features"
+ * (Indexer.forward: non-interleaved RoPE on the first 64 of 128 features in
+ * float32, cast back to the input type, block-FP8 quantisation with one
+ * float32 scale per 128-element block, keys written to the cache before
+ * scoring). The Hadamard rotation the pages apply before quantisation is not
+ * part of this call (it leaves exact scores unchanged).
+ *
+ * Per query row r = (b, s) at position p = pos[b][s]:
+ *  1. if k_raw != NULL: key row k_raw[b][s] is rotated with table row p,
+ *     rounded to the activation dtype, quantised, and written to
+ *     k_cache[b][p] / k_scale[b][p];
+ *  2. the H query rows q_raw[b][s][h] are rotated with row p, rounded,
+ *     quantised (to q_fp8/q_scale when given, else to the workspace);
+ *  3. for every key 0 <= s' <= p (n_valid = p + 1):
+ *       scores[r][s'] = k_scale[b][s'] * sum_h w[r][h] * q_scale[r][h] *
+ *                       ReLU(sum_d q8[r][h][d] * k8[b][s'][d])
+ *     with q8/k8 the E4M3 code values; entries s' > p are not written.
+ * w carries every constant factor (H^-0.5, the 128^-0.5 score scale): the
+ * call applies none.
+ * Codes: OCP E4M3 (max 448), round to nearest even, saturating; scale =
+ * amax/448 (float32 division), 1 for an all-zero row.
+ *
+ * Layouts (row-major, contiguous):
+ *   q_raw   [B][S][H][128]  act_dtype         k_raw  [B][S][128] act_dtype
+ *   pos     [B][S] int32                      w      [B][S][H] float32
+ *   rope_cos/rope_sin [P][32] float32 (dsa_rope_table's output)
+ *   k_cache [B][Lmax][128] uint8 (in/out)     k_scale [B][Lmax] float32 (in/out)
+ *   q_fp8   [B][S][H][128] uint8 (out, optional)
+ *   q_scale [B][S][H] float32 (out, optional; given iff q_fp8 is)
+ *   scores  row r at scores + r*ld_scores, float32, ld_scores >= Lmax
+ * Limits: 1 <= H <= 64, B, S >= 1, 1 <= Lmax, P >= 1. A row whose position
+ * lies outside [0, min(Lmax, P)) is skipped (nothing appended or scored).
+ * With S > 1 every row's key is appended before any row is scored, so a
+ * prefill row sees the keys of earlier rows of the same call. Rows of one
+ * batch row must have distinct positions (their cache rows are written
+ * concurrently).
+ * flags: 0, or DSA_INDEXER_APPEND_ONLY to run step 1 alone (fills the key
+ * cache, the pages' k_cache/k_scale_cache write); then k_raw is required and
+ * q_raw, w, q_fp8, q_scale, scores and the workspace are ignored (may be
+ * NULL).
+ * Workspace: dsa_indexer_workspace() bytes, 256-byte aligned; 0 when both
+ * q_fp8 and q_scale are given.
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_indexer_args {
+    int32_t B, S, H, Lmax, P;
+    int32_t act_dtype;           /* DSA_DTYPE_F32 or DSA_DTYPE_BF16 */
+    const void* q_raw;
+    const void* k_raw;           /* NULL: append nothing */
+    const int32_t* pos;
+    const float* rope_cos;
+    const float* rope_sin;
+    const float* w;
+    uint8_t* k_cache;
+    float* k_scale;
+    uint8_t* q_fp8;              /* optional */
+    float* q_scale;              /* optional */
+    float* scores;
+    int64_t ld_scores;
+    uint32_t flags;              /* 0 or DSA_INDEXER_APPEND_ONLY */
+    void* workspace;
+    size_t workspace_bytes;
+} dsa_indexer_args;
+
+dsa_status dsa_indexer_workspace(const dsa_indexer_args* args, size_t* bytes);
+dsa_status dsa_indexer(const dsa_indexer_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Call 2: causal top-k. Pages: "Sparse latent attention" (a lightning
+ * indexer chooses up to 2,048 positions per query; selection mask over
+ * top_2048 of the causally masked score); "Rotate first features"
+ * (topk(min(index_topk, end_pos))).
+ * Row r = (b, s) has n_valid = pos[b][s] + 1 candidates scores[r][0..n_valid)
+ * (0 when the position is outside [0, Lmax)). It selects
+ * k_eff = min(K, n_valid) positions under the order (score descending,
+ * position ascending) -- equal scores keep the lower position; -0.0 and
+ * +0.0 are equal -- and writes them to idx[r][0..k_eff) in ascending
+ * position order, then -1 in idx[r][k_eff..K). count[r] = k_eff if given.
+ * Scores must be finite (NaN is not ordered).
+ * Layouts: scores row r at scores + r*ld_scores (ld_scores >= Lmax),
+ *   pos [B][S] int32, idx [B][S][K] int32, count [B][S] int32 (optional).
+ * Limits: 1 <= K <= 2048, B, S, Lmax >= 1. Workspace: dsa_topk_workspace().
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_topk_args {
+    int32_t B, S, Lmax, K;
+    const float* scores;
+    int64_t ld_scores;
+    const int32_t* pos;
+    int32_t* idx;
+    int32_t* count;              /* optional */
+    void* workspace;
+    size_t workspace_bytes;
+} dsa_topk_args;
+
+dsa_status dsa_topk_workspace(const dsa_topk_args* args, size_t* bytes);
+dsa_status dsa_topk(const dsa_topk_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Call 3: sparse latent attention, absorbed (MQA) form. Pages:
+ * "Similarities" (MLA decode excerpt: scores = (q_nope_absorbed . kv_cache
+ * + q_pe . pe_cache) * softmax_scale, index mask, softmax, scores .
+ * kv_cache); "Sparse latent attention" (S' = S m^2/sqrt(192), softmax,
+ * O = AV; attention runs over the selected positions alone).
+ * For row r = (b, s) and head h, over the selected positions
+ * p = idx[r][j] with 0 <= p < Lmax (other entries, e.g. -1, are skipped):
+ *   z_j = scale * (q[r][h][0:512] . latent[b][p] + q[r][h][512:576] . rope[b][p])
+ *   out[r][h][:] = sum_j softmax(z)_j * latent[b][p_j]       (bf16)
+ *   lse[r][h]    = log sum_j exp(z_j)                         (float32)
+ * Products and sums in float32; the probabilities are rounded to bf16 for
+ * the value product. A row with no selected position gives out = 0 and
+ * lse = -inf. q's 64 trailing features and the rope cache are used as
+ * given (already rotated by the caller, interleaved pairing).
+ * Layouts: q [B][S][Hq][576] bf16 contiguous; latent row p of batch b at
+ *   latent + b*latent_batch_stride + p*latent_row_stride (elements, 512
+ *   bf16 per row); rope likewise (64 bf16 per row) -- one fused 576-wide
+ *   cache row works by pointing rope at latent + 512; idx [B][S][K] int32;
+ *   out [B][S][Hq][512] bf16; lse [B][S][Hq] float32 (optional).
+ * Limits: 1 <= Hq <= 128, 1 <= K <= 2048, B, S, Lmax >= 1; pointers 16-byte
+ * aligned, strides multiples of 8 elements. scale > 0 and finite.
+ * Workspace: dsa_sparse_mla_workspace() bytes (key-split partial results).
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_mla_args {
+    int32_t B, S, Hq, Lmax, K;
+    const uint16_t* q;
+    const uint16_t* latent;
+    int64_t latent_row_stride;
+    int64_t latent_batch_stride;
+    const uint16_t* rope;
+    int64_t rope_row_stride;
+    int64_t rope_batch_stride;
+    const int32_t* idx;
+    float scale;
+    uint16_t* out;
+    float* lse;                  /* optional */
+    void* workspace;
+    size_t workspace_bytes;
+} dsa_mla_args;
+
+dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* args, size_t* bytes);
+dsa_status dsa_sparse_mla(const dsa_mla_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Helpers.
+ * ---------------------------------------------------------------------- */
+const char* dsa_status_str(dsa_status status);   /* static string, never NULL */
+int dsa_abi_version(void);                       /* DSA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,316 @@
+"""Python binding of libdsa.so, the MI355X (gfx950) DeepSeek Sparse
+Attention hot-path library declared in include/dsa.h.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current HIP stream. The library
+must be built (``python -m sparse_attention_index_amd.build`` or
+``__graft_entry__.build()``); there is no fallback path.
+
+Calls (same names as the C ABI, without the ``dsa_`` prefix):
+    rope_table(P, yarn=..., ...)            -> (cos, sin) float32 [P, 32]
+    indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, k_raw=None, ...)
+                                            -> scores float32 [B, S, Lmax]
+    topk(scores, pos, K)                    -> idx int32 [B, S, K]
+    sparse_mla(q, latent, rope, idx, scale) -> out bf16 [B, S, Hq, 512] (, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK = 0
+DSA_DTYPE_F32 = 0
+DSA_DTYPE_BF16 = 1
+INDEX_DIM = 128
+LATENT_DIM = 512
+ROPE_DIM = 64
+MAX_TOPK = 2048
+APPEND_ONLY = 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class RopeTableArgs(ctypes.Structure):
+    _fields_ = [("P", _i32), ("yarn", _i32), ("orig_len", _i32), ("theta", _f32),
+                ("factor", _f32), ("beta_fast", _f32), ("beta_slow", _f32),
+                ("cos_out", _vp), ("sin_out", _vp)]
+
+
+class IndexerArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("S", _i32), ("H", _i32), ("Lmax", _i32), ("P", _i32),
+                ("act_dtype", _i32), ("q_raw", _vp), ("k_raw", _vp), ("pos", _vp),
+                ("rope_cos", _vp), ("rope_sin", _vp), ("w", _vp), ("k_cache", _vp),
+                ("k_scale", _vp), ("q_fp8", _vp), ("q_scale", _vp), ("scores", _vp),
+                ("ld_scores", _i64), ("flags", ctypes.c_uint32), ("workspace", _vp),
+                ("workspace_bytes", _sz)]
+
+
+class TopkArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("S", _i32), ("Lmax", _i32), ("K", _i32), ("scores", _vp),
+                ("ld_scores", _i64), ("pos", _vp), ("idx", _vp), ("count", _vp),
+                ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class MlaArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("S", _i32), ("Hq", _i32), ("Lmax", _i32), ("K", _i32),
+                ("q", _vp), ("latent", _vp), ("latent_row_stride", _i64),
+                ("latent_batch_stride", _i64), ("rope", _vp), ("rope_row_stride", _i64),
+                ("rope_batch_stride", _i64), ("idx", _vp), ("scale", _f32), ("out", _vp),
+                ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+EXPORTS = ("dsa_rope_table", "dsa_indexer_workspace", "dsa_indexer", "dsa_topk_workspace",
+           "dsa_topk", "dsa_sparse_mla_workspace", "dsa_sparse_mla", "dsa_status_str",
+           "dsa_abi_version")
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def lib():
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_attention_index_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.dsa_status_str.restype = ctypes.c_char_p
+    L.dsa_status_str.argtypes = [ctypes.c_int]
+    L.dsa_abi_version.restype = ctypes.c_int
+    L.dsa_abi_version.argtypes = []
+    for name, st in (("rope_table", RopeTableArgs), ("indexer", IndexerArgs),
+                     ("topk", TopkArgs), ("sparse_mla", MlaArgs)):
+        fn = getattr(L, "dsa_" + name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(st), _vp]
+        if name != "rope_table":
+            ws = getattr(L, f"dsa_{name}_workspace")
+            ws.restype = ctypes.c_int
+            ws.argtypes = [ctypes.POINTER(st), ctypes.POINTER(_sz)]
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != DSA_OK:
+        raise DSAError(code, lib().dsa_status_str(code).decode())
+
+
+def status_str(code: int) -> str:
+    return lib().dsa_status_str(code).decode()
+
+
+def _stream():
+    import torch
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------- calls --
+
+def rope_table(P: int, yarn: bool = False, theta: float = 10000.0, orig_len: int = 4096,
+               factor: float = 40.0, beta_fast: float = 32.0, beta_slow: float = 1.0,
+               device="cuda"):
+    import torch
+    cos = torch.empty((P, ROPE_DIM // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    a = RopeTableArgs(P, int(bool(yarn)), orig_len, theta, factor, beta_fast, beta_slow,
+                      _ptr(cos), _ptr(sin))
+    _check(lib().dsa_rope_table(ctypes.byref(a), _stream()))
+    return cos, sin
+
+
+def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, q_fp8=None,
+                 q_scale=None, workspace=None) -> IndexerArgs:
+    import torch
+    B, S, H, D = q_raw.shape
+    Lmax = k_cache.shape[1]
+    dt = {torch.float32: DSA_DTYPE_F32, torch.bfloat16: DSA_DTYPE_BF16}.get(q_raw.dtype)
+    if dt is None:
+        raise TypeError("q_raw must be float32 or bfloat16")
+    _need(q_raw, "q_raw", q_raw.dtype, (B, S, H, INDEX_DIM))
+    _need(w, "w", torch.float32, (B, S, H))
+    _need(pos, "pos", torch.int32, (B, S))
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32, cos.shape)
+    _need(k_cache, "k_cache", torch.uint8, (B, Lmax, INDEX_DIM))
+    _need(k_scale, "k_scale", torch.float32, (B, Lmax))
+    if scores.dim() != 3 or scores.shape[:2] != (B, S) or scores.stride(2) != 1 \
+            or scores.stride(0) != S * scores.stride(1):
+        raise ValueError("scores must be [B, S, >=Lmax] with unit inner stride")
+    if not scores.is_cuda or scores.dtype != torch.float32:
+        raise TypeError("scores must be a float32 device tensor")
+    if k_raw is not None:
+        _need(k_raw, "k_raw", q_raw.dtype, (B, S, INDEX_DIM))
+    if q_fp8 is not None:
+        _need(q_fp8, "q_fp8", torch.uint8, (B, S, H, INDEX_DIM))
+        _need(q_scale, "q_scale", torch.float32, (B, S, H))
+    return IndexerArgs(B, S, H, Lmax, cos.shape[0], dt, _ptr(q_raw), _ptr(k_raw), _ptr(pos),
+                       _ptr(cos), _ptr(sin), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                       _ptr(q_fp8), _ptr(q_scale), _ptr(scores), scores.stride(1), 0,
+                       _ptr(workspace), 0 if workspace is None else workspace.numel())
+
+
+def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale):
+    """Call 1 with DSA_INDEXER_APPEND_ONLY: rotate, quantise and write the
+    key rows k_raw [B, S, 128] into k_cache/k_scale at pos [B, S]."""
+    import torch
+    B, S = pos.shape
+    Lmax = k_cache.shape[1]
+    dt = {torch.float32: DSA_DTYPE_F32, torch.bfloat16: DSA_DTYPE_BF16}.get(k_raw.dtype)
+    if dt is None:
+        raise TypeError("k_raw must be float32 or bfloat16")
+    _need(k_raw, "k_raw", k_raw.dtype, (B, S, INDEX_DIM))
+    _need(pos, "pos", torch.int32, (B, S))
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32, cos.shape)
+    _need(k_cache, "k_cache", torch.uint8, (B, Lmax, INDEX_DIM))
+    _need(k_scale, "k_scale", torch.float32, (B, Lmax))
+    a = IndexerArgs(B, S, 1, Lmax, cos.shape[0], dt, None, _ptr(k_raw), _ptr(pos), _ptr(cos),
+                    _ptr(sin), None, _ptr(k_cache), _ptr(k_scale), None, None, None, Lmax,
+                    APPEND_ONLY, None, 0)
+    _check(lib().dsa_indexer(ctypes.byref(a), _stream()))
+
+
+def indexer_workspace_bytes(args: IndexerArgs) -> int:
+    n = _sz(0)
+    _check(lib().dsa_indexer_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device):
+    import torch
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, scores=None, k_raw=None, q_fp8=None,
+            q_scale=None, workspace=None):
+    """Call 1: append k_raw rows (if given) and score every causal key.
+    Returns scores [B, S, Lmax] float32 (entries past each row's position
+    are left as they were)."""
+    import torch
+    B, S = q_raw.shape[:2]
+    if scores is None:
+        scores = torch.empty((B, S, k_cache.shape[1]), dtype=torch.float32, device=q_raw.device)
+    a = indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw, q_fp8, q_scale,
+                     workspace)
+    need = indexer_workspace_bytes(a)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = _workspace(need, q_raw.device)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(lib().dsa_indexer(ctypes.byref(a), _stream()))
+    return scores
+
+
+def topk_args(scores, pos, K, idx, count=None) -> TopkArgs:
+    import torch
+    B, S = pos.shape
+    _need(pos, "pos", torch.int32, (B, S))
+    _need(idx, "idx", torch.int32, (B, S, K))
+    if count is not None:
+        _need(count, "count", torch.int32, (B, S))
+    if scores.dim() != 3 or scores.shape[:2] != (B, S) or scores.stride(2) != 1 \
+            or scores.stride(0) != S * scores.stride(1) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [B, S, L] with unit inner stride")
+    return TopkArgs(B, S, scores.shape[2], K, _ptr(scores), scores.stride(1), _ptr(pos),
+                    _ptr(idx), _ptr(count), None, 0)
+
+
+def topk(scores, pos, K: int, idx=None, count=None):
+    """Call 2: causal top-K of every score row; returns idx [B, S, K] int32."""
+    import torch
+    B, S = pos.shape
+    if idx is None:
+        idx = torch.empty((B, S, K), dtype=torch.int32, device=scores.device)
+    a = topk_args(scores, pos, K, idx, count)
+    _check(lib().dsa_topk(ctypes.byref(a), _stream()))
+    return idx
+
+
+def mla_args(q, latent, rope, idx, scale, out, lse=None, workspace=None) -> MlaArgs:
+    import torch
+    B, S, Hq, Dq = q.shape
+    K = idx.shape[-1]
+    _need(q, "q", torch.bfloat16, (B, S, Hq, LATENT_DIM + ROPE_DIM))
+    _need(idx, "idx", torch.int32, (B, S, K))
+    _need(out, "out", torch.bfloat16, (B, S, Hq, LATENT_DIM))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, S, Hq))
+    for name, t, d in (("latent", latent, LATENT_DIM), ("rope", rope, ROPE_DIM)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != B \
+                or t.shape[2] != d or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor [B, Lmax, {d}] "
+                             "with unit inner stride")
+    if latent.shape[1] != rope.shape[1]:
+        raise ValueError("latent and rope must have the same Lmax")
+    return MlaArgs(B, S, Hq, latent.shape[1], K, _ptr(q), _ptr(latent), latent.stride(1),
+                   latent.stride(0), _ptr(rope), rope.stride(1), rope.stride(0), _ptr(idx),
+                   float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                   0 if workspace is None else workspace.numel())
+
+
+def sparse_mla_workspace_bytes(args: MlaArgs) -> int:
+    n = _sz(0)
+    _check(lib().dsa_sparse_mla_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace=None,
+               return_lse: bool = False):
+    """Call 3: absorbed sparse MLA; returns out [B, S, Hq, 512] bf16 (and lse)."""
+    import torch
+    B, S, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, S, Hq, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device)
+    a = mla_args(q, latent, rope, idx, scale, out, lse, workspace)
+    need = sparse_mla_workspace_bytes(a)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = _workspace(need, q.device)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(lib().dsa_sparse_mla(ctypes.byref(a), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def softmax_scale(qk_head_dim: int = 192, yarn: bool = False, rope_factor: float = 40.0,
+                  mscale: float = 1.0) -> float:
+    """qk_head_dim^-0.5, times m^2 with m = 1 + 0.1*mscale*ln(rope_factor) when
+    the YaRN correction applies (page "RoPE coefficients", MLA __init__)."""
+    s = qk_head_dim ** -0.5
+    if yarn:
+        m = 0.1 * mscale * math.log(rope_factor) + 1.0
+        s *= m * m
+    return s

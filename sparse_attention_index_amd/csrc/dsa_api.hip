@@ -1,0 +1,240 @@
+// dsa_api.hip -- host side of the C ABI declared in include/dsa.h:
+// argument validation, workspace sizing and kernel launches. Every check
+// runs before the first launch, so an invalid call has no side effects.
+#include "../../include/dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+namespace dsa {
+hipError_t launch_rope_table(int P, int npairs, double base, int yarn, double low, double high,
+                             double factor, float* cos_out, float* sin_out, hipStream_t stream);
+hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
+                          int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
+                          const float* sin_t, uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
+                        const float* qscale, const float* w, const int32_t* pos,
+                        const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
+                        hipStream_t stream);
+hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
+                       const int32_t* pos, int32_t* idx, int32_t* count, hipStream_t stream);
+size_t mla_workspace_bytes(int rows, int Hq, int K);
+hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
+                             const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
+                             const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
+                             const int32_t* idx, float scale, uint16_t* out, float* lse,
+                             void* workspace, hipStream_t stream);
+}  // namespace dsa
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------- indexer ---
+dsa_status check_indexer(const dsa_indexer_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->S < 1 || a->H < 1 || a->H > DSA_MAX_INDEX_HEADS || a->Lmax < 1 || a->P < 1)
+        return DSA_ERR_SHAPE;
+    if (!(a->flags & DSA_INDEXER_APPEND_ONLY) && static_cast<int64_t>(a->B) * a->S > kMaxGridY)
+        return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(a->B) * a->S > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(a->B) * a->Lmax > (int64_t(1) << 40)) return DSA_ERR_SHAPE;
+    if (a->ld_scores < a->Lmax) return DSA_ERR_SHAPE;
+    if (a->act_dtype != DSA_DTYPE_F32 && a->act_dtype != DSA_DTYPE_BF16) return DSA_ERR_UNSUPPORTED;
+    if ((a->flags & ~DSA_INDEXER_APPEND_ONLY) != 0) return DSA_ERR_UNSUPPORTED;
+    const size_t esz = a->act_dtype == DSA_DTYPE_BF16 ? 2 : 4;
+    const bool append_only = (a->flags & DSA_INDEXER_APPEND_ONLY) != 0;
+    if (!a->pos || !a->rope_cos || !a->rope_sin || !a->k_cache || !a->k_scale) return DSA_ERR_NULL;
+    if (append_only) {
+        if (!a->k_raw) return DSA_ERR_NULL;
+    } else {
+        if (!a->q_raw || !a->w || !a->scores) return DSA_ERR_NULL;
+        if ((a->q_fp8 == nullptr) != (a->q_scale == nullptr)) return DSA_ERR_NULL;
+    }
+    const uintptr_t amask = esz - 1;
+    if (!aligned16(a->k_cache) || (reinterpret_cast<uintptr_t>(a->k_raw) & amask) ||
+        !aligned4(a->k_scale) || !aligned4(a->pos) || !aligned4(a->rope_cos) ||
+        !aligned4(a->rope_sin))
+        return DSA_ERR_ALIGN;
+    if (!append_only &&
+        ((reinterpret_cast<uintptr_t>(a->q_raw) & amask) || (a->q_fp8 && !aligned16(a->q_fp8)) ||
+         !aligned4(a->scores) || !aligned4(a->w) || (a->q_scale && !aligned4(a->q_scale))))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+size_t indexer_ws(const dsa_indexer_args* a) {
+    if (a->q_fp8 != nullptr || (a->flags & DSA_INDEXER_APPEND_ONLY)) return 0;
+    const size_t rows = static_cast<size_t>(a->B) * a->S * a->H;
+    return round_up(rows * 128, 256) + round_up(rows * sizeof(float), 256);
+}
+
+// ---------------------------------------------------------------- topk ---
+dsa_status check_topk(const dsa_topk_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->S < 1 || a->Lmax < 1 || a->K < 1 || a->K > DSA_MAX_TOPK)
+        return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(a->B) * a->S > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
+    if (a->ld_scores < a->Lmax) return DSA_ERR_SHAPE;
+    if (!a->scores || !a->pos || !a->idx) return DSA_ERR_NULL;
+    if (!aligned4(a->scores) || !aligned4(a->pos) || !aligned4(a->idx) ||
+        (a->count && !aligned4(a->count)))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+// ----------------------------------------------------------------- mla ---
+dsa_status check_mla(const dsa_mla_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->S < 1 || a->Hq < 1 || a->Hq > DSA_MAX_ATTN_HEADS || a->Lmax < 1 ||
+        a->K < 1 || a->K > DSA_MAX_TOPK)
+        return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(a->B) * a->S > kMaxGridY) return DSA_ERR_SHAPE;
+    if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return DSA_ERR_SHAPE;
+    if (a->latent_row_stride < DSA_LATENT_DIM || a->rope_row_stride < DSA_ROPE_DIM ||
+        a->latent_batch_stride < 0 || a->rope_batch_stride < 0)
+        return DSA_ERR_SHAPE;
+    if (!a->q || !a->latent || !a->rope || !a->idx || !a->out) return DSA_ERR_NULL;
+    if (!aligned16(a->q) || !aligned16(a->latent) || !aligned16(a->rope) || !aligned16(a->out) ||
+        !aligned4(a->idx) || (a->lse && !aligned4(a->lse)))
+        return DSA_ERR_ALIGN;
+    if ((a->latent_row_stride % 8) || (a->latent_batch_stride % 8) || (a->rope_row_stride % 8) ||
+        (a->rope_batch_stride % 8))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_str(dsa_status s) {
+    switch (s) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+        case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size or stride is out of range";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: unknown dtype or flag";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+        case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: pointer or stride not aligned";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown dsa_status";
+}
+
+dsa_status dsa_rope_table(const dsa_rope_table_args* a, hipStream_t stream) {
+    if (a == nullptr || a->cos_out == nullptr || a->sin_out == nullptr) return DSA_ERR_NULL;
+    if (a->P < 1 || !(a->theta > 1.0f) || !std::isfinite(a->theta)) return DSA_ERR_SHAPE;
+    if (a->yarn != 0 && a->yarn != 1) return DSA_ERR_UNSUPPORTED;
+    if (!aligned4(a->cos_out) || !aligned4(a->sin_out)) return DSA_ERR_ALIGN;
+    const int npairs = DSA_INDEX_ROPE / 2;
+    const int dim = DSA_INDEX_ROPE;
+    double low = 0.0, high = 1.0;
+    if (a->yarn) {
+        if (a->orig_len < 1 || !(a->factor >= 1.0f) || !(a->beta_fast > a->beta_slow) ||
+            !(a->beta_slow > 0.0f) || !std::isfinite(a->factor) || !std::isfinite(a->beta_fast))
+            return DSA_ERR_SHAPE;
+        // YaRN correction dims: d(r) = dim * ln(orig / (2 pi r)) / (2 ln base)
+        const double pi = 3.14159265358979323846;
+        auto corr = [&](double r) {
+            return dim * std::log(static_cast<double>(a->orig_len) / (r * 2.0 * pi)) /
+                   (2.0 * std::log(static_cast<double>(a->theta)));
+        };
+        low = std::floor(corr(a->beta_fast));
+        high = std::ceil(corr(a->beta_slow));
+        if (low < 0.0) low = 0.0;
+        if (high > dim - 1) high = dim - 1;
+        if (low == high) high += 0.001;
+    }
+    return hip_status(dsa::launch_rope_table(a->P, npairs, static_cast<double>(a->theta), a->yarn,
+                                             low, high, static_cast<double>(a->factor),
+                                             a->cos_out, a->sin_out, stream));
+}
+
+dsa_status dsa_indexer_workspace(const dsa_indexer_args* a, size_t* bytes) {
+    if (bytes == nullptr) return DSA_ERR_NULL;
+    const dsa_status st = check_indexer(a);
+    if (st != DSA_OK) return st;
+    *bytes = indexer_ws(a);
+    return DSA_OK;
+}
+
+dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
+    dsa_status st = check_indexer(a);
+    if (st != DSA_OK) return st;
+    const size_t need = indexer_ws(a);
+    uint8_t* q8 = a->q_fp8;
+    if (a->flags & DSA_INDEXER_APPEND_ONLY) q8 = nullptr;
+    float* qs = a->q_scale;
+    if (need > 0) {
+        if (a->workspace == nullptr || a->workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+        const size_t rows = static_cast<size_t>(a->B) * a->S * a->H;
+        q8 = static_cast<uint8_t*>(a->workspace);
+        qs = reinterpret_cast<float*>(q8 + round_up(rows * 128, 256));
+    }
+    const bool bf16 = a->act_dtype == DSA_DTYPE_BF16;
+    const int64_t qrows = static_cast<int64_t>(a->B) * a->S * a->H;
+    hipError_t e = hipSuccess;
+    if (a->k_raw != nullptr) {
+        e = dsa::launch_prepare(bf16, true, static_cast<int64_t>(a->B) * a->S, 1, a->S, a->Lmax,
+                                a->P, a->k_raw, a->pos, a->rope_cos, a->rope_sin, a->k_cache,
+                                a->k_scale, stream);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    if (a->flags & DSA_INDEXER_APPEND_ONLY) return DSA_OK;
+    e = dsa::launch_prepare(bf16, false, qrows, a->H, a->S, a->Lmax, a->P, a->q_raw, a->pos,
+                            a->rope_cos, a->rope_sin, q8, qs, stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    e = dsa::launch_score(a->B, a->S, a->H, a->Lmax, a->P, q8, qs, a->w, a->pos, a->k_cache,
+                          a->k_scale, a->scores, a->ld_scores, stream);
+    return hip_status(e);
+}
+
+dsa_status dsa_topk_workspace(const dsa_topk_args* a, size_t* bytes) {
+    if (bytes == nullptr) return DSA_ERR_NULL;
+    const dsa_status st = check_topk(a);
+    if (st != DSA_OK) return st;
+    *bytes = 0;
+    return DSA_OK;
+}
+
+dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
+    const dsa_status st = check_topk(a);
+    if (st != DSA_OK) return st;
+    return hip_status(dsa::launch_topk(a->B * a->S, a->Lmax, a->K, a->scores, a->ld_scores,
+                                       a->pos, a->idx, a->count, stream));
+}
+
+dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* a, size_t* bytes) {
+    if (bytes == nullptr) return DSA_ERR_NULL;
+    const dsa_status st = check_mla(a);
+    if (st != DSA_OK) return st;
+    *bytes = dsa::mla_workspace_bytes(a->B * a->S, a->Hq, a->K);
+    return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla(const dsa_mla_args* a, hipStream_t stream) {
+    const dsa_status st = check_mla(a);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::mla_workspace_bytes(a->B * a->S, a->Hq, a->K);
+    if (need > 0) {
+        if (a->workspace == nullptr || a->workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+    }
+    return hip_status(dsa::launch_sparse_mla(
+        a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->latent, a->latent_row_stride,
+        a->latent_batch_stride, a->rope, a->rope_row_stride, a->rope_batch_stride, a->idx,
+        a->scale, a->out, a->lse, a->workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// dsa_common.h -- device helpers shared by the gfx950 kernels of the DSA
+// library (internal header; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> float ------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round a finite float to the nearest bf16 (ties to even); returns the bits.
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ---- OCP E4M3 encoding (round to nearest even, saturating at 448) --------
+// Works on the bits of the float32 input: subnormal outputs (|v| < 2^-6)
+// are multiples of 2^-9, so they are rint(|v| * 2^9); normal outputs keep
+// three mantissa bits, rounded half-to-even from the 23 float32 bits.
+__device__ __forceinline__ uint8_t e4m3_encode(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    float a = __uint_as_float(u & 0x7FFFFFFFu);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {                 // 2^-6: subnormal range
+        code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // exact scaling, RNE
+    } else {
+        uint32_t ua = __float_as_uint(a);
+        int32_t e = static_cast<int32_t>(ua >> 23) - 127;           // -6 .. 8
+        uint32_t mant = ua & 0x7FFFFFu;
+        uint32_t keep = mant >> 20;
+        uint32_t rem = mant & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+        if (keep == 8u) { keep = 0u; ++e; }
+        code = (static_cast<uint32_t>(e + 7) << 3) | keep;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return static_cast<uint8_t>(sign | code);
+}
+
+// ---- wave reductions (wave64) ---------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Exact conversion of four packed E4M3 bytes to four bf16 values.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t packed, bf16x2& lo, bf16x2& hi) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true);
+}
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    bf16x2 a, b, c, d;
+    e4m3x4_to_bf16(w0, a, b);
+    e4m3x4_to_bf16(w1, c, d);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 E4M3 x E4M3 -> f32 (unscaled form of the block-scaled MFMA).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0.0 is mapped like +0.0.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

@@ -1,0 +1,222 @@
+// indexer.hip -- lightning-indexer kernels for gfx950.
+//
+// Method (aipricedb digest, indexer formula; page "Sparse latent
+// attention", equation S^I; page "Rotate first features", Indexer.forward):
+//   I[t,s] = sum_h w[t,h] * ReLU(q[t,h] . k[s]),   64 heads x 128 features,
+// q and k rotated on features 0..63 with the non-interleaved pairing
+// (j, j+32) in float32, cast back to the activation dtype, then block-FP8
+// quantised (one float32 scale per 128 features, OCP E4M3 codes).
+//
+// Kernels:
+//   prepare_rows_kernel  one wave per 128-feature row: RoPE, cast, amax,
+//                        scale, E4M3 encode; q rows go to q_fp8/q_scale,
+//                        k rows are appended to k_cache/k_scale at pos.
+//   score_kernel         one block per (query row, key block): the q codes of
+//                        the row live in registers as bf16 MFMA operands, the
+//                        FP8 key cache streams through in 16-key subtiles.
+//                        Codes are converted exactly to bf16 and multiplied on
+//                        the bf16 MFMA (products of E4M3 values are exact in
+//                        float32); the epilogue applies ReLU, the per-head
+//                        weight w*q_scale, the head sum across lanes and the
+//                        key's scale.
+#include "dsa_common.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// prepare: RoPE (non-interleaved, first 64 features) + cast + block FP8.
+// Lane l holds features l and l+64 of its row; the rotation pairs feature j
+// (lane j) with j+32 (lane j+32), exchanged with one cross-lane swap.
+// ---------------------------------------------------------------------------
+template <bool BF16_IN, bool TO_CACHE>
+__global__ __launch_bounds__(256) void prepare_rows_kernel(
+    int64_t nrows, int rows_per_pos, int S, int Lmax, int P, const void* __restrict__ x,
+    const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, uint8_t* __restrict__ codes_out,
+    float* __restrict__ scales_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const int64_t r = row / rows_per_pos;          // query-row index b*S + s
+    const int p = pos[r];
+    if (p < 0 || p >= Lmax || p >= P) return;
+
+    float x0, x1;
+    if (BF16_IN) {
+        const uint16_t* xr = static_cast<const uint16_t*>(x) + row * 128;
+        x0 = bf16_bits_to_float(xr[lane]);
+        x1 = bf16_bits_to_float(xr[lane + 64]);
+    } else {
+        const float* xr = static_cast<const float*>(x) + row * 128;
+        x0 = xr[lane];
+        x1 = xr[lane + 64];
+    }
+    const float other = __shfl_xor(x0, 32);
+    const int j = lane & 31;
+    const float c = cos_t[static_cast<int64_t>(p) * 32 + j];
+    const float s = sin_t[static_cast<int64_t>(p) * 32 + j];
+    float y0;
+    {
+#pragma clang fp contract(off)
+        // pair (a, b) = (x[j], x[j+32]):  a' = a c - b s,  b' = a s + b c
+        if (lane < 32) {
+            const float ac = x0 * c, bs = other * s;
+            y0 = ac - bs;
+        } else {
+            const float as = other * s, bc = x0 * c;
+            y0 = as + bc;
+        }
+    }
+    if (BF16_IN) y0 = bf16_bits_to_float(float_to_bf16_bits(y0));   // cast back to bf16
+
+    const float amax = wave_max(fmaxf(fabsf(y0), fabsf(x1)));
+    float scale = amax / 448.0f;
+    if (!(scale > 0.0f)) scale = 1.0f;
+    const uint8_t c0 = e4m3_encode(y0 / scale);
+    const uint8_t c1 = e4m3_encode(x1 / scale);
+
+    int64_t dst;
+    if (TO_CACHE) {
+        const int64_t b = r / S;
+        dst = b * Lmax + p;
+    } else {
+        dst = row;
+    }
+    codes_out[dst * 128 + lane] = c0;
+    codes_out[dst * 128 + lane + 64] = c1;
+    if (lane == 0) scales_out[dst] = scale;
+}
+
+hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
+                          int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
+                          const float* sin_t, uint8_t* codes, float* scales, hipStream_t stream) {
+    if (nrows <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((nrows + 3) / 4)), block(256);
+#define DSA_PREP(B, C)                                                                         \
+    hipLaunchKernelGGL((prepare_rows_kernel<B, C>), grid, block, 0, stream, nrows, rows_per_pos, \
+                       S, Lmax, P, x, pos, cos_t, sin_t, codes, scales)
+    if (bf16_in) {
+        if (to_cache) DSA_PREP(true, true); else DSA_PREP(true, false);
+    } else {
+        if (to_cache) DSA_PREP(false, true); else DSA_PREP(false, false);
+    }
+#undef DSA_PREP
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// score: block = 4 waves, covers 64*U consecutive keys of one query row.
+// MFMA 16x16x32 bf16, M = 16 heads, N = 16 keys, K = 32 features; four
+// K-steps cover the 128 features and four head groups cover 64 heads.
+// Operand lane layout: lane (m = l%16, g = l/16) supplies row m, feature
+// chunk g; both operands use feature 32g + 8kk + j for MFMA kk, element j.
+// Result lane layout: lane (n = l%16, g) holds heads 4g..4g+3 of key n.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void score_kernel(
+    int S, int H, int Lmax, int P, const uint8_t* __restrict__ q8,
+    const float* __restrict__ qscale, const float* __restrict__ w,
+    const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
+    const float* __restrict__ kscale, float* __restrict__ scores, int64_t ld) {
+    const int row = blockIdx.y;
+    const int p = pos[row];
+    if (p < 0 || p >= Lmax || p >= P) return;
+    const int n_valid = p + 1;
+    const int kblock0 = blockIdx.x * (64 * U);
+    if (kblock0 >= n_valid) return;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t b = row / S;
+
+    bf16x8 qa[4][4];
+    float wq[4][4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+        const int h = hg * 16 + m;
+        if (h < H) {
+            const uint4* src = reinterpret_cast<const uint4*>(
+                q8 + (static_cast<int64_t>(row) * H + h) * 128 + g * 32);
+            const uint4 lo = src[0], hi = src[1];
+            qa[hg][0] = e4m3x8_to_bf16x8(lo.x, lo.y);
+            qa[hg][1] = e4m3x8_to_bf16x8(lo.z, lo.w);
+            qa[hg][2] = e4m3x8_to_bf16x8(hi.x, hi.y);
+            qa[hg][3] = e4m3x8_to_bf16x8(hi.z, hi.w);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qa[hg][kk][e] = static_cast<__bf16>(0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = hg * 16 + 4 * g + i;
+            wq[hg][i] = hh < H ? w[static_cast<int64_t>(row) * H + hh] *
+                                     qscale[static_cast<int64_t>(row) * H + hh]
+                               : 0.0f;
+        }
+    }
+
+    const uint8_t* kb = kcache + b * Lmax * 128;
+    const float* ksb = kscale + b * Lmax;
+    float* out = scores + static_cast<int64_t>(row) * ld;
+    const int wkey0 = kblock0 + wave * 16 * U;
+
+    uint4 kraw[U][2];
+    float ks[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int key = wkey0 + u * 16 + m;
+        key = key < n_valid ? key : n_valid - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * 128 + g * 32);
+        kraw[u][0] = src[0];
+        kraw[u][1] = src[1];
+        ks[u] = ksb[key];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int key0 = wkey0 + u * 16;
+        if (key0 >= n_valid) break;
+        bf16x8 kbf[4];
+        kbf[0] = e4m3x8_to_bf16x8(kraw[u][0].x, kraw[u][0].y);
+        kbf[1] = e4m3x8_to_bf16x8(kraw[u][0].z, kraw[u][0].w);
+        kbf[2] = e4m3x8_to_bf16x8(kraw[u][1].x, kraw[u][1].y);
+        kbf[3] = e4m3x8_to_bf16x8(kraw[u][1].z, kraw[u][1].w);
+        float part = 0.0f;
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += wq[hg][i] * fmaxf(acc[i], 0.0f);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        const int key = key0 + m;
+        if (g == 0 && key < n_valid) out[key] = part * ks[u];
+    }
+}
+
+// Keys per block: 64*U. Pick the largest U that still gives enough blocks to
+// fill the chip (blocks past a row's causal end exit at once).
+hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
+                        const float* qscale, const float* w, const int32_t* pos,
+                        const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
+                        hipStream_t stream) {
+    const int64_t rows = static_cast<int64_t>(B) * S;
+    int U = 4;
+    while (U > 1 && rows * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
+    const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)),
+                    static_cast<unsigned>(rows));
+#define DSA_SCORE(UU)                                                                          \
+    hipLaunchKernelGGL((score_kernel<UU>), grid, dim3(256), 0, stream, S, H, Lmax, P, q8, qscale, \
+                       w, pos, kcache, kscale, scores, ld)
+    if (U == 4) DSA_SCORE(4);
+    else if (U == 2) DSA_SCORE(2);
+    else DSA_SCORE(1);
+#undef DSA_SCORE
+    return hipGetLastError();
+}
+
+}  // namespace dsa

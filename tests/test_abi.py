@@ -1,0 +1,169 @@
+"""C-ABI checks that need no GPU: libdsa.so loads, exports every function
+include/dsa.h declares, the ctypes structs match the C layout, and the host
+validation rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_attention_index_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dsa_status|const char\*|int)\s+(dsa_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = dsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(dsa.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (dsa_\w+)$", out, re.M))
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_strings():
+    L = dsa.lib()
+    assert L.dsa_abi_version() == 1
+    for code in range(7):
+        assert dsa.status_str(code).startswith("DSA_")
+    assert dsa.status_str(99) == "unknown dsa_status"
+
+
+STRUCTS = {
+    "dsa_rope_table_args": dsa.RopeTableArgs,
+    "dsa_indexer_args": dsa.IndexerArgs,
+    "dsa_topk_args": dsa.TopkArgs,
+    "dsa_mla_args": dsa.MlaArgs,
+}
+
+
+def test_ctypes_structs_match_c_layout(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dsa.h"', 'int main(void) {']
+    for cname, st in STRUCTS.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in st._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I",
+                    "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n"):
+        if ln:
+            c, f, v = ln.split()
+            got[(c, f)] = int(v)
+    for cname, st in STRUCTS.items():
+        assert got[(cname, "size")] == ctypes.sizeof(st), cname
+        for fname, _ in st._fields_:
+            assert got[(cname, fname)] == getattr(st, fname).offset, (cname, fname)
+
+
+# ---- host-side validation (no launch happens on these paths) -----------------
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address that is never touched
+
+
+def good_indexer():
+    return dsa.IndexerArgs(1, 1, 64, 16384, 16384, dsa.DSA_DTYPE_BF16, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16384, 0, None, 0)
+
+
+def call(fn, args):
+    return fn(ctypes.byref(args), None)
+
+
+def test_indexer_validation():
+    L = dsa.lib()
+    n = ctypes.c_size_t(123)
+    assert L.dsa_indexer_workspace(ctypes.byref(good_indexer()), ctypes.byref(n)) == 0
+    assert n.value == 0                         # q_fp8/q_scale given -> no workspace
+    cases = [
+        (dict(H=65), 2), (dict(H=0), 2), (dict(B=0), 2), (dict(Lmax=0), 2), (dict(P=0), 2),
+        (dict(ld_scores=100), 2), (dict(act_dtype=7), 3), (dict(flags=2), 3),
+        (dict(flags=1, k_raw=None), 1), (dict(flags=1, k_raw=FAKE + 1), 5),
+        (dict(q_raw=None), 1), (dict(scores=None), 1), (dict(q_scale=None), 1),
+        (dict(k_cache=FAKE + 8), 5), (dict(B=300, S=300), 2),
+    ]
+    for change, code in cases:
+        a = good_indexer()
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(L.dsa_indexer, a) == code, change
+    # missing workspace when q_fp8 is not given
+    a = good_indexer()
+    a.q_fp8, a.q_scale = None, None
+    assert L.dsa_indexer_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value >= 64 * 128 + 64 * 4
+    assert call(L.dsa_indexer, a) == 4
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert call(L.dsa_indexer, a) == 4
+    assert L.dsa_indexer(None, None) == 1
+
+
+def good_topk():
+    return dsa.TopkArgs(2, 1, 16384, 2048, FAKE, 16384, FAKE, FAKE, None, None, 0)
+
+
+def test_topk_validation():
+    L = dsa.lib()
+    for change, code in [(dict(K=2049), 2), (dict(K=0), 2), (dict(ld_scores=10), 2),
+                         (dict(scores=None), 1), (dict(idx=None), 1), (dict(pos=FAKE + 2), 5)]:
+        a = good_topk()
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(L.dsa_topk, a) == code, change
+    n = ctypes.c_size_t(7)
+    assert L.dsa_topk_workspace(ctypes.byref(good_topk()), ctypes.byref(n)) == 0
+
+
+def good_mla(B=1, S=1, K=2048):
+    return dsa.MlaArgs(B, S, 128, 16384, K, FAKE, FAKE, 512, 512 * 16384, FAKE, 64, 64 * 16384,
+                       FAKE, 0.07, FAKE, None, None, 0)
+
+
+def test_mla_validation():
+    L = dsa.lib()
+    for change, code in [(dict(Hq=129), 2), (dict(K=4096), 2), (dict(scale=0.0), 2),
+                         (dict(scale=float("inf")), 2), (dict(latent_row_stride=500), 2),
+                         (dict(latent_row_stride=516), 5), (dict(q=FAKE + 4), 5),
+                         (dict(out=None), 1), (dict(idx=None), 1)]:
+        a = good_mla()
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(L.dsa_sparse_mla, a) == code, change
+    # decode row needs key-split partials -> workspace required
+    n = ctypes.c_size_t(0)
+    a = good_mla()
+    assert L.dsa_sparse_mla_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert call(L.dsa_sparse_mla, a) == 4
+    # a large batch of rows runs unsplit: no workspace
+    a = good_mla(B=1, S=4096)
+    assert L.dsa_sparse_mla_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_rope_table_validation():
+    L = dsa.lib()
+    a = dsa.RopeTableArgs(100, 1, 4096, 10000.0, 40.0, 1.0, 32.0, FAKE, FAKE)   # fast < slow
+    assert call(L.dsa_rope_table, a) == 2
+    a = dsa.RopeTableArgs(0, 0, 4096, 10000.0, 40.0, 32.0, 1.0, FAKE, FAKE)
+    assert call(L.dsa_rope_table, a) == 2
+    a = dsa.RopeTableArgs(10, 2, 4096, 10000.0, 40.0, 32.0, 1.0, FAKE, FAKE)
+    assert call(L.dsa_rope_table, a) == 3
+    a = dsa.RopeTableArgs(10, 0, 4096, 10000.0, 40.0, 32.0, 1.0, None, FAKE)
+    assert call(L.dsa_rope_table, a) == 1

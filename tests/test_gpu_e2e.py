@@ -1,0 +1,175 @@
+"""End-to-end GPU parity of one decode step (and sampled prefill rows):
+call 1 -> call 2 -> call 3 on the seeded workloads, against the oracle
+computing the same step from the same raw inputs.
+
+Rules: codes and scales bit-exact; scores within the indexer tolerance;
+selected sets equal except for positions whose oracle score lies within the
+indexer tolerance of the oracle's k-th score; attention outputs within 2e-2
+max-abs (rows whose selection differs are re-run on the oracle's selection)."""
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_index_amd as dsa
+import synth
+from gpu_util import (MLA_ATOL, check_scores, check_topk_membership, check_topk_properties, dev,
+                      dev_act, dev_bf16, host, host_bf16_as_f32, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_decode(wl, x, cos, sin, fill_all=True):
+    import torch
+    B, S, H, L = wl.B, wl.S, wl.H, wl.Lmax
+    kc = torch.zeros((B, L, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, L), dtype=torch.float32, device="cuda")
+    dcos, dsin = dev(cos), dev(sin)
+    act = wl.act_bf16
+    pos = x["pos"]
+    # cache fill for every position (the call re-appends the row's own key)
+    dsa.indexer_append(dev_act(x["k_raw"], act),
+                       dev(np.broadcast_to(np.arange(L, dtype=np.int32), (B, L)).copy()),
+                       dcos, dsin, kc, ks)
+    k_call = np.stack([x["k_raw"][b, pos[b]] for b in range(B)])
+    scores = dsa.indexer(dev_act(x["q_raw"], act), dev(x["w"]), dev(pos), dcos, dsin, kc, ks,
+                         k_raw=dev_act(k_call, act))
+    idx = dsa.topk(scores, dev(pos), wl.K)
+    out, lse = dsa.sparse_mla(dev_bf16(x["q_mla"]), dev_bf16(x["latent"]), dev_bf16(x["kpe"]),
+                              idx, wl.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    return dict(kc=host(kc), ks=host(ks), scores=host(scores), idx=host(idx),
+                out=host_bf16_as_f32(out), lse=host(lse))
+
+
+def oracle_scores_rows(wl, x, cos, sin, rows_sel=None):
+    """Oracle codes for every key and the score rows of the chosen query rows."""
+    B, L = wl.B, wl.Lmax
+    kpos = np.broadcast_to(np.arange(L, dtype=np.int32), (B, L))
+    k8, ks, _ = oracle.indexer_prepare(x["k_raw"], kpos, cos, sin, wl.act_bf16)
+    q_raw, pos = x["q_raw"], x["pos"]
+    if rows_sel is not None:
+        q_raw, pos = q_raw[:, rows_sel], pos[:, rows_sel]
+    q8, qs, _ = oracle.indexer_prepare(q_raw, pos[..., None], cos, sin, wl.act_bf16)
+    w = x["w"] if rows_sel is None else x["w"][:, rows_sel]
+    sc = oracle.indexer_scores(oracle.dequantize(q8, qs), w, oracle.dequantize(k8, ks), pos + 1)
+    return k8, ks, sc, pos
+
+
+def oracle_mla_rows(x, idx, scale, b, rows):
+    """Oracle attention for batch row b, query rows `rows`, selection idx [len(rows), K]."""
+    sel = np.unique(idx[idx >= 0])
+    remap = np.full(x["latent"].shape[1], -1, np.int64)
+    remap[sel] = np.arange(sel.size)
+    ib = np.where(idx >= 0, remap[np.maximum(idx, 0)], -1).astype(np.int32)
+    lat = synth.bf16_bits_to_f32(x["latent"][b, sel])[None]
+    pe = synth.bf16_bits_to_f32(x["kpe"][b, sel])[None]
+    q = synth.bf16_bits_to_f32(x["q_mla"][b, rows])[None]
+    o, l = oracle.sparse_mla(q, lat, pe, ib[None], scale)
+    return o[0], l[0]
+
+
+def compare_mla(wl, x, gidx, oidx, gout, glse, b, rows, label):
+    """Compare GPU attention rows with the oracle on the oracle's selection;
+    rows whose GPU selection differs are recomputed on the GPU with the
+    oracle's selection first."""
+    import torch
+    o, ol = oracle_mla_rows(x, oidx, wl.softmax_scale, b, rows)
+    same = np.all(gidx == oidx, axis=-1)
+    g = gout.copy()
+    gl = glse.copy()
+    if not np.all(same):
+        bad = np.nonzero(~same)[0]
+        q = dev_bf16(x["q_mla"][b:b + 1, rows][:, bad])
+        out2, lse2 = dsa.sparse_mla(q, dev_bf16(x["latent"][b:b + 1]), dev_bf16(x["kpe"][b:b + 1]),
+                                    dev(oidx[bad][None]), wl.softmax_scale, return_lse=True)
+        torch.cuda.synchronize()
+        g[bad] = host_bf16_as_f32(out2)[0]
+        gl[bad] = host(lse2)[0]
+    err = np.abs(g - o).max()
+    say(f"  {label}: mla max abs err {err:.3e}, rows with a different selection: {int((~same).sum())}")
+    assert err <= MLA_ATOL
+    assert np.allclose(gl, ol, atol=1e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode16k", "batch32"])
+def test_decode_step_end_to_end(name):
+    wl = synth.workload(name)
+    say(f"e2e decode {name}: B={wl.B} Lmax={wl.Lmax} H={wl.H} Hq={wl.Hq} K={wl.K}")
+    x = synth.make_inputs(wl)
+    cos, sin = oracle.rope_table(wl.Lmax, yarn=wl.yarn)
+    gres = gpu_decode(wl, x, cos, sin)
+    k8, ks, osc, pos = oracle_scores_rows(wl, x, cos, sin)
+    n_valid = (pos + 1).reshape(-1)
+    for b in range(wl.B):
+        n = n_valid[b]
+        assert np.array_equal(gres["kc"][b, :n], k8[b, :n]) and np.array_equal(gres["ks"][b, :n], ks[b, :n])
+    worst = check_scores(gres["scores"].reshape(wl.B, -1), osc.reshape(wl.B, -1), n_valid, name)
+    oidx = oracle.topk(np.nan_to_num(osc.reshape(wl.B, -1)), n_valid, wl.K)
+    gidx = gres["idx"].reshape(wl.B, -1)
+    mism = check_topk_membership(gidx, oidx, osc.reshape(wl.B, -1), n_valid, wl.K, name)
+    check_topk_properties(gres["scores"].reshape(wl.B, -1), gidx, n_valid, wl.K, name)
+    say(f"  worst score err {worst:.2e}; rows with boundary swaps {mism}")
+    for b in range(wl.B):
+        compare_mla(wl, x, gidx[b:b + 1], oidx[b:b + 1], gres["out"][b], gres["lse"][b], b,
+                    np.array([0]), f"{name} b={b}")
+
+
+def test_prefill_sampled_rows():
+    import torch
+    wl = synth.workload("prefill4k")
+    say("e2e prefill4k (sampled rows)")
+    x = synth.make_inputs(wl)
+    cos, sin = oracle.rope_table(wl.Lmax)
+    T = wl.S
+    kc = torch.zeros((1, T, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((1, T), dtype=torch.float32, device="cuda")
+    pos = x["pos"]
+    scores = dsa.indexer(dev_act(x["q_raw"], True), dev(x["w"]), dev(pos), dev(cos), dev(sin),
+                         kc, ks, k_raw=dev_act(x["k_raw"], True))
+    idx = dsa.topk(scores, dev(pos), wl.K)
+    out, lse = dsa.sparse_mla(dev_bf16(x["q_mla"]), dev_bf16(x["latent"]), dev_bf16(x["kpe"]),
+                              idx, wl.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    g_sc, g_idx = host(scores)[0], host(idx)[0]
+    g_out, g_lse = host_bf16_as_f32(out)[0], host(lse)[0]
+    check_topk_properties(g_sc, g_idx, np.arange(1, T + 1), wl.K, "prefill all rows")
+    rows = np.array([0, 1, 2, 17, 2046, 2047, 2048, 2049, 3001, 4094, 4095])
+    k8, oks, osc, opos = oracle_scores_rows(wl, x, cos, sin, rows)
+    assert np.array_equal(host(kc)[0], k8[0]) and np.array_equal(host(ks)[0], oks[0])
+    n_valid = rows + 1
+    check_scores(g_sc[rows], osc[0], n_valid, "prefill")
+    oidx = oracle.topk(np.nan_to_num(osc[0]), n_valid, wl.K)
+    check_topk_membership(g_idx[rows], oidx, osc[0], n_valid, wl.K, "prefill")
+    compare_mla(wl, x, g_idx[rows], oidx, g_out[rows], g_lse[rows], 0, rows, "prefill")
+
+
+def test_decode128k_sampled_keys():
+    """Long-context decode at full size (B=4, L=131072, YaRN table): scores
+    at sampled key positions against the oracle, top-k by its defining
+    properties on the GPU scores, attention output finite."""
+    import torch
+    wl = synth.workload("decode128k")
+    say("e2e decode128k (sampled keys)")
+    x = synth.make_inputs(wl)
+    cos, sin = oracle.rope_table(wl.Lmax, yarn=True)
+    g = gpu_decode(wl, x, cos, sin)
+    B, L = wl.B, wl.Lmax
+    rng = synth.rng(5)
+    keys = np.unique(np.concatenate([np.arange(64), L - 64 + np.arange(64),
+                                     rng.choice(L, 4096, replace=False)]))
+    k8, kss, _ = oracle.indexer_prepare(x["k_raw"][:, keys], keys[None].astype(np.int32), cos,
+                                        sin, True)
+    for b in range(B):
+        assert np.array_equal(g["kc"][b, keys], k8[b]) and np.array_equal(g["ks"][b, keys], kss[b])
+    q8, qs, _ = oracle.indexer_prepare(x["q_raw"], x["pos"][..., None], cos, sin, True)
+    osc = oracle.indexer_scores(oracle.dequantize(q8, qs), x["w"], oracle.dequantize(k8, kss),
+                                np.full((B, 1), keys.size, np.int32))
+    gsc = g["scores"].reshape(B, L)
+    for b in range(B):
+        o = osc[b, 0]
+        floor = 0.01 * np.abs(o).max()       # sampled maximum: no looser than the full row's
+        den = np.maximum(np.abs(o), floor)
+        assert np.all(np.abs(gsc[b, keys] - o) <= 1e-3 * den), b
+    n_valid = (x["pos"] + 1).reshape(-1)
+    check_topk_properties(gsc, g["idx"].reshape(B, -1), n_valid, wl.K, "decode128k")
+    assert np.all(np.isfinite(g["out"])) and np.all(np.isfinite(g["lse"]))

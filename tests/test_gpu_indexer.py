@@ -1,0 +1,161 @@
+"""GPU parity of call 1 (RoPE table, prepare, lightning-indexer score)
+against the oracle, through the C ABI.
+
+The quantised codes and scales must be bit-identical to the oracle's (both
+sides take every rounding decision in float32 with one IEEE rounding per
+operation). Scores must lie within 1e-3 of the oracle's fp64 score on the
+dequantised values, relative to max(|score|, 1% of the row's largest
+|score|)."""
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_index_amd as dsa
+import synth
+from gpu_util import (check_scores, dev, dev_act, host, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("P,yarn", [(5, False), (16384, False), (131072, True)])
+def test_rope_table_matches_oracle(P, yarn):
+    say(f"rope_table P={P} yarn={yarn}")
+    c, s = dsa.rope_table(P, yarn=yarn)
+    oc, os_ = oracle.rope_table(P, yarn=yarn)
+    for g, o in ((host(c), oc), (host(s), os_)):
+        ulps = np.abs(g.view(np.int32).astype(np.int64) - o.view(np.int32).astype(np.int64))
+        # opposite-sign zeros aside, at most one unit in the last place
+        same = (g == o)
+        assert np.all(same | (ulps <= 1))
+        assert np.mean(~same) < 1e-4
+
+
+def run_indexer(B, S, H, Lmax, pos, act_bf16, seed, yarn=False, w_scale=None):
+    """Fill the whole cache with the append-only call, then score with the
+    call's own key rows appended again (identical values)."""
+    import torch
+    g = synth.rng(seed)
+    q_raw = g.standard_normal((B, S, H, 128), dtype=np.float32)
+    k_all = g.standard_normal((B, Lmax, 128), dtype=np.float32)
+    w = g.standard_normal((B, S, H), dtype=np.float32) * np.float32(
+        w_scale if w_scale is not None else (H ** -0.5) * 128 ** -0.5)
+    if act_bf16:
+        q_raw = synth.bf16_bits_to_f32(synth.to_bf16_bits(q_raw))
+        k_all = synth.bf16_bits_to_f32(synth.to_bf16_bits(k_all))
+    pos = np.asarray(pos, np.int32).reshape(B, S)
+    cos, sin = oracle.rope_table(Lmax, yarn=yarn)
+    dcos, dsin = dev(cos), dev(sin)
+    kc = torch.zeros((B, Lmax, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, Lmax), dtype=torch.float32, device="cuda")
+    all_pos = np.broadcast_to(np.arange(Lmax, dtype=np.int32), (B, Lmax)).copy()
+    dsa.indexer_append(dev_act(k_all, act_bf16), dev(all_pos), dcos, dsin, kc, ks)
+    k_call = np.stack([k_all[b, pos[b]] for b in range(B)])          # [B,S,128]
+    scores = torch.full((B, S, Lmax), float("nan"), dtype=torch.float32, device="cuda")
+    q8 = torch.empty((B, S, H, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    dsa.indexer(dev_act(q_raw, act_bf16), dev(w), dev(pos), dcos, dsin, kc, ks, scores,
+                k_raw=dev_act(k_call, act_bf16), q_fp8=q8, q_scale=qs)
+    torch.cuda.synchronize()
+    return dict(q_raw=q_raw, k_all=k_all, w=w, pos=pos, cos=cos, sin=sin, kc=host(kc),
+                ks=host(ks), q8=host(q8), qs=host(qs), scores=host(scores))
+
+
+def oracle_indexer(r, act_bf16):
+    B, Lmax = r["k_all"].shape[:2]
+    kpos = np.broadcast_to(np.arange(Lmax, dtype=np.int32), (B, Lmax))
+    k8, ks, _ = oracle.indexer_prepare(r["k_all"], kpos, r["cos"], r["sin"], act_bf16)
+    q8, qs, _ = oracle.indexer_prepare(r["q_raw"], r["pos"][..., None], r["cos"], r["sin"],
+                                       act_bf16)
+    sc = oracle.indexer_scores(oracle.dequantize(q8, qs), r["w"], oracle.dequantize(k8, ks),
+                               r["pos"] + 1)
+    return dict(k8=k8, ks=ks, q8=q8, qs=qs, scores=sc)
+
+
+CASES = [
+    # B, S, H, Lmax, positions, bf16 activations, seed
+    ("tiny-shape", 1, 1, 4, 256, [[255]], False, 0),
+    ("ragged", 3, 2, 20, 1000, [[999, 5], [0, 640], [63, 64]], True, 101),
+    ("one-key", 1, 1, 64, 17, [[0]], True, 102),
+    ("tail", 2, 1, 64, 4133, [[4132], [2000]], True, 103),
+    ("f32", 1, 3, 64, 700, [[699, 100, 1]], False, 104),
+]
+
+
+@pytest.mark.parametrize("name,B,S,H,Lmax,pos,bf16,seed", CASES, ids=[c[0] for c in CASES])
+def test_indexer_parity(name, B, S, H, Lmax, pos, bf16, seed):
+    say(f"indexer case {name}: B={B} S={S} H={H} Lmax={Lmax}")
+    r = run_indexer(B, S, H, Lmax, pos, bf16, seed)
+    o = oracle_indexer(r, bf16)
+    assert np.array_equal(r["q8"], o["q8"]) and np.array_equal(r["qs"], o["qs"])
+    assert np.array_equal(r["kc"], o["k8"]) and np.array_equal(r["ks"], o["ks"])
+    n_valid = r["pos"] + 1
+    gs = r["scores"].reshape(B * S, Lmax)
+    worst = check_scores(gs, o["scores"].reshape(B * S, Lmax), n_valid, name)
+    say(f"  worst normalised score error {worst:.2e}")
+    for row, n in enumerate(n_valid.reshape(-1)):
+        assert np.all(np.isnan(gs[row, n:])), "entries past the causal end were written"
+
+
+def test_indexer_decode16k_full_size():
+    wl = synth.workload("decode16k")
+    say("indexer decode16k full size")
+    r = run_indexer(wl.B, wl.S, wl.H, wl.Lmax, synth.positions(wl), True, wl.seed,
+                    w_scale=wl.w_scale)
+    o = oracle_indexer(r, True)
+    assert np.array_equal(r["kc"], o["k8"]) and np.array_equal(r["ks"], o["ks"])
+    assert np.array_equal(r["q8"], o["q8"]) and np.array_equal(r["qs"], o["qs"])
+    worst = check_scores(r["scores"][:, 0], o["scores"][:, 0], r["pos"][:, 0] + 1, "decode16k")
+    say(f"  worst normalised score error {worst:.2e}")
+
+
+def test_indexer_zero_and_extreme_rows():
+    """All-zero rows quantise to scale 1 and zero codes; rows mixing huge and
+    tiny magnitudes exercise saturation-free scaling and E4M3 subnormals."""
+    import torch
+    B, S, H, Lmax = 1, 1, 16, 64
+    g = synth.rng(7)
+    q_raw = g.standard_normal((B, S, H, 128)).astype(np.float32)
+    q_raw[0, 0, 0] = 0.0
+    q_raw[0, 0, 1] *= np.float32(1e-6)
+    q_raw[0, 0, 2, :3] = np.float32(3e4)
+    q_raw[0, 0, 3] = np.exp2(g.integers(-30, 10, size=128)).astype(np.float32)
+    k_all = g.standard_normal((B, Lmax, 128)).astype(np.float32)
+    k_all[0, 5] = 0.0
+    k_all[0, 6] = np.exp2(g.integers(-30, 10, size=128)).astype(np.float32)
+    w = g.standard_normal((B, S, H)).astype(np.float32)
+    pos = np.array([[Lmax - 1]], np.int32)
+    cos, sin = oracle.rope_table(Lmax)
+    kc = torch.zeros((B, Lmax, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, Lmax), dtype=torch.float32, device="cuda")
+    dsa.indexer_append(dev(k_all), dev(np.arange(Lmax, dtype=np.int32)[None]), dev(cos),
+                       dev(sin), kc, ks)
+    q8 = torch.empty((B, S, H, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    sc = dsa.indexer(dev(q_raw), dev(w), dev(pos), dev(cos), dev(sin), kc, ks, q_fp8=q8,
+                     q_scale=qs)
+    ok8, oks, _ = oracle.indexer_prepare(k_all, np.arange(Lmax, dtype=np.int32)[None], cos,
+                                         sin, False)
+    oq8, oqs, _ = oracle.indexer_prepare(q_raw, pos[..., None], cos, sin, False)
+    assert np.array_equal(host(kc), ok8) and np.array_equal(host(ks), oks)
+    assert np.array_equal(host(q8), oq8) and np.array_equal(host(qs), oqs)
+    assert host(qs)[0, 0, 0] == 1.0 and np.all(host(q8)[0, 0, 0] & 0x7F == 0)
+    o = oracle.indexer_scores(oracle.dequantize(oq8, oqs), w, oracle.dequantize(ok8, oks),
+                              pos + 1)
+    check_scores(host(sc)[:, 0], o[:, 0], pos[:, 0] + 1, "extreme")
+
+
+def test_positions_out_of_range_are_skipped():
+    import torch
+    B, S, H, Lmax = 2, 1, 8, 128
+    g = synth.rng(9)
+    cos, sin = oracle.rope_table(Lmax)
+    kc = torch.zeros((B, Lmax, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, Lmax), dtype=torch.float32, device="cuda")
+    scores = torch.full((B, S, Lmax), 7.0, dtype=torch.float32, device="cuda")
+    pos = np.array([[-1], [Lmax]], np.int32)
+    dsa.indexer(dev(g.standard_normal((B, S, H, 128)).astype(np.float32)),
+                dev(np.ones((B, S, H), np.float32)), dev(pos), dev(cos), dev(sin), kc, ks,
+                scores, k_raw=dev(g.standard_normal((B, S, 128)).astype(np.float32)))
+    torch.cuda.synchronize()
+    assert np.all(host(scores) == 7.0)
+    assert np.all(host(kc) == 0) and np.all(host(ks) == 0)
