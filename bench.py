@@ -1,0 +1,316 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one decode step of the whole path on one batch of synthetic
+queries, replayed as one captured HIP graph per cache replica: call 1
+(append the new key, quantise q, lightning-indexer score), call 2 (causal
+top-2048), call 3 (sparse absorbed MLA). The default workload
+is decode at L = 16384 (B = 1), the configuration the headline metric is
+quoted on; --workload selects another one (batch32, decode128k).
+
+Inputs are resident in HBM before the timed region. Every step reads its
+caches from one of R replicas (R * footprint >= 1 GiB) so the 256 MiB
+Infinity Cache cannot serve them; scores/idx/out buffers are reused like a
+serving loop's workspace. HIP events on the launch stream bracket the timed
+region. Each call's device time is then measured the same way over a graph
+that runs that call once per replica, back to back; the call with the
+largest average is the "dominant kernel" of the roofline object.
+
+Prints ONE JSON line. `cpu_baseline` is the CPU oracle (oracle/) timed on
+the host's cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode16k",
+                    choices=["decode16k", "batch32", "decode128k"])
+    ap.add_argument("--replica-bytes", type=float, default=float(1 << 30),
+                    help="minimum total bytes of rotated cache replicas")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ byte model --
+
+def algorithmic_bytes(wl, n_valid, keff):
+    """Bytes the method itself must move per call, summed over the batch
+    (the per-row figures of the byte model in the design doc)."""
+    n_valid = np.asarray(n_valid, np.int64)
+    keff = np.asarray(keff, np.int64)
+    H, Hq = wl.H, wl.Hq
+    act = 2
+    indexer = int(np.sum(n_valid * (128 + 4) + H * 128 * act + H * 4 + (128 * act + 128 + 4)))
+    topk = int(np.sum(4 * n_valid + 4 * keff))
+    mla = int(np.sum(4 * keff + 1152 * keff + Hq * 576 * 2 + Hq * 512 * 2))
+    # step total: the scores round trip (write by call 1, read by call 2) is
+    # a cost of the three-call split, not of the method
+    step = indexer + int(np.sum(4 * keff)) + int(np.sum(1152 * keff + Hq * 576 * 2 + Hq * 512 * 2))
+    return dict(indexer=indexer, topk=topk, sparse_mla=mla, step=step)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_index_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_call, srchash):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel_call)
+    if not ent or rec.get("source_hash") != srchash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- setup --
+
+def setup(wl, replica_bytes):
+    import torch
+
+    import sparse_attention_index_amd as dsa
+    import synth
+
+    x = synth.make_inputs(wl)
+    dev = torch.device("cuda")
+    B, S, L = wl.B, wl.S, wl.Lmax
+    cos, sin = dsa.rope_table(L, yarn=wl.yarn)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_all = torch.from_numpy(x["k_raw"]).to(dev).to(torch.bfloat16)
+    kc = torch.zeros((B, L, 128), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, L), dtype=torch.float32, device=dev)
+    dsa.indexer_append(k_all, torch.arange(L, dtype=torch.int32, device=dev)[None].expand(B, L)
+                       .contiguous(), cos, sin, kc, ks)
+    latent, kpe = bf16(x["latent"]), bf16(x["kpe"])
+    pos_np = x["pos"]
+    pos = torch.from_numpy(pos_np).to(dev)
+    k_new = torch.stack([k_all[b, pos_np[b]] for b in range(B)]).contiguous()   # [B,S,128]
+    q_raw = torch.from_numpy(x["q_raw"]).to(dev).to(torch.bfloat16)
+    w = torch.from_numpy(x["w"]).to(dev)
+    q_mla = bf16(x["q_mla"])
+    del k_all
+    per_replica = kc.numel() + ks.numel() * 4 + latent.numel() * 2 + kpe.numel() * 2
+    R = max(2, int(np.ceil(replica_bytes / per_replica)))
+    reps = [dict(kc=kc, ks=ks, latent=latent, kpe=kpe)]
+    for _ in range(R - 1):
+        reps.append(dict(kc=kc.clone(), ks=ks.clone(), latent=latent.clone(), kpe=kpe.clone()))
+    scores = torch.empty((B, S, L), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, S, wl.K), dtype=torch.int32, device=dev)
+    out = torch.empty((B, S, wl.Hq, 512), dtype=torch.bfloat16, device=dev)
+    q8 = torch.empty((B, S, wl.H, 128), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, S, wl.H), dtype=torch.float32, device=dev)
+    # workspaces sized once, outside the timed region
+    mla_ws_args = dsa.mla_args(q_mla, latent, kpe, idx, wl.softmax_scale, out)
+    mla_ws = torch.empty(max(1, dsa.sparse_mla_workspace_bytes(mla_ws_args)), dtype=torch.uint8,
+                         device=dev)
+    torch.cuda.synchronize()
+    return dict(x=x, cos=cos, sin=sin, pos=pos, k_new=k_new, q_raw=q_raw, w=w, q_mla=q_mla,
+                reps=reps, R=R, per_replica=per_replica, scores=scores, idx=idx, out=out, q8=q8,
+                qs=qs, mla_ws=mla_ws)
+
+
+def make_calls(wl, st):
+    """The three calls of one step, bound to replica r."""
+    import sparse_attention_index_amd as dsa
+
+    def indexer(r):
+        rep = st["reps"][r % st["R"]]
+        dsa.indexer(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], rep["kc"], rep["ks"],
+                    st["scores"], k_raw=st["k_new"], q_fp8=st["q8"], q_scale=st["qs"])
+
+    def topk(r):
+        dsa.topk(st["scores"], st["pos"], wl.K, idx=st["idx"])
+
+    def sparse_mla(r):
+        rep = st["reps"][r % st["R"]]
+        dsa.sparse_mla(st["q_mla"], rep["latent"], rep["kpe"], st["idx"], wl.softmax_scale,
+                       out=st["out"], workspace=st["mla_ws"])
+
+    return {"indexer": indexer, "topk": topk, "sparse_mla": sparse_mla}
+
+
+def capture(fn):
+    """Record fn() into a HIP graph (launches on torch's capture stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+# ----------------------------------------------------------- cpu oracle --
+
+def cpu_baseline(wl, x, seconds):
+    """The oracle's decode step on the host: prepare q and the new key,
+    dequantise the FP8 key cache, score, top-k, sparse MLA. The key cache is
+    quantised by the oracle and the latent/rope caches widened to float64
+    once, outside the timed region (the oracle's resident cache form).
+    Timed over whole queries until `seconds` of work have run."""
+    import oracle
+    import synth
+    B, L = wl.B, wl.Lmax
+    cos, sin = oracle.rope_table(L, yarn=wl.yarn)
+    b = 0
+    n = int(wl.lengths[b])
+    kpos = np.arange(n, dtype=np.int32)[None]
+    k8, ks, _ = oracle.indexer_prepare(x["k_raw"][b:b + 1, :n], kpos, cos, sin, True)
+    lat = synth.bf16_bits_to_f32(x["latent"][b:b + 1, :n]).astype(np.float64)
+    kpe = synth.bf16_bits_to_f32(x["kpe"][b:b + 1, :n]).astype(np.float64)
+    qm = synth.bf16_bits_to_f32(x["q_mla"][b:b + 1]).astype(np.float64)
+    pos = x["pos"][b:b + 1]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        q8, qs, _ = oracle.indexer_prepare(x["q_raw"][b:b + 1], pos[..., None], cos, sin, True)
+        kn8, kns, _ = oracle.indexer_prepare(x["k_raw"][b:b + 1, pos[0, 0]][:, None],
+                                             pos, cos, sin, True)
+        k8[0, pos[0, 0]] = kn8[0, 0]
+        ks[0, pos[0, 0]] = kns[0, 0]
+        kd = oracle.dequantize(k8, ks)
+        sc = oracle.indexer_scores(oracle.dequantize(q8, qs), x["w"][b:b + 1], kd, pos + 1)
+        idx = oracle.topk(sc[0], pos[0] + 1, wl.K)[None]
+        oracle.sparse_mla(qm, lat, kpe, idx, wl.softmax_scale)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 1000:
+            break
+    return dict(value=done / el, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{done} single-query decode steps of {wl.name} (batch row 0, "
+                       f"L={n}, H=64, top-{wl.K}, 128 heads) in {el:.1f} s")
+
+
+# ------------------------------------------------------------------ main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(batch rows and long rows would shard across GPUs as DESIGN.md describes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    wl = synth.workload(args.workload)
+    torch.cuda.set_device(0)
+    st = setup(wl, args.replica_bytes)
+    calls = make_calls(wl, st)
+    R = st["R"]
+
+    def step(r):
+        for c in ("indexer", "topk", "sparse_mla"):
+            calls[c](r)
+
+    # eager warm-up (one-time kernel attribute set-up happens here), then one
+    # graph per replica for the step and one graph per call covering all
+    # replicas back to back
+    for r in range(min(R, 3)):
+        step(r)
+    torch.cuda.synchronize()
+    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    call_graphs = {c: capture(lambda c=c: [calls[c](r) for r in range(R)]) for c in calls}
+    for i in range(args.warmup):
+        step_graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step_graphs[i % R].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+
+    # per-call device time: each call graph runs the call once per replica
+    reps_call = max(1, (K + R - 1) // R)
+    avg_us = {}
+    for c, g in call_graphs.items():
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps_call):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        avg_us[c] = a.elapsed_time(b) * 1000.0 / (reps_call * R)
+
+    n_valid = [int(p) + 1 for p in st["x"]["pos"].reshape(-1)]
+    keff = [min(wl.K, n) for n in n_valid]
+    ab = algorithmic_bytes(wl, n_valid, keff)
+    dom = max(avg_us, key=avg_us.get)
+    achieved = ab[dom] / (avg_us[dom] * 1e-6) / 1e9
+    srch = source_hash()
+    traffic = load_traffic(dom, srch)
+    ms_per_step = total_ms / K
+    queries = wl.B * wl.S
+    value = queries * K / (total_ms / 1000.0)
+
+    rec = {
+        "metric": "decode queries/s (indexer+top-2048+sparse MLA) at L=16K; % HBM roofline",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3/bf16 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) activations and caches; no trained weights)",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.Lmax, "indexer_heads": wl.H,
+                   "attn_heads": wl.Hq, "topk": wl.K, "replicas": st["R"],
+                   "replica_bytes": st["per_replica"], "launch": "one HIP graph per step"},
+        "step_algorithmic_bytes": ab["step"],
+        "step_hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": ab[dom],
+                     "avg_launch_us": round(avg_us[dom], 3)},
+        "source_hash": srch,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, st["x"], args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,11 @@ hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
                         hipStream_t stream);
+hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, const void* q_raw,
+                               const void* k_raw, const int32_t* pos, const float* cos_t,
+                               const float* sin_t, const float* w, uint8_t* kcache,
+                               float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
+                               int64_t ld, hipStream_t stream);
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
                        const int32_t* pos, int32_t* idx, int32_t* count, hipStream_t stream);
 size_t mla_workspace_bytes(int rows, int Hq, int K);
@@ -70,7 +75,7 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
 }
 
 size_t indexer_ws(const dsa_indexer_args* a) {
-    if (a->q_fp8 != nullptr || (a->flags & DSA_INDEXER_APPEND_ONLY)) return 0;
+    if (a->q_fp8 != nullptr || (a->flags & DSA_INDEXER_APPEND_ONLY) || a->S == 1) return 0;
     const size_t rows = static_cast<size_t>(a->B) * a->S * a->H;
     return round_up(rows * 128, 256) + round_up(rows * sizeof(float), 256);
 }
@@ -185,6 +190,13 @@ dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
     const bool bf16 = a->act_dtype == DSA_DTYPE_BF16;
     const int64_t qrows = static_cast<int64_t>(a->B) * a->S * a->H;
     hipError_t e = hipSuccess;
+    if (a->S == 1 && !(a->flags & DSA_INDEXER_APPEND_ONLY)) {
+        // decode: one fused launch (quantise q, append the new key, score)
+        e = dsa::launch_decode_score(bf16, a->B, a->H, a->Lmax, a->P, a->q_raw, a->k_raw, a->pos,
+                                     a->rope_cos, a->rope_sin, a->w, a->k_cache, a->k_scale,
+                                     a->q_fp8, a->q_scale, a->scores, a->ld_scores, stream);
+        return hip_status(e);
+    }
     if (a->k_raw != nullptr) {
         e = dsa::launch_prepare(bf16, true, static_cast<int64_t>(a->B) * a->S, 1, a->S, a->Lmax,
                                 a->P, a->k_raw, a->pos, a->rope_cos, a->rope_sin, a->k_cache,

@@ -27,29 +27,22 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 }
 
 // ---- OCP E4M3 encoding (round to nearest even, saturating at 448) --------
-// Works on the bits of the float32 input: subnormal outputs (|v| < 2^-6)
-// are multiples of 2^-9, so they are rint(|v| * 2^9); normal outputs keep
-// three mantissa bits, rounded half-to-even from the 23 float32 bits.
+// Branch-free, on the bits of the float32 input. Normal outputs: adding
+// 0x7FFFF plus the lowest kept bit to the magnitude bits rounds the 23-bit
+// mantissa to 3 bits half-to-even (a carry bumps the exponent); shifting out
+// 20 bits and re-biasing the exponent from 127 to 7 gives the code, clamped
+// to 0x7E (448). Subnormal outputs (|v| < 2^-6) are multiples of 2^-9:
+// rint(|v| * 512), exact scaling, round half to even.
 __device__ __forceinline__ uint8_t e4m3_encode(float v) {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    float a = __uint_as_float(u & 0x7FFFFFFFu);
-    uint32_t code;
-    if (a >= 448.0f) {
-        code = 0x7Eu;
-    } else if (a < 0.015625f) {                 // 2^-6: subnormal range
-        code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // exact scaling, RNE
-    } else {
-        uint32_t ua = __float_as_uint(a);
-        int32_t e = static_cast<int32_t>(ua >> 23) - 127;           // -6 .. 8
-        uint32_t mant = ua & 0x7FFFFFu;
-        uint32_t keep = mant >> 20;
-        uint32_t rem = mant & 0xFFFFFu;
-        if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-        if (keep == 8u) { keep = 0u; ++e; }
-        code = (static_cast<uint32_t>(e + 7) << 3) | keep;
-        if (code > 0x7Eu) code = 0x7Eu;
-    }
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t ua = u & 0x7FFFFFFFu;
+    const float a = __uint_as_float(ua);
+    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+    int32_t cn = static_cast<int32_t>(r >> 20) - (120 << 3);
+    cn = cn < 0x7E ? cn : 0x7E;
+    const uint32_t cs = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+    const uint32_t code = a < 0.015625f ? cs : static_cast<uint32_t>(cn);
     return static_cast<uint8_t>(sign | code);
 }
 

@@ -198,6 +198,231 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode path (one query row per batch row): every block quantises its
+// row's 64 query heads itself (into LDS) while its key loads are in flight,
+// and the block that covers the row's own position also rotates, quantises
+// and appends the new key, using it straight from LDS. One launch replaces
+// prepare(k) + prepare(q) + score.
+// Query quantisation layout: thread t owns head t/4, quarter t%4 of the 128
+// features; quarters 0/1 hold rotary pairs (j, j+32) for j in [16q, 16q+16),
+// quarters 2/3 hold features 64..95 / 96..127. The head's amax is reduced
+// over its four threads.
+// ---------------------------------------------------------------------------
+template <bool BF16_IN>
+__device__ __forceinline__ float load_act(const void* base, int64_t i) {
+    if (BF16_IN) return bf16_bits_to_float(static_cast<const uint16_t*>(base)[i]);
+    return static_cast<const float*>(base)[i];
+}
+
+template <bool BF16_IN>
+__device__ __forceinline__ float round_act(float v) {
+    return BF16_IN ? bf16_bits_to_float(float_to_bf16_bits(v)) : v;
+}
+
+template <int U, bool BF16_IN>
+__global__ __launch_bounds__(256) void decode_score_kernel(
+    int H, int Lmax, int P, const void* __restrict__ q_raw, const void* __restrict__ k_raw,
+    const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, const float* __restrict__ w, uint8_t* __restrict__ kcache,
+    float* __restrict__ kscale, uint8_t* __restrict__ q8_out, float* __restrict__ qs_out,
+    float* __restrict__ scores, int64_t ld) {
+    __shared__ __align__(16) uint8_t qcodes[64 * 128];
+    __shared__ float qscale[64];
+    __shared__ __align__(16) uint8_t kcodes[128];
+    __shared__ float kscale_new;
+
+    const int row = blockIdx.y;
+    const int p = pos[row];
+    if (p < 0 || p >= Lmax || p >= P) return;
+    const int n_valid = p + 1;
+    const int kblock0 = blockIdx.x * (64 * U);
+    if (kblock0 >= n_valid) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t b = row;
+    const uint8_t* kb = kcache + b * Lmax * 128;
+    const float* ksb = kscale + b * Lmax;
+    const int wkey0 = kblock0 + wave * 16 * U;
+    const bool has_new = k_raw != nullptr && kblock0 + 64 * U > p;   // block covers key p
+
+    // 1. key loads first (the new key, if any, is taken from LDS later)
+    uint4 kraw[U][2];
+    float ks[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int key = wkey0 + u * 16 + m;
+        key = key < n_valid ? key : n_valid - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * 128 + g * 32);
+        kraw[u][0] = src[0];
+        kraw[u][1] = src[1];
+        ks[u] = ksb[key];
+    }
+
+    // 2. quantise the row's query heads into LDS
+    {
+#pragma clang fp contract(off)
+        const int hh = tid >> 2, qt = tid & 3;
+        float v[32];
+        float amax = 0.0f;
+        if (hh < H) {
+            const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128;
+            if (qt < 2) {
+                const int j0 = 16 * qt;
+                const float* c = cos_t + static_cast<int64_t>(p) * 32 + j0;
+                const float* sn = sin_t + static_cast<int64_t>(p) * 32 + j0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float a = load_act<BF16_IN>(q_raw, base + j0 + j);
+                    const float bb = load_act<BF16_IN>(q_raw, base + j0 + j + 32);
+                    const float ac = a * c[j], bs = bb * sn[j];
+                    const float as = a * sn[j], bc = bb * c[j];
+                    v[j] = round_act<BF16_IN>(ac - bs);
+                    v[16 + j] = round_act<BF16_IN>(as + bc);
+                }
+            } else {
+                const int f0 = 64 + 32 * (qt - 2);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) v[j] = load_act<BF16_IN>(q_raw, base + f0 + j);
+            }
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        float scale = amax / 448.0f;
+        if (!(scale > 0.0f)) scale = 1.0f;
+        // 32 codes packed into two 16-byte LDS stores
+        uint32_t pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                word |= static_cast<uint32_t>(e4m3_encode(v[4 * i + e] / scale)) << (8 * e);
+            pk[i] = hh < H ? word : 0u;
+        }
+        // quarters 0/1: features [16q, 16q+16) and [16q+32, 16q+48); 2/3: [32q, 32q+32)
+        const int off0 = qt < 2 ? 16 * qt : 32 * qt;
+        const int off1 = qt < 2 ? 16 * qt + 32 : 32 * qt + 16;
+        uint4* dst0 = reinterpret_cast<uint4*>(qcodes + hh * 128 + off0);
+        uint4* dst1 = reinterpret_cast<uint4*>(qcodes + hh * 128 + off1);
+        *dst0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *dst1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        if (qt == 0) qscale[hh] = hh < H ? scale : 0.0f;
+    }
+    // 3. the new key (block covering position p): wave 0, lane l holds l, l+64
+    if (has_new && wave == 0) {
+#pragma clang fp contract(off)
+        const int64_t base = b * 128;
+        const float x0 = load_act<BF16_IN>(k_raw, base + lane);
+        const float x1 = load_act<BF16_IN>(k_raw, base + lane + 64);
+        const float other = __shfl_xor(x0, 32);
+        const int j = lane & 31;
+        const float c = cos_t[static_cast<int64_t>(p) * 32 + j];
+        const float sn = sin_t[static_cast<int64_t>(p) * 32 + j];
+        float y0;
+        if (lane < 32) {
+            const float ac = x0 * c, bs = other * sn;
+            y0 = ac - bs;
+        } else {
+            const float as = other * sn, bc = x0 * c;
+            y0 = as + bc;
+        }
+        y0 = round_act<BF16_IN>(y0);
+        const float amax = wave_max(fmaxf(fabsf(y0), fabsf(x1)));
+        float scale = amax / 448.0f;
+        if (!(scale > 0.0f)) scale = 1.0f;
+        const uint8_t c0 = e4m3_encode(y0 / scale), c1 = e4m3_encode(x1 / scale);
+        kcodes[lane] = c0;
+        kcodes[lane + 64] = c1;
+        uint8_t* kdst = kcache + (b * Lmax + p) * 128;
+        kdst[lane] = c0;
+        kdst[lane + 64] = c1;
+        if (lane == 0) {
+            kscale_new = scale;
+            kscale[b * Lmax + p] = scale;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && q8_out != nullptr) {
+        for (int i = tid; i < H * 8; i += 256)
+            reinterpret_cast<uint4*>(q8_out + static_cast<int64_t>(row) * H * 128)[i] =
+                reinterpret_cast<const uint4*>(qcodes)[i];
+        if (tid < H) qs_out[static_cast<int64_t>(row) * H + tid] = qscale[tid];
+    }
+
+    // 4. operands from LDS, MFMA stream (as score_kernel)
+    bf16x8 qa[4][4];
+    float wq[4][4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+        const uint4* src = reinterpret_cast<const uint4*>(qcodes + (hg * 16 + m) * 128 + g * 32);
+        const uint4 lo = src[0], hi = src[1];
+        qa[hg][0] = e4m3x8_to_bf16x8(lo.x, lo.y);
+        qa[hg][1] = e4m3x8_to_bf16x8(lo.z, lo.w);
+        qa[hg][2] = e4m3x8_to_bf16x8(hi.x, hi.y);
+        qa[hg][3] = e4m3x8_to_bf16x8(hi.z, hi.w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = hg * 16 + 4 * g + i;
+            wq[hg][i] = h < H ? w[static_cast<int64_t>(row) * H + h] * qscale[h] : 0.0f;
+        }
+    }
+    float* out = scores + static_cast<int64_t>(row) * ld;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int key0 = wkey0 + u * 16;
+        if (key0 >= n_valid) break;
+        const int key = key0 + m;
+        float ksc = ks[u];
+        if (has_new && key == p) {
+            kraw[u][0] = reinterpret_cast<const uint4*>(kcodes + g * 32)[0];
+            kraw[u][1] = reinterpret_cast<const uint4*>(kcodes + g * 32)[1];
+            ksc = kscale_new;
+        }
+        bf16x8 kbf[4];
+        kbf[0] = e4m3x8_to_bf16x8(kraw[u][0].x, kraw[u][0].y);
+        kbf[1] = e4m3x8_to_bf16x8(kraw[u][0].z, kraw[u][0].w);
+        kbf[2] = e4m3x8_to_bf16x8(kraw[u][1].x, kraw[u][1].y);
+        kbf[3] = e4m3x8_to_bf16x8(kraw[u][1].z, kraw[u][1].w);
+        float part = 0.0f;
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += wq[hg][i] * fmaxf(acc[i], 0.0f);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (g == 0 && key < n_valid) out[key] = part * ksc;
+    }
+}
+
+hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, const void* q_raw,
+                               const void* k_raw, const int32_t* pos, const float* cos_t,
+                               const float* sin_t, const float* w, uint8_t* kcache,
+                               float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
+                               int64_t ld, hipStream_t stream) {
+    int U = 4;
+    while (U > 1 && static_cast<int64_t>(B) * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
+    const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)), static_cast<unsigned>(B));
+#define DSA_DEC(UU, BF)                                                                          \
+    hipLaunchKernelGGL((decode_score_kernel<UU, BF>), grid, dim3(256), 0, stream, H, Lmax, P,    \
+                       q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out, qs_out,     \
+                       scores, ld)
+    if (bf16_in) {
+        if (U == 4) DSA_DEC(4, true); else if (U == 2) DSA_DEC(2, true); else DSA_DEC(1, true);
+    } else {
+        if (U == 4) DSA_DEC(4, false); else if (U == 2) DSA_DEC(2, false); else DSA_DEC(1, false);
+    }
+#undef DSA_DEC
+    return hipGetLastError();
+}
+
 // Keys per block: 64*U. Pick the largest U that still gives enough blocks to
 // fill the chip (blocks past a row's causal end exit at once).
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,

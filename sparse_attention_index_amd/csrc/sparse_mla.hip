@@ -65,7 +65,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     v4f acc[kDl / 16];
 #pragma unroll
     for (int t = 0; t < kDl / 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    // l_run sums the float32 probabilities (for lse); lr_run sums the bf16
+    // values that actually weight the latent rows (for the normalisation).
+    float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
 
     const int j_begin = split * slots_per_split;
     const int j_end = min(K, j_begin + slots_per_split);
@@ -134,15 +136,17 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         const bool live = m_new != -INFINITY;
         const float corr = live ? exp2f(m_run - m_new) : 1.0f;
         bf16x8 pv;
-        float psum = 0.0f;
+        float psum = 0.0f, prsum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float pe = live ? exp2f(z[i] - m_new) : 0.0f;
             const __bf16 pb = static_cast<__bf16>(pe);
             pv[i] = pb;
-            psum += static_cast<float>(pb);
+            psum += pe;
+            prsum += static_cast<float>(pb);
         }
         l_run = l_run * corr + psum;
+        lr_run = lr_run * corr + prsum;
         m_run = m_new;
 #pragma unroll
         for (int t = 0; t < kDl / 16; ++t) {
@@ -157,9 +161,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    float lr_tot = lr_run + __shfl_xor(lr_run, 16);
+    lr_tot += __shfl_xor(lr_tot, 32);
     if (h >= Hq) return;
     if (nsplit == 1) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
         uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
 #pragma unroll
         for (int t = 0; t < kDl / 16; ++t) {
@@ -179,50 +185,78 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         for (int t = 0; t < kDl / 16; ++t)
             *reinterpret_cast<float4*>(wo + 16 * t) =
                 make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-        if (g == 0) {
-            ws_ml[slot * 2] = m_run;
-            ws_ml[slot * 2 + 1] = l_tot;
-        }
+        if (g == 0)
+            *reinterpret_cast<float4*>(ws_ml + slot * 4) = make_float4(m_run, l_tot, lr_tot, 0.0f);
     }
 }
 
-// Merge of key-split partials: block per (row, head), 128 threads x 4 features.
+// Merge of key-split partials: block per (row, head), 128 threads x 4
+// features. The (m, l, lr) triples of all splits are staged in LDS first so
+// the partial-output loads below are independent and overlap.
+constexpr int kMaxSplits = 64;
+
 __global__ __launch_bounds__(128) void combine_kernel(int Hq, int nsplit,
                                                       const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+    __shared__ float4 ml[kMaxSplits];
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float s_M, s_L, s_Lr;
     const int rh = blockIdx.x;
     const int64_t row = rh / Hq;
     const int h = rh - static_cast<int>(row * Hq);
-    const int d = threadIdx.x * 4;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((row * nsplit + s) * Hq + h) * 2]);
-    float L = 0.0f;
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t slot = (row * nsplit + s) * Hq + h;
-            const float ms = ws_ml[slot * 2];
-            if (ms == -INFINITY) continue;
-            const float e = exp2f(ms - M);
-            L += ws_ml[slot * 2 + 1] * e;
-            const float4 v = *reinterpret_cast<const float4*>(ws_o + slot * kDl + d);
-            o0 += e * v.x;
-            o1 += e * v.y;
-            o2 += e * v.z;
-            o3 += e * v.w;
+    const int tid = threadIdx.x;
+    const int d = tid * 4;
+    if (tid < nsplit)
+        ml[tid] = *reinterpret_cast<const float4*>(ws_ml + ((row * nsplit + tid) * Hq + h) * 4);
+    __syncthreads();
+    if (tid < 64) {
+        float M = -INFINITY;
+        for (int s = tid; s < nsplit; s += 64) M = fmaxf(M, ml[s].x);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        float L = 0.0f, Lr = 0.0f;
+        for (int s = tid; s < nsplit; s += 64) {
+            const float e = (ml[s].x == -INFINITY) ? 0.0f : exp2f(ml[s].x - M);
+            wgt[s] = e;
+            L += ml[s].y * e;
+            Lr += ml[s].z * e;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            L += __shfl_xor(L, o);
+            Lr += __shfl_xor(Lr, o);
+        }
+        if (tid == 0) {
+            s_M = M;
+            s_L = L;
+            s_Lr = Lr;
         }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    __syncthreads();
+    const float* base = ws_o + (row * nsplit * Hq + h) * kDl + d;
+    const int64_t sstride = static_cast<int64_t>(Hq) * kDl;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) {
+        const float e = wgt[s];
+        const float4 v = *reinterpret_cast<const float4*>(base + s * sstride);
+        acc.x += e * v.x;
+        acc.y += e * v.y;
+        acc.z += e * v.z;
+        acc.w += e * v.w;
+    }
+    const float Lr = s_Lr;
+    const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
     uint16_t* oh = out + (row * Hq + h) * kDl + d;
-    const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(o0 * inv)) |
-                        (static_cast<uint32_t>(float_to_bf16_bits(o1 * inv)) << 16);
-    const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(o2 * inv)) |
-                        (static_cast<uint32_t>(float_to_bf16_bits(o3 * inv)) << 16);
+    const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc.x * inv)) |
+                        (static_cast<uint32_t>(float_to_bf16_bits(acc.y * inv)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc.z * inv)) |
+                        (static_cast<uint32_t>(float_to_bf16_bits(acc.w * inv)) << 16);
     *reinterpret_cast<uint2*>(oh) = make_uint2(lo, hi);
-    if (lse != nullptr && threadIdx.x == 0)
-        lse[row * Hq + h] = L > 0.0f ? M * 0.69314718055994531f + logf(L) : -INFINITY;
+    if (lse != nullptr && tid == 0)
+        lse[row * Hq + h] = s_L > 0.0f ? s_M * 0.69314718055994531f + logf(s_L) : -INFINITY;
 }
 
 // Split plan: enough (row, split) blocks to occupy the chip, each split a
@@ -230,7 +264,8 @@ __global__ __launch_bounds__(128) void combine_kernel(int Hq, int nsplit,
 void mla_plan(int rows, int K, int* nsplit, int* slots_per_split) {
     const int tiles = (K + kTile - 1) / kTile;
     int ns = (256 + rows - 1) / rows;
-    const int cap = tiles >= 2 ? tiles / 2 : 1;
+    int cap = tiles >= 2 ? tiles / 2 : 1;
+    if (cap > kMaxSplits) cap = kMaxSplits;
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
     const int tiles_per = (tiles + ns - 1) / ns;
@@ -244,7 +279,7 @@ size_t mla_workspace_bytes(int rows, int Hq, int K) {
     mla_plan(rows, K, &ns, &sps);
     if (ns == 1) return 0;
     const size_t slots = static_cast<size_t>(rows) * ns * Hq;
-    return slots * kDl * sizeof(float) + slots * 2 * sizeof(float) + 256;
+    return slots * kDl * sizeof(float) + slots * 4 * sizeof(float) + 256;
 }
 
 template <int NW>

@@ -103,9 +103,12 @@ def test_indexer_validation():
         for k, v in change.items():
             setattr(a, k, v)
         assert call(L.dsa_indexer, a) == code, change
-    # missing workspace when q_fp8 is not given
+    # missing workspace when q_fp8 is not given (multi-row calls; a decode
+    # call with S == 1 keeps its quantised query on chip)
     a = good_indexer()
     a.q_fp8, a.q_scale = None, None
+    assert L.dsa_indexer_workspace(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
+    a.S = 2
     assert L.dsa_indexer_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
     assert n.value >= 64 * 128 + 64 * 4
     assert call(L.dsa_indexer, a) == 4
