@@ -134,10 +134,11 @@ def setup(wl, replica_bytes):
     mla_ws_args = dsa.mla_args(q_mla, latent, kpe, idx, wl.softmax_scale, out)
     mla_ws = torch.empty(max(1, dsa.sparse_mla_workspace_bytes(mla_ws_args)), dtype=torch.uint8,
                          device=dev)
+    topk_ws = dsa.topk_workspace(scores, pos, wl.K)
     torch.cuda.synchronize()
     return dict(x=x, cos=cos, sin=sin, pos=pos, k_new=k_new, q_raw=q_raw, w=w, q_mla=q_mla,
                 reps=reps, R=R, per_replica=per_replica, scores=scores, idx=idx, out=out, q8=q8,
-                qs=qs, mla_ws=mla_ws)
+                qs=qs, mla_ws=mla_ws, topk_ws=topk_ws)
 
 
 def make_calls(wl, st):
@@ -150,7 +151,7 @@ def make_calls(wl, st):
                     st["scores"], k_raw=st["k_new"], q_fp8=st["q8"], q_scale=st["qs"])
 
     def topk(r):
-        dsa.topk(st["scores"], st["pos"], wl.K, idx=st["idx"])
+        dsa.topk(st["scores"], st["pos"], wl.K, idx=st["idx"], workspace=st["topk_ws"])
 
     def sparse_mla(r):
         rep = st["reps"][r % st["R"]]

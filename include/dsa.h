@@ -179,7 +179,12 @@ dsa_status dsa_indexer(const dsa_indexer_args* args, hipStream_t stream);
  * Scores must be finite (NaN is not ordered).
  * Layouts: scores row r at scores + r*ld_scores (ld_scores >= Lmax),
  *   pos [B][S] int32, idx [B][S][K] int32, count [B][S] int32 (optional).
- * Limits: 1 <= K <= 2048, B, S, Lmax >= 1. Workspace: dsa_topk_workspace().
+ * Limits: 1 <= K <= 2048, B, S, Lmax >= 1.
+ * Workspace: dsa_topk_workspace() bytes (0 for short rows), 256-byte
+ * aligned. It carries per-row histograms and counters between the call's
+ * launches and MUST be zero-filled before its first use; every call leaves
+ * it zero-filled again, so a workspace can be reused across calls on one
+ * stream without clearing. Calls that overlap in time need their own.
  * ---------------------------------------------------------------------- */
 typedef struct dsa_topk_args {
     int32_t B, S, Lmax, K;

@@ -234,7 +234,7 @@ def indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, scores=None, k_raw=None, 
     return scores
 
 
-def topk_args(scores, pos, K, idx, count=None) -> TopkArgs:
+def topk_args(scores, pos, K, idx, count=None, workspace=None) -> TopkArgs:
     import torch
     B, S = pos.shape
     _need(pos, "pos", torch.int32, (B, S))
@@ -245,16 +245,38 @@ def topk_args(scores, pos, K, idx, count=None) -> TopkArgs:
             or scores.stride(0) != S * scores.stride(1) or scores.dtype != torch.float32:
         raise ValueError("scores must be float32 [B, S, L] with unit inner stride")
     return TopkArgs(B, S, scores.shape[2], K, _ptr(scores), scores.stride(1), _ptr(pos),
-                    _ptr(idx), _ptr(count), None, 0)
+                    _ptr(idx), _ptr(count), _ptr(workspace),
+                    0 if workspace is None else workspace.numel())
 
 
-def topk(scores, pos, K: int, idx=None, count=None):
-    """Call 2: causal top-K of every score row; returns idx [B, S, K] int32."""
+def topk_workspace_bytes(args: TopkArgs) -> int:
+    n = _sz(0)
+    _check(lib().dsa_topk_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def topk_workspace(scores, pos, K: int):
+    """A zero-filled workspace for topk() on these shapes (reusable across
+    calls on one stream: every call leaves it zero-filled)."""
+    import torch
+    B, S = pos.shape
+    idx = torch.empty((B, S, K), dtype=torch.int32, device=scores.device)
+    n = topk_workspace_bytes(topk_args(scores, pos, K, idx))
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=scores.device)
+
+
+def topk(scores, pos, K: int, idx=None, count=None, workspace=None):
+    """Call 2: causal top-K of every score row; returns idx [B, S, K] int32.
+    `workspace` must come from topk_workspace() (zero-filled) when given."""
     import torch
     B, S = pos.shape
     if idx is None:
         idx = torch.empty((B, S, K), dtype=torch.int32, device=scores.device)
-    a = topk_args(scores, pos, K, idx, count)
+    a = topk_args(scores, pos, K, idx, count, workspace)
+    need = topk_workspace_bytes(a)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(lib().dsa_topk(ctypes.byref(a), _stream()))
     return idx
 

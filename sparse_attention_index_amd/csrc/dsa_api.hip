@@ -24,7 +24,9 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
                                int64_t ld, hipStream_t stream);
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
-                       const int32_t* pos, int32_t* idx, int32_t* count, hipStream_t stream);
+                       const int32_t* pos, int32_t* idx, int32_t* count, void* workspace,
+                       hipStream_t stream);
+size_t topk_workspace_bytes(int rows, int Lmax);
 size_t mla_workspace_bytes(int rows, int Hq, int K);
 hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
@@ -87,6 +89,7 @@ dsa_status check_topk(const dsa_topk_args* a) {
         return DSA_ERR_SHAPE;
     if (static_cast<int64_t>(a->B) * a->S > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
     if (a->ld_scores < a->Lmax) return DSA_ERR_SHAPE;
+    if (a->Lmax > (1 << 21)) return DSA_ERR_SHAPE;
     if (!a->scores || !a->pos || !a->idx) return DSA_ERR_NULL;
     if (!aligned4(a->scores) || !aligned4(a->pos) || !aligned4(a->idx) ||
         (a->count && !aligned4(a->count)))
@@ -216,15 +219,20 @@ dsa_status dsa_topk_workspace(const dsa_topk_args* a, size_t* bytes) {
     if (bytes == nullptr) return DSA_ERR_NULL;
     const dsa_status st = check_topk(a);
     if (st != DSA_OK) return st;
-    *bytes = 0;
+    *bytes = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax);
     return DSA_OK;
 }
 
 dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
     const dsa_status st = check_topk(a);
     if (st != DSA_OK) return st;
+    const size_t need = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax);
+    if (need > 0) {
+        if (a->workspace == nullptr || a->workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+    }
     return hip_status(dsa::launch_topk(a->B * a->S, a->Lmax, a->K, a->scores, a->ld_scores,
-                                       a->pos, a->idx, a->count, stream));
+                                       a->pos, a->idx, a->count, a->workspace, stream));
 }
 
 dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* a, size_t* bytes) {

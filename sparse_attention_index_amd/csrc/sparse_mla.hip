@@ -7,53 +7,93 @@
 //   z_j = scale * (q[h][0:512] . latent[p_j] + q[h][512:576] . rope[p_j])
 //   out[h] = sum_j softmax(z)_j latent[p_j],  lse[h] = log sum_j exp(z_j).
 //
-// Design: one block serves 16*NW heads of one query row over a contiguous
-// range ("split") of its selected positions. Selected rows are gathered 32
-// at a time into LDS: K tile [32][576] row-major (padded) and a transposed
-// copy of the latent part, V^T [512][32]. Per wave (16 heads):
-//   S^T = K Q^T       bf16 MFMA 16x16x32, M = keys, N = heads, K = features;
-//                     the wave's Q^T operands stay in registers.
-//   online softmax    per head (one head per lane column), in log2 units.
-//   O^T += V^T P^T    bf16 MFMA, M = 16 latent features, N = heads,
-//                     K = the 32 keys; P^T comes straight from the S^T
-//                     result registers (the key order inside the MFMA K
-//                     dimension is free as long as both operands agree).
+// Design: one block of 4 waves serves 64 heads (16 per wave) of one query
+// row over a contiguous range ("split") of its selected positions; two such
+// blocks share a CU, so one block's gather latency hides behind the other's
+// MFMA work. The two head-group blocks of a (row, split) get launch indices
+// 8 apart in one 1-D grid: the same XCD and back to back in dispatch order,
+// so the second block's gather is served by that XCD's L2. The split's
+// index list is staged in LDS once. Selected rows are gathered 32 at a time
+// (8 threads per row) into an LDS tile K [32][576] (row-major, padded).
+// Per wave:
+//   S^T = K Q^T       bf16 MFMA 16x16x32, M = keys (2 tiles of 16), N = the
+//                     wave's 16 heads, K = features; Q^T stays in VGPRs.
+//   online softmax    per head (one head per lane column, four lanes per
+//                     head), in log2 units, against a reference maximum that
+//                     moves only when the running maximum passes it by 8:
+//                     the accumulator is rescaled only then.
+//   O^T += V^T P^T    bf16 MFMA 16x16x32, M = 16 latent features (32 tiles),
+//                     N = heads, K = the 32 keys. P^T comes straight from the
+//                     S^T result registers (the key order inside the MFMA K
+//                     dimension only has to match between the operands); V^T
+//                     is read from the row-major K tile with the transposing
+//                     LDS read ds_read_b64_tr_b16: within each 16-lane group,
+//                     lane 4e+q addresses features 4q..4q+3 of key e and lane
+//                     i receives feature i of keys 0..3.
 // With several splits per row the unnormalised partials (O, m, l) go to the
 // workspace and combine_kernel merges them with the log-sum-exp rule.
 #include "dsa_common.h"
 
 namespace dsa {
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+
 constexpr int kDl = 512, kDr = 64, kDq = 576;
 constexpr int kTile = 32;
 constexpr int kKtStride = kDq + 8;      // bf16 per K-tile row (1168 B, staggers banks)
-constexpr int kVtStride = kTile + 4;    // bf16 per V^T row (72 B)
-constexpr size_t kMlaLdsBytes =
-    sizeof(uint16_t) * (kTile * kKtStride + kDl * kVtStride) + sizeof(int) * kTile;
+constexpr int kMlaThreads = 256;        // 4 waves x 16 heads
+constexpr int kHeadsPerBlock = 64;
+constexpr int kMaxSlots = 2048;         // selected positions per split, at most
+constexpr int kMaxSplits = 64;
+constexpr size_t kMlaLdsBytes = sizeof(uint16_t) * kTile * kKtStride + sizeof(int) * kMaxSlots;
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
-    int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit,
+__device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_v4s*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))));
+}
+
+__global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
+    int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
     const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* Vt = Kt + kTile * kKtStride;
-    int* tile_pos = reinterpret_cast<int*>(Vt + kDl * kVtStride);
+    int* sidx = reinterpret_cast<int*>(Kt + kTile * kKtStride);
 
-    constexpr int kThreads = NW * 64;
-    const int row = blockIdx.y, split = blockIdx.x;
+    // launch index -> (work item = row * nsplit + split, head group): the
+    // head groups of one item sit 8 apart (same XCD, adjacent dispatch)
+    const int L = blockIdx.x;
+    const int item = (L / (8 * hgroups)) * 8 + (L & 7);
+    const int hg = (L / 8) % hgroups;
+    if (item >= nitems) return;
+    const int row = item / nsplit, split = item - row * nsplit;
     const int64_t b = row / S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int h = wave * 16 + m;
+    const int h = hg * kHeadsPerBlock + wave * 16 + m;
+    const bool active = hg * kHeadsPerBlock + wave * 16 < Hq;   // wave has a real head
 
-    // Q^T operand: lane (n = head h, g) holds q[h][32 ks + 8 g .. +7].
+    const int j_begin = split * slots_per_split;
+    const int j_end = min(K, j_begin + slots_per_split);
+    const int count = j_end - j_begin;
+    const int ntiles = count > 0 ? (count + kTile - 1) / kTile : 0;
+    {
+        const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
+        for (int i = tid; i < ntiles * kTile; i += kMlaThreads) {
+            const int p = i < count ? irow[i] : -1;
+            sidx[i] = (p >= 0 && p < Lmax) ? p : -1;
+        }
+    }
+
+    // Q^T operand: lane (head h, chunk g) holds q[h][32 ks + 8 g .. +7].
     bf16x8 qreg[kDq / 32];
     {
-        const uint16_t* qh = q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+        const uint16_t* qh =
+            q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < kDq / 32; ++ks) {
             uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
@@ -61,54 +101,52 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             qreg[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
-
     v4f acc[kDl / 16];
 #pragma unroll
-    for (int t = 0; t < kDl / 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t2 = 0; t2 < kDl / 16; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     // l_run sums the float32 probabilities (for lse); lr_run sums the bf16
     // values that actually weight the latent rows (for the normalisation).
     float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
 
-    const int j_begin = split * slots_per_split;
-    const int j_end = min(K, j_begin + slots_per_split);
-    const int32_t* irow = idx + static_cast<int64_t>(row) * K;
     const uint16_t* lat_b = latent + b * lat_bs;
     const uint16_t* rope_b = rope + b * rope_bs;
+    __syncthreads();                               // sidx ready
 
-    for (int j0 = j_begin; j0 < j_end; j0 += kTile) {
-        __syncthreads();                     // previous tile fully consumed
-        if (tid < kTile) {
-            const int j = j0 + tid;
-            int p = j < j_end ? irow[j] : -1;
-            if (p < 0 || p >= Lmax) p = -1;
-            tile_pos[tid] = p;
-        }
-        __syncthreads();
-        // gather: 32 rows x 72 chunks of 16 B (64 latent + 8 rope chunks)
-        for (int c = tid; c < kTile * 72; c += kThreads) {
-            const int key = c / 72, part = c - key * 72;
-            const int p = tile_pos[key];
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (p >= 0) {
-                const uint16_t* src = part < 64 ? lat_b + p * lat_rs + part * 8
-                                                : rope_b + p * rope_rs + (part - 64) * 8;
-                v = *reinterpret_cast<const uint4*>(src);
-            }
-            *reinterpret_cast<uint4*>(Kt + key * kKtStride + part * 8) = v;
-        }
-        __syncthreads();
-        // transposed copy of the latent part: Vt[d][key]
-        for (int c = tid; c < kTile * 64; c += kThreads) {
-            const int key = c & 31, ch = c >> 5;
-            const uint4 v = *reinterpret_cast<const uint4*>(Kt + key * kKtStride + ch * 8);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    // Gather mapping: 8 threads per key row (wave w loads keys 8w..8w+7);
+    // thread sub = tid % 8 loads latent chunks sub + 8i (i < 8, 8 features
+    // each) and rope chunk sub: one row pointer per thread, immediate offsets,
+    // 128 contiguous bytes per 8 lanes. Unselected slots read row 0 and are
+    // zeroed (no divergent branches).
+    const int gkey = tid >> 3, gsub = tid & 7;
+    auto load_tile = [&](int t) {
+        const int p = sidx[t * kTile + gkey];
+        const int pc = p >= 0 ? p : 0;
+        const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
+        const uint16_t* rrow = rope_b + static_cast<int64_t>(pc) * rope_rs + gsub * 8;
+        uint4 G[9];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Vt[(ch * 8 + 2 * e) * kVtStride + key] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-                Vt[(ch * 8 + 2 * e + 1) * kVtStride + key] = static_cast<uint16_t>(w4[e] >> 16);
-            }
+        for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
+        G[8] = *reinterpret_cast<const uint4*>(rrow);
+        if (p < 0) {
+#pragma unroll
+            for (int i = 0; i < 9; ++i) G[i] = make_uint4(0u, 0u, 0u, 0u);
         }
+        uint16_t* dst = Kt + gkey * kKtStride + gsub * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 64 * i) = G[i];
+        *reinterpret_cast<uint4*>(dst + 512) = G[8];
+    };
+
+    // transposing-read addresses (bf16 units within the tile): lane 4e+q of
+    // group g reads features 4q.. of key 4g+e (k-step keys 0..15) and of key
+    // 16+4g+e (keys 16..31)
+    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kKtStride + 4 * (lane & 3);
+
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();                           // previous tile fully consumed
+        load_tile(t);
         __syncthreads();
+        if (!active) continue;
 
         // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
         v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -122,40 +160,54 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             s1 = mfma_bf16_16x16x32(a1, qreg[ks], s1);
         }
         float z[8];
+        float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = tile_pos[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
-            z[4 + i] = tile_pos[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
+            z[i] = sidx[t * kTile + 4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
+            z[4 + i] = sidx[t * kTile + 16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
         }
-        float tmax = z[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+        for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const bool live = m_new != -INFINITY;
-        const float corr = live ? exp2f(m_run - m_new) : 1.0f;
-        bf16x8 pv;
-        float psum = 0.0f, prsum = 0.0f;
+        // Lazy rescaling: probabilities are taken relative to a reference
+        // maximum m_run that only moves when the running maximum exceeds it
+        // by more than 8 (so p <= 2^8, exact enough in float and bf16).
+        if (tmax > m_run + 8.0f) {
+            const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
+            l_run *= corr;
+            lr_run *= corr;
+            m_run = tmax;
+            if (__ballot(corr != 1.0f)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float pe = live ? exp2f(z[i] - m_new) : 0.0f;
-            const __bf16 pb = static_cast<__bf16>(pe);
-            pv[i] = pb;
-            psum += pe;
-            prsum += static_cast<float>(pb);
+                for (int t2 = 0; t2 < kDl / 16; ++t2) acc[t2] *= corr;
+            }
         }
-        l_run = l_run * corr + psum;
-        lr_run = lr_run * corr + prsum;
-        m_run = m_new;
+        bf16x8 pv;
+        {
+            const bool live = m_run != -INFINITY;
+            float psum = 0.0f, prsum = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kDl / 16; ++t) {
-            acc[t] *= corr;
-            const int d = 16 * t + m;
-            const uint2 lo = *reinterpret_cast<const uint2*>(Vt + d * kVtStride + 4 * g);
-            const uint2 hi = *reinterpret_cast<const uint2*>(Vt + d * kVtStride + 16 + 4 * g);
-            const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            acc[t] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8, v), pv, acc[t]);
+            for (int i = 0; i < 8; ++i) {
+                const float pe = live ? exp2f(z[i] - m_run) : 0.0f;
+                const __bf16 pb = static_cast<__bf16>(pe);
+                pv[i] = pb;
+                psum += pe;
+                prsum += static_cast<float>(pb);
+            }
+            l_run += psum;
+            lr_run += prsum;
+        }
+        // O^T += V^T P^T, V^T operands by transposing reads of the K tile
+#pragma unroll
+        for (int t2 = 0; t2 < kDl / 16; ++t2) {
+            // whole-register bit casts: element-wise 16-bit extraction here
+            // was mis-scheduled into a lane-mixing permute
+            const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
+            const uint2 hi =
+                __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kKtStride + 16 * t2));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            acc[t2] = mfma_bf16_16x16x32(a, pv, acc[t2]);
         }
     }
 
@@ -163,17 +215,18 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     l_tot += __shfl_xor(l_tot, 32);
     float lr_tot = lr_run + __shfl_xor(lr_run, 16);
     lr_tot += __shfl_xor(lr_tot, 32);
-    if (h >= Hq) return;
+    if (!active || h >= Hq) return;
+    // lane holds O^T[16 t2 + 4 g + i][h], i = 0..3
     if (nsplit == 1) {
         const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
         uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
 #pragma unroll
-        for (int t = 0; t < kDl / 16; ++t) {
-            const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t][0] * inv)) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t][1] * inv)) << 16);
-            const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t][2] * inv)) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t][3] * inv)) << 16);
-            *reinterpret_cast<uint2*>(oh + 16 * t) = make_uint2(lo, hi);
+        for (int t2 = 0; t2 < kDl / 16; ++t2) {
+            const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][0] * inv)) |
+                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][1] * inv)) << 16);
+            const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][2] * inv)) |
+                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][3] * inv)) << 16);
+            *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
         }
         if (lse != nullptr && g == 0)
             lse[static_cast<int64_t>(row) * Hq + h] =
@@ -182,9 +235,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         const int64_t slot = (static_cast<int64_t>(row) * nsplit + split) * Hq + h;
         float* wo = ws_o + slot * kDl + 4 * g;
 #pragma unroll
-        for (int t = 0; t < kDl / 16; ++t)
-            *reinterpret_cast<float4*>(wo + 16 * t) =
-                make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        for (int t2 = 0; t2 < kDl / 16; ++t2)
+            *reinterpret_cast<float4*>(wo + 16 * t2) =
+                make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
         if (g == 0)
             *reinterpret_cast<float4*>(ws_ml + slot * 4) = make_float4(m_run, l_tot, lr_tot, 0.0f);
     }
@@ -193,7 +246,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 // Merge of key-split partials: block per (row, head), 128 threads x 4
 // features. The (m, l, lr) triples of all splits are staged in LDS first so
 // the partial-output loads below are independent and overlap.
-constexpr int kMaxSplits = 64;
 
 __global__ __launch_bounds__(128) void combine_kernel(int Hq, int nsplit,
                                                       const float* __restrict__ ws_o,
@@ -260,11 +312,12 @@ __global__ __launch_bounds__(128) void combine_kernel(int Hq, int nsplit,
 }
 
 // Split plan: enough (row, split) blocks to occupy the chip, each split a
-// whole number of 32-key tiles.
+// whole number of 32-key tiles and at least four of them (so the gather of
+// the next tile has a tile of MFMA work to hide behind), at most kMaxSplits.
 void mla_plan(int rows, int K, int* nsplit, int* slots_per_split) {
     const int tiles = (K + kTile - 1) / kTile;
     int ns = (256 + rows - 1) / rows;
-    int cap = tiles >= 2 ? tiles / 2 : 1;
+    int cap = tiles / 4;
     if (cap > kMaxSplits) cap = kMaxSplits;
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;
@@ -282,24 +335,6 @@ size_t mla_workspace_bytes(int rows, int Hq, int K) {
     return slots * kDl * sizeof(float) + slots * 4 * sizeof(float) + 256;
 }
 
-template <int NW>
-static hipError_t launch_mla_nw(dim3 grid, hipStream_t stream, int S, int Hq, int Lmax, int K,
-                                int sps, int ns, const uint16_t* q, const uint16_t* latent,
-                                int64_t lat_rs, int64_t lat_bs, const uint16_t* rope,
-                                int64_t rope_rs, int64_t rope_bs, const int32_t* idx,
-                                float scale_log2, uint16_t* out, float* lse, float* ws_o,
-                                float* ws_ml) {
-    // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_mla_kernel<NW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), kMlaLdsBytes, stream, S, Hq,
-                       Lmax, K, sps, ns, q, latent, lat_rs, lat_bs, rope, rope_rs, rope_bs, idx,
-                       scale_log2, out, lse, ws_o, ws_ml);
-    return hipGetLastError();
-}
-
 hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
@@ -314,18 +349,19 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
         ws_o = static_cast<float*>(workspace);
         ws_ml = ws_o + static_cast<size_t>(rows) * ns * Hq * kDl;
     }
+    // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&sparse_mla_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
+    if (attr != hipSuccess) return attr;
     const float scale_log2 = scale * 1.4426950408889634f;
-    const dim3 grid(ns, rows);
-    const int nw = (Hq + 15) / 16;
-    hipError_t e;
-#define DSA_MLA(NWV)                                                                           \
-    e = launch_mla_nw<NWV>(grid, stream, S, Hq, Lmax, K, sps, ns, q, latent, lat_rs, lat_bs,   \
-                           rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml)
-    if (nw <= 1) DSA_MLA(1);
-    else if (nw <= 2) DSA_MLA(2);
-    else if (nw <= 4) DSA_MLA(4);
-    else DSA_MLA(8);
-#undef DSA_MLA
+    const int nitems = rows * ns;
+    const int hgroups = (Hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int nblocks = ((nitems + 7) / 8) * 8 * hgroups;
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(nblocks), dim3(kMlaThreads), kMlaLdsBytes, stream,
+                       S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
+                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ns > 1) {
         hipLaunchKernelGGL(combine_kernel, dim3(rows * Hq), dim3(128), 0, stream, Hq, ns, ws_o,
