@@ -48,7 +48,80 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy five times (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn four rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and "
+                         "WRITE_SIZE of this benchmark, then of --calibrate-copy) into "
+                         "profiles/counters.json and exit")
     return ap.parse_args()
+
+
+# kernels launched by each call of the path (substrings of rocprofv3 kernel names)
+KERNELS_OF_CALL = {
+    "indexer": ["decode_score_kernel"],
+    "topk": ["topk_kernel"],
+    "sparse_mla": ["sparse_mla_kernel", "combine_kernel"],
+}
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload):
+    """HBM bytes per call launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the ratio of the true bytes of a 512 MiB device
+    copy to what the same counter reads for that copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        d = defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    d[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return d
+
+    def mean_of(d, sub):
+        vals = [v for k, vs in d.items() if sub in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named like {sub!r}")
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = float(512 << 20)
+    f_scale = copy_bytes / mean_of(per_kernel(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")[0]
+    w_scale = copy_bytes / mean_of(per_kernel(copy_write_csv, "WRITE_SIZE"), "copyBuffer")[0]
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    rec = {"source_hash": source_hash(), "workload": workload,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    for call, subs in KERNELS_OF_CALL.items():
+        ent = {"kernels": {}}
+        tf = tw = 0.0
+        for sub in subs:
+            fb, n = mean_of(fetch, sub)
+            wb, _ = mean_of(write, sub)
+            ent["kernels"][sub] = {"fetch_bytes": round(fb * f_scale), "write_bytes": round(wb * w_scale),
+                                   "dispatches": n}
+            tf += fb * f_scale
+            tw += wb * w_scale
+        ent.update(fetch_bytes=round(tf), write_bytes=round(tw), bytes_per_launch=round(tf + tw))
+        rec[call] = ent
+    out = os.path.join(ROOT, "profiles", "counters.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def calibrate_copy():
+    import torch
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 5}), flush=True)
 
 
 # ------------------------------------------------------------ byte model --
@@ -220,10 +293,16 @@ def main():
               "(batch rows and long rows would shard across GPUs as DESIGN.md describes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, workload=args.workload)
+        return
     import torch
 
     import synth
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     wl = synth.workload(args.workload)
     torch.cuda.set_device(0)
     st = setup(wl, args.replica_bytes)
