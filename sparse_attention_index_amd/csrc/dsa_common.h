@@ -53,6 +53,44 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// DPP lane moves. `old` is what a lane keeps when its source lane is outside
+// the row (row_shr) or its row is masked off (row_bcast).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the last lane of row 0 (of rows 0-1) is broadcast into
+// rows 1 and 3 (rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan_add(int x) {
+    x += dpp_move<kDppRowShr1, 0xF>(0, x);
+    x += dpp_move<kDppRowShr2, 0xF>(0, x);
+    x += dpp_move<kDppRowShr4, 0xF>(0, x);
+    x += dpp_move<kDppRowShr8, 0xF>(0, x);
+    x += dpp_move<kDppRowBcast15, 0xA>(0, x);
+    x += dpp_move<kDppRowBcast31, 0xC>(0, x);
+    return x;
+}
+
+// Max / min of a float over the wave, returned to every lane (the same
+// prefix pattern with max/min, then lane 63 read back as a scalar).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    constexpr int kNegInf = static_cast<int>(0xFF800000u);
+    int x = __float_as_int(v);
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowShr1, 0xF>(kNegInf, x))));
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowShr2, 0xF>(kNegInf, x))));
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowShr4, 0xF>(kNegInf, x))));
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowShr8, 0xF>(kNegInf, x))));
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowBcast15, 0xA>(kNegInf, x))));
+    x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_move<kDppRowBcast31, 0xC>(kNegInf, x))));
+    return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
+__device__ __forceinline__ float wave_min_dpp(float v) { return -wave_max_dpp(-v); }
+
 // Exact conversion of four packed E4M3 bytes to four bf16 values.
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t packed, bf16x2& lo, bf16x2& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false);

@@ -7,103 +7,91 @@
 // k_eff = min(K, n_valid) of them under (score desc, position asc), written
 // in ascending position order and padded with -1.
 //
-// One 1024-thread block per row; rows of up to kLdsKeys scores are cached
-// in LDS, longer rows are re-read from global memory by each walk.
-//  1. min/max of the row.
+// Rows of up to 16,384 scores: one block per row, the row held in
+// registers (16 scores per thread; wave w owns the contiguous run
+// [1024 w, 1024 w + 1024), lane l item j at 1024 w + 64 j + l).
+//  1. Load (adding +0.0 folds -0.0 into +0.0) and the row's min/max.
 //  2. Bucket pass: bucket(v) = floor((v - min) * 2048 / (max - min)), a
 //     monotone non-decreasing map, so every score in a higher bucket is
-//     larger than every score in a lower one. Score rows are smooth, so the
-//     LDS histogram sees little atomic contention (the bits of a float's
-//     exponent, by contrast, pile most scores into a few bins).
-//  3. The bucket holding the k_eff-th largest score is found by a block
-//     scan; its members (few) are collected and an exact three-pass radix
-//     select (11/11/10-bit digits of the order-preserving uint32 key, -0.0
-//     folded into +0.0) over them gives the threshold key T and how many
-//     keys equal to T are taken. Degenerate rows (all equal, infinities, an
-//     overfull bucket) run the radix select over the whole row instead.
-//  4. Compaction in position order: each wave owns a contiguous run and
-//     ranks ties and selections with ballots; two scans over the wave totals
-//     give each wave its starting ranks. Ascending output falls out.
+//     larger than every score in a lower one. An LDS histogram, scanned by
+//     one wave with DPP prefix sums, gives the bucket b* holding the
+//     k_eff-th largest score and the count G above it.
+//  3. Threshold key T (the k_eff-th largest order key, counted with
+//     multiplicity): when b* holds at most 64 scores one wave ranks them;
+//     otherwise an exact three-pass radix select (11/11/10-bit digits of the
+//     order key) runs over the scores of b*. Rows whose min/max give no
+//     usable bucket map (all equal, infinities) run it over the whole row.
+//     Every key above T is taken, and of the keys equal to T the ones with
+//     the lowest positions, as many as k_eff leaves.
+//  4. Ordered compaction: per-wave counts of keys above / equal to T (taken
+//     during step 3 when one wave ranked b*, else by a ballot pass) give each
+//     wave its output start, and each wave writes its taken positions in
+//     order. Ascending output falls out of the position order of the runs.
 #include "dsa_common.h"
 
 namespace dsa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kLdsKeys = 16384;
+constexpr int kRegItems = 16;                           // scores per thread
+constexpr int kRegMaxThreads = 1024;
+constexpr int kRegMaxWaves = kRegMaxThreads / kWave;
+constexpr int kLdsKeys = kRegItems * kRegMaxThreads;    // longest row of the one-block path
 constexpr int kBuckets = 2048;
-constexpr int kCandCap = 4096;
+constexpr int kRankCap = kWave;                         // bucket sizes ranked by one wave
 
-struct TopkShared {
-    uint32_t hist[2048];
-    int wsum[kTopkWaves];
-    float wmin[kTopkWaves];
-    float wmax[kTopkWaves];
+struct alignas(16) RegShared {
+    uint32_t hist[kBuckets];
+    uint32_t cand[kRankCap];
+    int cand_wave[kRankCap];
+    int wa[kRegMaxWaves];                   // per wave: keys above T
+    int wb[kRegMaxWaves];                   // per wave: keys equal to T
+    float wmin[kRegMaxWaves];
+    float wmax[kRegMaxWaves];
     uint32_t digit;
     int above;
     int ccount;
+    uint32_t T;
+    int gtc;
 };
 
-// Exclusive scan of one int per thread across the block (two barriers).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
+// Over hist[0..nbins) (nbins = 1024 or 2048): the bin holding the want-th
+// largest entry, counting from the top bin down, and how many entries lie in
+// higher bins, written to sh.digit / sh.above by wave 0 alone
+// (1 <= want <= total). Lane l sums the bins [nbins - nb (l+1), nbins - nb l);
+// a DPP prefix sum over the lanes finds the lane whose range holds the
+// want-th entry, and a second one over that range's bins (one per lane, top
+// first) finds the bin. The caller synchronises the block afterwards.
+template <int NBINS>
+__device__ __forceinline__ void find_digit_wave0(RegShared& sh, int want) {
+    constexpr int nb = NBINS / kWave;
+    const int lane = threadIdx.x & 63;
+    const int lo = NBINS - nb * (lane + 1);
+    int sum = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
+    for (int b = 0; b < nb; b += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sh.hist[lo + b]);
+        sum += static_cast<int>(v.x + v.y + v.z + v.w);
     }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int before = 0;
-#pragma unroll
-    for (int i = 0; i < kTopkWaves; ++i) before += (i < wave) ? wsum[i] : 0;
-    __syncthreads();
-    return before + incl - v;
+    const int incl = wave_incl_scan_add(sum);
+    const int excl = incl - sum;
+    // the lane whose range holds the want-th entry (exactly one: counts are
+    // non-negative and the total is at least want)
+    const uint64_t hit = __ballot(excl < want && incl >= want);
+    const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    const int lo_s = NBINS - nb * (src + 1);
+    const int ex_s = __builtin_amdgcn_readlane(excl, src);
+    // its nb bins, top one first, one per lane; a second prefix sum finds the bin
+    const int cb = lane < nb ? static_cast<int>(sh.hist[lo_s + nb - 1 - lane]) : 0;
+    const int in2 = ex_s + wave_incl_scan_add(cb);
+    const uint64_t hit2 = __ballot(lane < nb && in2 >= want && in2 - cb < want);
+    const int l2 = __ffsll(static_cast<unsigned long long>(hit2)) - 1;
+    if (lane == l2) {
+        sh.digit = static_cast<uint32_t>(lo_s + nb - 1 - lane);
+        sh.above = in2 - cb;
+    }
 }
 
-// Largest `want`-th key among n keys get(i): returns T and how many of the
-// keys equal to T belong to the top `want` (1 <= want <= n).
-template <typename Get>
-__device__ void radix_select(int n, Get get, int want, TopkShared& sh, uint32_t& T,
-                             int& remaining) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, mask = 0;
-    remaining = want;
-    const int shifts[3] = {21, 10, 0};
-    const uint32_t dmasks[3] = {0x7FFu, 0x7FFu, 0x3FFu};
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = shifts[pass];
-        const uint32_t dmask = dmasks[pass];
-        sh.hist[tid] = 0u;
-        sh.hist[tid + 1024] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t u = get(i);
-            if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        // thread t owns digits hi = 2047-2t and lo = 2046-2t (descending)
-        const uint32_t hi = 2047u - 2u * tid, lo = hi - 1u;
-        const int chi = static_cast<int>(sh.hist[hi]), clo = static_cast<int>(sh.hist[lo]);
-        const int above = block_exclusive_scan(chi + clo, sh.wsum);
-        if (above < remaining && above + chi + clo >= remaining) {
-            if (above + chi >= remaining) {
-                sh.digit = hi;
-                sh.above = above;
-            } else {
-                sh.digit = lo;
-                sh.above = above + chi;
-            }
-        }
-        __syncthreads();
-        prefix |= sh.digit << shift;
-        mask |= dmask << shift;
-        remaining -= sh.above;
-        __syncthreads();
-    }
-    T = prefix;
+__device__ __forceinline__ void clear_hist(RegShared& sh) {
+    for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) sh.hist[b] = 0u;
 }
 
 __device__ __forceinline__ int bucket_of(float v, float vmin, float scale) {
@@ -112,252 +100,228 @@ __device__ __forceinline__ int bucket_of(float v, float vmin, float scale) {
     return b < kBuckets - 1 ? b : kBuckets - 1;
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    int Lmax, int K, const float* __restrict__ scores, int64_t ld,
+// blockDim.x: a power of two from 64 to 1024 with 16 * blockDim.x >= Lmax.
+// speculative: issue the score loads of the whole row before pos[row] is
+// known (lower latency for a few rows; rows that turn out to keep all their
+// keys waste the loads, so many-row launches pass false).
+__global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
+    int Lmax, int K, int speculative, const float* __restrict__ scores, int64_t ld,
     const int32_t* __restrict__ pos, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-    __shared__ TopkShared sh;
-    __shared__ int w_gt[kTopkWaves], w_eq[kTopkWaves], w_off[kTopkWaves], w_eqb[kTopkWaves];
-    __shared__ uint32_t s_T;
-    __shared__ int s_rem;
-    extern __shared__ uint32_t dyn[];
-    uint32_t* ckey = dyn;                                         // [kCandCap]
-    int* cpos = reinterpret_cast<int*>(dyn + kCandCap);           // [kCandCap]
-    float* lvals = reinterpret_cast<float*>(dyn + 2 * kCandCap);  // [Lmax] when IN_LDS
-
+    __shared__ RegShared sh;
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = static_cast<int>(blockDim.x) >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const float* srow = scores + static_cast<int64_t>(row) * ld;
+    const int base = wave * (kWave * kRegItems) + lane;
+
+    // 1. load the scores (speculatively: every in-row score, before pos is
+    // known; scores past the causal end are masked below), min/max of the
+    // causal ones
+    float v[kRegItems];
+    if (speculative) {
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) {
+            const int i = base + kWave * j;
+            v[j] = i < Lmax ? srow[i] : 0.0f;
+        }
+    }
     const int p = pos[row];
     const int n = (p >= 0 && p < Lmax) ? p + 1 : 0;
     const int keff = n < K ? n : K;
     int32_t* out = idx + static_cast<int64_t>(row) * K;
-    const float* srow = scores + static_cast<int64_t>(row) * ld;
     if (count != nullptr && tid == 0) count[row] = keff;
-
     if (keff == n) {                        // everything causal is selected
-        for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? i : -1;
+        for (int i = tid; i < K; i += blockDim.x) out[i] = i < n ? i : -1;
         return;
     }
-    auto val = [&](int i) -> float { return IN_LDS ? lvals[i] : srow[i] + 0.0f; };
-    auto key = [&](int i) -> uint32_t { return float_order_key(val(i)); };
-
-    // every walk uses the same mapping: wave w owns the contiguous run
-    // [w0, w1) of the row and steps through it 64 positions at a time
-    const int wseg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
-    const int w0 = wave * wseg;
-    const int w1 = (w0 + wseg < n) ? w0 + wseg : n;
-
-    // walk 1: load (adding +0.0 folds -0.0 into +0.0), min/max; the loads of
-    // 16 steps are issued together so their latencies overlap
+    if (!speculative) {
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) {
+            const int i = base + kWave * j;
+            v[j] = i < n ? srow[i] : 0.0f;
+        }
+    }
     float vmin = INFINITY, vmax = -INFINITY;
-    for (int cb = w0; cb < w1; cb += 16 * 64) {
-        float v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int i = cb + 64 * j + lane;
-            v[j] = i < w1 ? srow[i] : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int i = cb + 64 * j + lane;
-            if (i < w1) {
-                const float x = v[j] + 0.0f;
-                if (IN_LDS) lvals[i] = x;
-                vmin = fminf(vmin, x);
-                vmax = fmaxf(vmax, x);
-            }
+    for (int j = 0; j < kRegItems; ++j) {
+        v[j] = v[j] + 0.0f;
+        if (base + kWave * j < n) {
+            vmin = fminf(vmin, v[j]);
+            vmax = fmaxf(vmax, v[j]);
         }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        vmin = fminf(vmin, __shfl_xor(vmin, o));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, o));
-    }
+    vmin = wave_min_dpp(vmin);
+    vmax = wave_max_dpp(vmax);
     if (lane == 0) {
         sh.wmin[wave] = vmin;
         sh.wmax[wave] = vmax;
-        w_eq[wave] = 0;
-        w_gt[wave] = 0;
+        sh.wa[wave] = 0;
+        sh.wb[wave] = 0;
     }
     if (tid == 0) sh.ccount = 0;
-    sh.hist[tid] = 0u;
-    sh.hist[tid + 1024] = 0u;
+    clear_hist(sh);
     __syncthreads();
     vmin = sh.wmin[0];
     vmax = sh.wmax[0];
-#pragma unroll
-    for (int i = 1; i < kTopkWaves; ++i) {
-        vmin = fminf(vmin, sh.wmin[i]);
-        vmax = fmaxf(vmax, sh.wmax[i]);
+    for (int w = 1; w < nw; ++w) {
+        vmin = fminf(vmin, sh.wmin[w]);
+        vmax = fmaxf(vmax, sh.wmax[w]);
     }
-    const float range = vmax - vmin;
-    const float scale = static_cast<float>(kBuckets) / range;
-    const bool bucketed = vmax > vmin && isfinite(range) && isfinite(scale) && scale > 0.0f;
 
-    uint32_t T = 0;
-    int remaining = 0;
-    int bstar = -1;                         // bucketed rows: the threshold bucket
-    if (bucketed) {
-        // walk 2: bucket histogram
-        for (int c = w0; c < w1; c += 64) {
-            const int i = c + lane;
-            if (i < w1) atomicAdd(&sh.hist[bucket_of(val(i), vmin, scale)], 1u);
-        }
-        __syncthreads();
-        // bucket of the k_eff-th largest score (thread t owns 2047-2t, 2046-2t)
-        const uint32_t hi = 2047u - 2u * tid, lo = hi - 1u;
-        const int chi = static_cast<int>(sh.hist[hi]), clo = static_cast<int>(sh.hist[lo]);
-        const int above = block_exclusive_scan(chi + clo, sh.wsum);
-        if (above < keff && above + chi + clo >= keff) {
-            if (above + chi >= keff) {
-                sh.digit = hi;
-                sh.above = above;
-            } else {
-                sh.digit = lo;
-                sh.above = above + chi;
-            }
-        }
-        __syncthreads();
-        bstar = static_cast<int>(sh.digit);
-        const int rem = keff - sh.above;
-        const int c = static_cast<int>(sh.hist[bstar]);
-        if (c <= kCandCap) {
-            // walk 3: per-wave count above b*, members of b* to the list
-            int gt = 0;
-            for (int c0 = w0; c0 < w1; c0 += 64) {
-                const int i = c0 + lane;
-                const float v = i < w1 ? val(i) : 0.0f;
-                const int bk = i < w1 ? bucket_of(v, vmin, scale) : -1;
-                gt += bk > bstar ? 1 : 0;
-                const bool is_c = bk == bstar;
-                const uint64_t m = __ballot(is_c);
-                int base = 0;
-                if (lane == 0 && m) base = atomicAdd(&sh.ccount, __popcll(m));
-                base = __shfl(base, 0);
-                if (is_c) {
-                    ckey[base + __popcll(m & lt_mask)] = float_order_key(v);
-                    cpos[base + __popcll(m & lt_mask)] = i;
-                }
-            }
+    uint32_t T;                             // threshold order key
+    int eq_take;                            // keys equal to T that are taken
+    bool counted = false;                   // sh.wa / sh.wb already hold the per-wave counts
+    if (!(vmax > vmin)) {                   // all causal scores equal
+        T = float_order_key(vmax);
+        eq_take = keff;
+    } else {
+        const float range = vmax - vmin;
+        const float scale = static_cast<float>(kBuckets) / range;
+        const bool bucketed = isfinite(range) && isfinite(scale) && scale > 0.0f;
+        int want = keff;
+        int bstar = -1;
+        if (bucketed) {
+            // 2. bucket histogram, threshold bucket (-1: not causal)
+            int bk[kRegItems];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) gt += __shfl_xor(gt, o);
-            if (lane == 0) w_gt[wave] = gt;
+            for (int j = 0; j < kRegItems; ++j) {
+                bk[j] = base + kWave * j < n ? bucket_of(v[j], vmin, scale) : -1;
+                if (bk[j] >= 0) atomicAdd(&sh.hist[bk[j]], 1u);
+            }
             __syncthreads();
-            if (c <= 64) {
-                // exact ranking inside one wave: (key desc, position asc)
-                if (wave == 0) {
-                    const uint32_t k = lane < c ? ckey[lane] : 0u;
-                    const int ps = lane < c ? cpos[lane] : 0x7FFFFFFF;
-                    int rank = 0, gtk = 0;
-                    for (int j = 0; j < c; ++j) {
-                        const uint32_t kj = __shfl(k, j);
-                        const int pj = __shfl(ps, j);
-                        rank += (kj > k || (kj == k && pj < ps)) ? 1 : 0;
-                    }
-                    const uint64_t hit = __ballot(lane < c && rank == rem - 1);
-                    const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-                    const uint32_t Tk = __shfl(k, src);
-                    gtk = (lane < c && k > Tk) ? 1 : 0;
+            if (wave == 0) find_digit_wave0<kBuckets>(sh, keff);
+            __syncthreads();
+            bstar = static_cast<int>(sh.digit);
+            want = keff - sh.above;
+            const int c = static_cast<int>(sh.hist[bstar]);
+            if (c <= kRankCap) {
+                // 3a. per wave: keys in buckets above b* (all above T);
+                // members of b* (key, wave) to LDS; one wave ranks them and
+                // adds their counts above / equal to T to their waves
+                int above_w = 0;
 #pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) gtk += __shfl_xor(gtk, o);
+                for (int j = 0; j < kRegItems; ++j) {
+                    above_w += __popcll(__ballot(bk[j] > bstar));
+                    const bool is_c = bk[j] == bstar;
+                    const uint64_t m = __ballot(is_c);
+                    if (m != 0ull) {
+                        int at = 0;
+                        if (lane == 0) at = atomicAdd(&sh.ccount, __popcll(m));
+                        at = __shfl(at, 0);
+                        if (is_c) {
+                            const int slot = at + __popcll(m & lt_mask);
+                            sh.cand[slot] = float_order_key(v[j]);
+                            sh.cand_wave[slot] = wave;
+                        }
+                    }
+                }
+                if (lane == 0) atomicAdd(&sh.wa[wave], above_w);
+                __syncthreads();
+                if (wave == 0) {
+                    const uint32_t k = lane < c ? sh.cand[lane] : 0u;
+                    int rank = 0;
+                    for (int jj = 0; jj < c; ++jj) {
+                        const uint32_t kj = static_cast<uint32_t>(
+                            __builtin_amdgcn_readlane(static_cast<int>(k), jj));
+                        rank += (kj > k || (kj == k && jj < lane)) ? 1 : 0;
+                    }
+                    const uint64_t hit = __ballot(lane < c && rank == want - 1);
+                    const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+                    const uint32_t Tk = static_cast<uint32_t>(
+                        __builtin_amdgcn_readlane(static_cast<int>(k), src));
+                    if (lane < c) {
+                        if (k > Tk) atomicAdd(&sh.wa[sh.cand_wave[lane]], 1);
+                        else if (k == Tk) atomicAdd(&sh.wb[sh.cand_wave[lane]], 1);
+                    }
+                    const int gtc = __popcll(__ballot(lane < c && k > Tk));
                     if (lane == 0) {
-                        s_T = Tk;
-                        s_rem = rem - gtk;
+                        sh.T = Tk;
+                        sh.gtc = gtc;
                     }
                 }
                 __syncthreads();
-                T = s_T;
-                remaining = s_rem;
-            } else {
-                radix_select(c, [&](int i) { return ckey[i]; }, rem, sh, T, remaining);
+                T = sh.T;
+                eq_take = want - sh.gtc;
+                counted = true;
             }
-            // per-wave keys above T / equal to T inside bucket b*
-            for (int i = tid; i < c; i += kTopkThreads) {
-                const int wv = cpos[i] / wseg;
-                if (ckey[i] > T) atomicAdd(&w_gt[wv], 1);
-                else if (ckey[i] == T) atomicAdd(&w_eq[wv], 1);
+        }
+        if (!counted) {
+            // 3b. radix select over the scores of b* (or of the whole row)
+            uint32_t memb = 0u;
+#pragma unroll
+            for (int j = 0; j < kRegItems; ++j) {
+                const bool in = base + kWave * j < n &&
+                                (bstar < 0 || bucket_of(v[j], vmin, scale) == bstar);
+                memb |= in ? (1u << j) : 0u;
             }
-            __syncthreads();
-        } else {
-            bstar = -1;                     // overfull bucket: plain compaction below
+            uint32_t prefix = 0u, mask = 0u;
+#pragma unroll 1
+            for (int pass = 0; pass < 3; ++pass) {
+                const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+                const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+                __syncthreads();            // previous readers of hist / digit are done
+                clear_hist(sh);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < kRegItems; ++j) {
+                    const uint32_t uj = float_order_key(v[j]);
+                    if (((memb >> j) & 1u) && (uj & mask) == prefix)
+                        atomicAdd(&sh.hist[(uj >> shift) & dmask], 1u);
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    if (pass == 2) find_digit_wave0<1024>(sh, want);
+                    else find_digit_wave0<kBuckets>(sh, want);
+                }
+                __syncthreads();
+                prefix |= sh.digit << shift;
+                mask |= dmask << shift;
+                want -= sh.above;
+            }
+            T = prefix;
+            eq_take = want;
         }
     }
-    if (bstar < 0) {
-        if (!bucketed) {
-            if (!(vmax > vmin)) {           // all scores equal
-                T = float_order_key(vmax);
-                remaining = keff;
-            } else {
-                radix_select(n, key, keff, sh, T, remaining);
-            }
-        } else {
-            radix_select(n, key, keff, sh, T, remaining);
-        }
-        // counting walk: per-wave keys above T / equal to T
-        int gt = 0, eq = 0;
-        for (int c0 = w0; c0 < w1; c0 += 64) {
-            const int i = c0 + lane;
-            const uint32_t u = i < w1 ? key(i) : 0u;
-            gt += (i < w1 && u > T) ? 1 : 0;
-            eq += (i < w1 && u == T) ? 1 : 0;
-        }
+
+    // 4. ordered compaction
+    if (!counted) {
+        int gtw = 0, eqw = 0;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            gt += __shfl_xor(gt, o);
-            eq += __shfl_xor(eq, o);
+        for (int j = 0; j < kRegItems; ++j) {
+            const bool ok = base + kWave * j < n;
+            const uint32_t uk = float_order_key(v[j]);
+            gtw += __popcll(__ballot(ok && uk > T));
+            eqw += __popcll(__ballot(ok && uk == T));
         }
         if (lane == 0) {
-            w_gt[wave] = gt;
-            w_eq[wave] = eq;
+            sh.wa[wave] = gtw;
+            sh.wb[wave] = eqw;
         }
         __syncthreads();
     }
-    // output start of every wave's run and its earlier ties
-    if (tid == 0) {
-        int o = 0, eb = 0;
-        for (int w = 0; w < kTopkWaves; ++w) {
-            w_off[w] = o;
-            w_eqb[w] = eb;
-            o += w_gt[w] + min(max(remaining - eb, 0), w_eq[w]);
-            eb += w_eq[w];
-        }
+    int gp = 0, ep = 0;
+    for (int w = 0; w < wave; ++w) {
+        gp += sh.wa[w];
+        ep += sh.wb[w];
     }
-    __syncthreads();
-    // walk 4: write the taken positions in order
-    {
-        int e = w_eqb[wave];
-        int o = w_off[wave];
-        for (int c0 = w0; c0 < w1; c0 += 64) {
-            const int i = c0 + lane;
-            bool take = false, eq = false;
-            if (i < w1) {
-                if (bstar >= 0) {
-                    const float v = val(i);
-                    const int bk = bucket_of(v, vmin, scale);
-                    if (bk > bstar) {
-                        take = true;
-                    } else if (bk == bstar) {
-                        const uint32_t u = float_order_key(v);
-                        take = u > T;
-                        eq = u == T;
-                    }
-                } else {
-                    const uint32_t u = key(i);
-                    take = u > T;
-                    eq = u == T;
-                }
-            }
-            const uint64_t eqm = __ballot(eq);
-            if (eq) take = e + __popcll(eqm & lt_mask) < remaining;
-            e += __popcll(eqm);
-            const uint64_t tm = __ballot(take);
-            const int slot = o + __popcll(tm & lt_mask);
-            if (take && slot < keff) out[slot] = i;
-            o += __popcll(tm);
-        }
+    int o = gp + (ep < eq_take ? ep : eq_take);
+    int e = ep;
+#pragma unroll
+    for (int j = 0; j < kRegItems; ++j) {
+        const int i = base + kWave * j;
+        const bool ok = i < n;
+        const uint32_t uk = float_order_key(v[j]);
+        const bool eq = ok && uk == T;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = (ok && uk > T) || (eq && e + __popcll(eqm & lt_mask) < eq_take);
+        e += __popcll(eqm);
+        const uint64_t tm = __ballot(take);
+        const int slot = o + __popcll(tm & lt_mask);
+        if (take && slot < K) out[slot] = i;
+        o += __popcll(tm);
     }
-    for (int i = keff + tid; i < K; i += kTopkThreads) out[i] = -1;
+    for (int i = keff + tid; i < K; i += blockDim.x) out[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -725,15 +689,11 @@ hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t l
                            pos, ws, idx, count);
         return hipGetLastError();
     }
-    const size_t bytes = sizeof(uint32_t) * (2 * kCandCap + static_cast<size_t>(Lmax));
-    // thread-safe one-time opt-in to more than 64 KiB of LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&topk_kernel<true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(sizeof(uint32_t) * (2 * kCandCap + kLdsKeys)));
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((topk_kernel<true>), dim3(rows), dim3(kTopkThreads), bytes, stream, Lmax, K,
-                       scores, ld, pos, idx, count);
+    int nt = kWave;
+    while (nt * kRegItems < Lmax) nt <<= 1;
+    const int speculative = rows <= 256 ? 1 : 0;
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(nt), 0, stream, Lmax, K, speculative, scores,
+                       ld, pos, idx, count);
     return hipGetLastError();
 }
 
