@@ -8,16 +8,16 @@
 //   out[h] = sum_j softmax(z)_j latent[p_j],  lse[h] = log sum_j exp(z_j).
 //
 // Design: one block of 4 waves serves 64 heads (16 per wave) of one query
-// row over a contiguous range ("split") of its selected positions; two such
-// blocks share a CU, so one block's gather latency hides behind the other's
-// MFMA work. The two head-group blocks of a (row, split) get launch indices
-// 8 apart in one 1-D grid: the same XCD and back to back in dispatch order,
-// so the second block's gather is served by that XCD's L2. The split's
-// index list is staged in LDS once. Selected rows are gathered 32 at a time
-// (8 threads per row) into an LDS tile K [32][576] (row-major, padded).
+// row over a contiguous range ("split") of its selected positions. The two
+// head-group blocks of a (row, split) get launch indices 8 apart in one 1-D
+// grid: the same XCD and back to back in dispatch order, so the second
+// block's gather is served by that XCD's L2. The split's index list is
+// staged in LDS once. Selected rows are gathered 32 at a time (8 threads
+// per row) into an LDS tile K [32][576] (row-major, padded).
 // Per wave:
 //   S^T = K Q^T       bf16 MFMA 16x16x32, M = keys (2 tiles of 16), N = the
-//                     wave's 16 heads, K = features; Q^T stays in VGPRs.
+//                     wave's 16 heads, K = features, four independent
+//                     accumulation chains; Q^T stays in VGPRs.
 //   online softmax    per head (one head per lane column, four lanes per
 //                     head), in log2 units, against a reference maximum that
 //                     moves only when the running maximum passes it by 8:
@@ -30,8 +30,15 @@
 //                     LDS read ds_read_b64_tr_b16: within each 16-lane group,
 //                     lane 4e+q addresses features 4q..4q+3 of key e and lane
 //                     i receives feature i of keys 0..3.
+// Two builds of the kernel: when the grid has at most one block per CU
+// (few query rows), one wave per SIMD has the CU to itself, so the gather of
+// the next tile is held in registers while the current one is computed and
+// the LDS operand reads run several MFMAs ahead; with more blocks, two
+// blocks share a CU and hide each other's latencies instead.
 // With several splits per row the unnormalised partials (O, m, l) go to the
-// workspace and combine_kernel merges them with the log-sum-exp rule.
+// workspace, each wave's 16 x 512 block stored exactly as its registers
+// hold it (every store instruction writes 1 KiB of consecutive bytes), and
+// combine_kernel merges them with the log-sum-exp rule.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -45,7 +52,14 @@ constexpr int kMlaThreads = 256;        // 4 waves x 16 heads
 constexpr int kHeadsPerBlock = 64;
 constexpr int kMaxSlots = 2048;         // selected positions per split, at most
 constexpr int kMaxSplits = 64;
+constexpr int kT2 = kDl / 16;           // 16-feature output tiles per head
 constexpr size_t kMlaLdsBytes = sizeof(uint16_t) * kTile * kKtStride + sizeof(int) * kMaxSlots;
+
+// Scheduling-group hints (no instructions): the next `n` instructions of a
+// kind (LDS reads / MFMAs) are placed in the order of these calls, which
+// keeps the LDS operand reads of a tile a fixed number of MFMAs ahead.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+#define DSA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
     typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -54,7 +68,8 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))));
 }
 
-__global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
+template <bool PIPE>
+__global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
@@ -74,8 +89,9 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
     const int64_t b = row / S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int h = hg * kHeadsPerBlock + wave * 16 + m;
-    const bool active = hg * kHeadsPerBlock + wave * 16 < Hq;   // wave has a real head
+    const int wg = hg * (kHeadsPerBlock / 16) + wave;             // 16-head group
+    const int h = wg * 16 + m;
+    const bool active = wg * 16 < Hq;                             // wave has a real head
 
     const int j_begin = split * slots_per_split;
     const int j_end = min(K, j_begin + slots_per_split);
@@ -101,9 +117,9 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
             qreg[ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
-    v4f acc[kDl / 16];
+    v4f acc[kT2];
 #pragma unroll
-    for (int t2 = 0; t2 < kDl / 16; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t2 = 0; t2 < kT2; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     // l_run sums the float32 probabilities (for lse); lr_run sums the bf16
     // values that actually weight the latent rows (for the normalisation).
     float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
@@ -118,16 +134,18 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
     // 128 contiguous bytes per 8 lanes. Unselected slots read row 0 and are
     // zeroed (no divergent branches).
     const int gkey = tid >> 3, gsub = tid & 7;
-    auto load_tile = [&](int t) {
+    uint4 G[9];
+    auto fetch_tile = [&](int t) {
         const int p = sidx[t * kTile + gkey];
         const int pc = p >= 0 ? p : 0;
         const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
         const uint16_t* rrow = rope_b + static_cast<int64_t>(pc) * rope_rs + gsub * 8;
-        uint4 G[9];
 #pragma unroll
         for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
         G[8] = *reinterpret_cast<const uint4*>(rrow);
-        if (p < 0) {
+    };
+    auto store_tile = [&](int t) {
+        if (sidx[t * kTile + gkey] < 0) {
 #pragma unroll
             for (int i = 0; i < 9; ++i) G[i] = make_uint4(0u, 0u, 0u, 0u);
         }
@@ -141,24 +159,63 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
     // group g reads features 4q.. of key 4g+e (k-step keys 0..15) and of key
     // 16+4g+e (keys 16..31)
     const int tr_off = (4 * g + ((lane >> 2) & 3)) * kKtStride + 4 * (lane & 3);
+    auto read_v = [&](int t2) -> bf16x8 {
+        // whole-register bit casts: element-wise 16-bit extraction here was
+        // mis-scheduled into a lane-mixing permute
+        const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
+        const uint2 hi =
+            __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kKtStride + 16 * t2));
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    const uint16_t* ka_row = Kt + m * kKtStride + 8 * g;
+    const uint16_t* kb_row = Kt + (16 + m) * kKtStride + 8 * g;
 
+    // LDS operand reads in flight ahead of their MFMAs
+    constexpr int kPipe = PIPE ? 4 : 2;       // S: K-operand pairs
+    constexpr int kPipeV = PIPE ? 6 : 3;      // O: V^T operands
+    if (PIPE && ntiles > 0) fetch_tile(0);
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();                           // previous tile fully consumed
-        load_tile(t);
+        if (!PIPE) fetch_tile(t);
+        store_tile(t);
         __syncthreads();
+        if (PIPE && t + 1 < ntiles) fetch_tile(t + 1);
         if (!active) continue;
 
         // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
-        v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        // Even and odd k-steps accumulate separately (four MFMA chains).
+        v4f s0, s1;
+        {
+            v4f c0[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            v4f c1[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            bf16x8 a0[kPipe], a1[kPipe];
 #pragma unroll
-        for (int ks = 0; ks < kDq / 32; ++ks) {
-            const bf16x8 a0 =
-                *reinterpret_cast<const bf16x8*>(Kt + m * kKtStride + ks * 32 + 8 * g);
-            const bf16x8 a1 =
-                *reinterpret_cast<const bf16x8*>(Kt + (16 + m) * kKtStride + ks * 32 + 8 * g);
-            s0 = mfma_bf16_16x16x32(a0, qreg[ks], s0);
-            s1 = mfma_bf16_16x16x32(a1, qreg[ks], s1);
+            for (int d = 0; d < kPipe; ++d) {
+                a0[d] = *reinterpret_cast<const bf16x8*>(ka_row + d * 32);
+                a1[d] = *reinterpret_cast<const bf16x8*>(kb_row + d * 32);
+            }
+            DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipe);
+#pragma unroll
+            for (int ks = 0; ks < kDq / 32; ++ks) {
+                const int sl = ks % kPipe;
+                c0[ks & 1] = mfma_bf16_16x16x32(a0[sl], qreg[ks], c0[ks & 1]);
+                c1[ks & 1] = mfma_bf16_16x16x32(a1[sl], qreg[ks], c1[ks & 1]);
+                DSA_SCHED_GROUP(kSchedMfma, 2);
+                if (ks + kPipe < kDq / 32) {
+                    a0[sl] = *reinterpret_cast<const bf16x8*>(ka_row + (ks + kPipe) * 32);
+                    a1[sl] = *reinterpret_cast<const bf16x8*>(kb_row + (ks + kPipe) * 32);
+                    DSA_SCHED_GROUP(kSchedDsRead, 2);
+                }
+            }
+            s0 = c0[0] + c0[1];
+            s1 = c1[0] + c1[1];
         }
+        // the first V^T operands are read while the softmax runs
+        bf16x8 va[kPipeV];
+#pragma unroll
+        for (int d = 0; d < kPipeV; ++d) va[d] = read_v(d);
+        DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipeV);
+
         float z[8];
         float tmax = -INFINITY;
 #pragma unroll
@@ -180,7 +237,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
             m_run = tmax;
             if (__ballot(corr != 1.0f)) {
 #pragma unroll
-                for (int t2 = 0; t2 < kDl / 16; ++t2) acc[t2] *= corr;
+                for (int t2 = 0; t2 < kT2; ++t2) acc[t2] *= corr;
             }
         }
         bf16x8 pv;
@@ -189,7 +246,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
             float psum = 0.0f, prsum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float pe = live ? exp2f(z[i] - m_run) : 0.0f;
+                const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run) : 0.0f;
                 const __bf16 pb = static_cast<__bf16>(pe);
                 pv[i] = pb;
                 psum += pe;
@@ -200,14 +257,14 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
         }
         // O^T += V^T P^T, V^T operands by transposing reads of the K tile
 #pragma unroll
-        for (int t2 = 0; t2 < kDl / 16; ++t2) {
-            // whole-register bit casts: element-wise 16-bit extraction here
-            // was mis-scheduled into a lane-mixing permute
-            const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
-            const uint2 hi =
-                __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kKtStride + 16 * t2));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc[t2] = mfma_bf16_16x16x32(a, pv, acc[t2]);
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const int sl = t2 % kPipeV;
+            acc[t2] = mfma_bf16_16x16x32(va[sl], pv, acc[t2]);
+            DSA_SCHED_GROUP(kSchedMfma, 1);
+            if (t2 + kPipeV < kT2) {
+                va[sl] = read_v(t2 + kPipeV);
+                DSA_SCHED_GROUP(kSchedDsRead, 2);
+            }
         }
     }
 
@@ -215,13 +272,14 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
     l_tot += __shfl_xor(l_tot, 32);
     float lr_tot = lr_run + __shfl_xor(lr_run, 16);
     lr_tot += __shfl_xor(lr_tot, 32);
-    if (!active || h >= Hq) return;
+    if (!active) return;
     // lane holds O^T[16 t2 + 4 g + i][h], i = 0..3
     if (nsplit == 1) {
+        if (h >= Hq) return;
         const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
         uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
 #pragma unroll
-        for (int t2 = 0; t2 < kDl / 16; ++t2) {
+        for (int t2 = 0; t2 < kT2; ++t2) {
             const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][0] * inv)) |
                                 (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][1] * inv)) << 16);
             const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][2] * inv)) |
@@ -232,83 +290,112 @@ __global__ __launch_bounds__(kMlaThreads, 2) void sparse_mla_kernel(
             lse[static_cast<int64_t>(row) * Hq + h] =
                 l_tot > 0.0f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
     } else {
-        const int64_t slot = (static_cast<int64_t>(row) * nsplit + split) * Hq + h;
-        float* wo = ws_o + slot * kDl + 4 * g;
+        // partial block of (row, split, 16-head group): [t2][lane] float4
+        const int nwg = (Hq + 15) / 16;
+        const int64_t blk = (static_cast<int64_t>(row) * nsplit + split) * nwg + wg;
+        float* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
 #pragma unroll
-        for (int t2 = 0; t2 < kDl / 16; ++t2)
-            *reinterpret_cast<float4*>(wo + 16 * t2) =
+        for (int t2 = 0; t2 < kT2; ++t2)
+            *reinterpret_cast<float4*>(wo + t2 * 256) =
                 make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
-        if (g == 0)
-            *reinterpret_cast<float4*>(ws_ml + slot * 4) = make_float4(m_run, l_tot, lr_tot, 0.0f);
+        if (g == 0 && h < Hq)
+            *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
+                make_float4(m_run, l_tot, lr_tot, 0.0f);
     }
 }
 
-// Merge of key-split partials: block per (row, head), 128 threads x 4
-// features. The (m, l, lr) triples of all splits are staged in LDS first so
-// the partial-output loads below are independent and overlap.
+// DPP prefix sum of a float over the wave (same lane moves as the integer
+// scan); lane 63 ends up with the total.
+__device__ __forceinline__ float wave_incl_sum_f(float v) {
+    int x = __float_as_int(v);
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr1, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr2, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr4, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr8, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowBcast15, 0xA>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowBcast31, 0xC>(0, x)));
+    return __int_as_float(x);
+}
 
-__global__ __launch_bounds__(128) void combine_kernel(int Hq, int nsplit,
+// Merge of key-split partials. Block = (row, 16-head group, quarter of the
+// 512 features), 256 threads: wave w covers feature tiles t2 = 8 quarter +
+// 2 w + {0, 1}; lane l = 16 g + m reads exactly what lane l of the producing
+// wave stored (head m, features 16 t2 + 4 g .. +3), so each partial load of
+// a wave is 1 KiB of consecutive bytes. Per head, wave w first turns the
+// (m, l, lr) triples of all splits (one split per lane) into weights
+// 2^(m_s - M) in LDS and the totals L, Lr.
+constexpr int kCombineQuarters = 4;
+
+__global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
                                                       const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
-    __shared__ float4 ml[kMaxSplits];
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float s_M, s_L, s_Lr;
-    const int rh = blockIdx.x;
-    const int64_t row = rh / Hq;
-    const int h = rh - static_cast<int>(row * Hq);
-    const int tid = threadIdx.x;
-    const int d = tid * 4;
-    if (tid < nsplit)
-        ml[tid] = *reinterpret_cast<const float4*>(ws_ml + ((row * nsplit + tid) * Hq + h) * 4);
-    __syncthreads();
-    if (tid < 64) {
-        float M = -INFINITY;
-        for (int s = tid; s < nsplit; s += 64) M = fmaxf(M, ml[s].x);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float L = 0.0f, Lr = 0.0f;
-        for (int s = tid; s < nsplit; s += 64) {
-            const float e = (ml[s].x == -INFINITY) ? 0.0f : exp2f(ml[s].x - M);
-            wgt[s] = e;
-            L += ml[s].y * e;
-            Lr += ml[s].z * e;
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            L += __shfl_xor(L, o);
-            Lr += __shfl_xor(Lr, o);
-        }
-        if (tid == 0) {
-            s_M = M;
-            s_L = L;
-            s_Lr = Lr;
+    __shared__ float wgt[kMaxSplits][16];
+    __shared__ float s_L[16], s_Lr[16], s_M[16];
+    const int nwg = (Hq + 15) / 16;
+    const int quarter = blockIdx.x % kCombineQuarters;
+    const int wg = (blockIdx.x / kCombineQuarters) % nwg;
+    const int64_t row = blockIdx.x / (kCombineQuarters * nwg);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // weights: wave w handles heads 4w .. 4w+3 of the group
+    for (int mm = 4 * wave; mm < 4 * wave + 4; ++mm) {
+        const int h = wg * 16 + mm;
+        if (h >= Hq) break;                        // wave-uniform
+        float4 ml = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+        if (lane < nsplit)
+            ml = *reinterpret_cast<const float4*>(ws_ml + ((row * nsplit + lane) * Hq + h) * 4);
+        const float M = wave_max_dpp(ml.x);
+        const float e = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
+        if (lane < nsplit) wgt[lane][mm] = e;
+        const float Ls = wave_incl_sum_f(ml.y * e);
+        const float Lrs = wave_incl_sum_f(ml.z * e);
+        if (lane == 63) {
+            s_M[mm] = M;
+            s_L[mm] = Ls;
+            s_Lr[mm] = Lrs;
         }
     }
     __syncthreads();
-    const float* base = ws_o + (row * nsplit * Hq + h) * kDl + d;
-    const int64_t sstride = static_cast<int64_t>(Hq) * kDl;
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
+    const int m = lane & 15, g = lane >> 4;
+    const int h = wg * 16 + m;
+    const int t2a = quarter * (kT2 / kCombineQuarters) + 2 * wave;
+    const float* base = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + lane * 4;
+    const int64_t sstride = static_cast<int64_t>(nwg) * kT2 * 64 * 4;
+    float4 a0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a1 = a0;
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
-        const float e = wgt[s];
-        const float4 v = *reinterpret_cast<const float4*>(base + s * sstride);
-        acc.x += e * v.x;
-        acc.y += e * v.y;
-        acc.z += e * v.z;
-        acc.w += e * v.w;
+        const float e = wgt[s][m];
+        const float4 v0 = *reinterpret_cast<const float4*>(base + s * sstride + t2a * 256);
+        const float4 v1 = *reinterpret_cast<const float4*>(base + s * sstride + (t2a + 1) * 256);
+        a0.x += e * v0.x;
+        a0.y += e * v0.y;
+        a0.z += e * v0.z;
+        a0.w += e * v0.w;
+        a1.x += e * v1.x;
+        a1.y += e * v1.y;
+        a1.z += e * v1.z;
+        a1.w += e * v1.w;
     }
-    const float Lr = s_Lr;
+    if (h >= Hq) return;
+    const float Lr = s_Lr[m];
     const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
-    uint16_t* oh = out + (row * Hq + h) * kDl + d;
-    const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc.x * inv)) |
-                        (static_cast<uint32_t>(float_to_bf16_bits(acc.y * inv)) << 16);
-    const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc.z * inv)) |
-                        (static_cast<uint32_t>(float_to_bf16_bits(acc.w * inv)) << 16);
-    *reinterpret_cast<uint2*>(oh) = make_uint2(lo, hi);
-    if (lse != nullptr && tid == 0)
-        lse[row * Hq + h] = s_L > 0.0f ? s_M * 0.69314718055994531f + logf(s_L) : -INFINITY;
+    uint16_t* oh = out + (row * Hq + h) * kDl + 4 * g;
+    auto pack = [&](float4 a) {
+        const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(a.x * inv)) |
+                            (static_cast<uint32_t>(float_to_bf16_bits(a.y * inv)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(a.z * inv)) |
+                            (static_cast<uint32_t>(float_to_bf16_bits(a.w * inv)) << 16);
+        return make_uint2(lo, hi);
+    };
+    *reinterpret_cast<uint2*>(oh + 16 * t2a) = pack(a0);
+    *reinterpret_cast<uint2*>(oh + 16 * (t2a + 1)) = pack(a1);
+    if (lse != nullptr && quarter == 0 && wave == 0 && g == 0) {
+        const float Ls = s_L[m];
+        lse[row * Hq + h] = Ls > 0.0f ? s_M[m] * 0.69314718055994531f + logf(Ls) : -INFINITY;
+    }
 }
 
 // Split plan: enough (row, split) blocks to occupy the chip, each split a
@@ -331,8 +418,28 @@ size_t mla_workspace_bytes(int rows, int Hq, int K) {
     int ns, sps;
     mla_plan(rows, K, &ns, &sps);
     if (ns == 1) return 0;
+    const size_t nwg = static_cast<size_t>((Hq + 15) / 16);
+    const size_t blocks = static_cast<size_t>(rows) * ns * nwg;
     const size_t slots = static_cast<size_t>(rows) * ns * Hq;
-    return slots * kDl * sizeof(float) + slots * 4 * sizeof(float) + 256;
+    return blocks * kT2 * 64 * 4 * sizeof(float) + slots * 4 * sizeof(float) + 256;
+}
+
+template <bool PIPE>
+static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq, int Lmax,
+                                    int K, int sps, int ns, int nitems, int hgroups,
+                                    const uint16_t* q, const uint16_t* latent, int64_t lat_rs,
+                                    int64_t lat_bs, const uint16_t* rope, int64_t rope_rs,
+                                    int64_t rope_bs, const int32_t* idx, float scale_log2,
+                                    uint16_t* out, float* lse, float* ws_o, float* ws_ml) {
+    // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(sparse_mla_kernel<PIPE>, grid, dim3(kMlaThreads), kMlaLdsBytes, stream, S,
+                       Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
+                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml);
+    return hipGetLastError();
 }
 
 hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
@@ -345,27 +452,29 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     mla_plan(rows, K, &ns, &sps);
     float* ws_o = nullptr;
     float* ws_ml = nullptr;
+    const int nwg = (Hq + 15) / 16;
     if (ns > 1) {
         ws_o = static_cast<float*>(workspace);
-        ws_ml = ws_o + static_cast<size_t>(rows) * ns * Hq * kDl;
+        ws_ml = ws_o + static_cast<size_t>(rows) * ns * nwg * kT2 * 64 * 4;
     }
-    // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_mla_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
-    if (attr != hipSuccess) return attr;
     const float scale_log2 = scale * 1.4426950408889634f;
     const int nitems = rows * ns;
     const int hgroups = (Hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const int nblocks = ((nitems + 7) / 8) * 8 * hgroups;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(nblocks), dim3(kMlaThreads), kMlaLdsBytes, stream,
-                       S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
-                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml);
-    hipError_t e = hipGetLastError();
+    // at most one block per CU: the pipelined one-block-per-CU build
+    const bool pipe = nblocks <= 256;
+    hipError_t e = pipe ? launch_mla_kernel<true>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
+                                                  nitems, hgroups, q, latent, lat_rs, lat_bs,
+                                                  rope, rope_rs, rope_bs, idx, scale_log2, out,
+                                                  lse, ws_o, ws_ml)
+                        : launch_mla_kernel<false>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
+                                                   nitems, hgroups, q, latent, lat_rs, lat_bs,
+                                                   rope, rope_rs, rope_bs, idx, scale_log2, out,
+                                                   lse, ws_o, ws_ml);
     if (e != hipSuccess) return e;
     if (ns > 1) {
-        hipLaunchKernelGGL(combine_kernel, dim3(rows * Hq), dim3(128), 0, stream, Hq, ns, ws_o,
-                           ws_ml, out, lse);
+        hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
+                           stream, Hq, ns, ws_o, ws_ml, out, lse);
         e = hipGetLastError();
     }
     return e;
