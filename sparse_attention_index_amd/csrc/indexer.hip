@@ -11,14 +11,13 @@
 //   prepare_rows_kernel  one wave per 128-feature row: RoPE, cast, amax,
 //                        scale, E4M3 encode; q rows go to q_fp8/q_scale,
 //                        k rows are appended to k_cache/k_scale at pos.
-//   score_kernel         one block per (query row, key block): the q codes of
-//                        the row live in registers as bf16 MFMA operands, the
-//                        FP8 key cache streams through in 16-key subtiles.
-//                        Codes are converted exactly to bf16 and multiplied on
-//                        the bf16 MFMA (products of E4M3 values are exact in
-//                        float32); the epilogue applies ReLU, the per-head
-//                        weight w*q_scale, the head sum across lanes and the
-//                        key's scale.
+//   score_tile_kernel    many query rows: 64 queries x 128 keys per block,
+//                        per-head GEMM tiles on the bf16 MFMA with the key
+//                        codes held in registers across all heads.
+//   decode_score_kernel  one query row per batch row, fused with prepare.
+// Codes are converted exactly to bf16 and multiplied on the bf16 MFMA
+// (products of E4M3 values are exact in float32); the epilogue applies ReLU,
+// the per-head weight w*q_scale, the head sum and the key's scale.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -105,96 +104,167 @@ hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_p
 }
 
 // ---------------------------------------------------------------------------
-// score: block = 4 waves, covers 64*U consecutive keys of one query row.
-// MFMA 16x16x32 bf16, M = 16 heads, N = 16 keys, K = 32 features; four
-// K-steps cover the 128 features and four head groups cover 64 heads.
-// Operand lane layout: lane (m = l%16, g = l/16) supplies row m, feature
-// chunk g; both operands use feature 32g + 8kk + j for MFMA kk, element j.
-// Result lane layout: lane (n = l%16, g) holds heads 4g..4g+3 of key n.
+// score (many query rows): block = 4 waves, a tile of 64 queries (of one
+// batch row) x 128 keys; wave w covers queries 32 (w & 1) .. +31 and keys
+// 64 (w >> 1) .. +63. Per head h the block's 64 query rows of codes are
+// converted to bf16 into LDS (double-buffered: head h+1 is staged while h is
+// multiplied) and each wave runs
+//   S_h = Q_h K^T    bf16 MFMA 32x32x16, M = 32 queries, N = 32 keys (two
+//                    key tiles), K = 16 features, eight K-steps;
+// the wave's key codes stay in registers as bf16 B operands for all heads.
+// Epilogue per head: I += (w q_scale)[t,h] * ReLU(S_h[t,s]); after the last
+// head I is scaled by the key's scale and stored for s < n_valid(t).
+// Lane layouts of the 32x32x16 MFMA: A/B lane l supplies row/column l%32,
+// features 8 (l/32) + j; result element i of lane l is row
+// 8 (i/4) + 4 (l/32) + i%4, column l%32.
+// Launch order: block L runs on XCD L % 8 and every XCD works through whole
+// query tiles (all their key tiles back to back), so a tile's query codes
+// are reused from that XCD's L2.
 // ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(256) void score_kernel(
-    int S, int H, int Lmax, int P, const uint8_t* __restrict__ q8,
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kQT = 64, kKT = 128;          // queries, keys per block tile
+constexpr int kQsStride = 128 + 8;          // bf16 per staged query row (bank stagger)
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 2) void score_tile_kernel(
+    int B, int S, int H, int Lmax, int P, int nqt, int nkt, const uint8_t* __restrict__ q8,
     const float* __restrict__ qscale, const float* __restrict__ w,
     const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
     const float* __restrict__ kscale, float* __restrict__ scores, int64_t ld) {
-    const int row = blockIdx.y;
-    const int p = pos[row];
-    if (p < 0 || p >= Lmax || p >= P) return;
-    const int n_valid = p + 1;
-    const int kblock0 = blockIdx.x * (64 * U);
-    if (kblock0 >= n_valid) return;
+    __shared__ __align__(16) uint16_t Qs[2][kQT][kQsStride];
+    __shared__ __align__(16) float wqs[64][kQT];       // [head][query] w * q_scale
+    __shared__ int nv[kQT];                            // n_valid per query of the tile
+    __shared__ int s_maxnv;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int64_t b = row / S;
+    const int L = blockIdx.x;
+    const int jx = L / 8;
+    const int qtile = (jx / nkt) * 8 + (L & 7);
+    const int kt = jx % nkt;
+    if (qtile >= B * nqt) return;
+    const int b = qtile / nqt;
+    const int t0 = (qtile - b * nqt) * kQT;
+    const int k0 = kt * kKT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t row0 = static_cast<int64_t>(b) * S + t0;
 
-    bf16x8 qa[4][4];
-    float wq[4][4];
+    if (tid == 0) s_maxnv = 0;
+    __syncthreads();
+    if (tid < kQT) {
+        int n = 0;
+        if (t0 + tid < S) {
+            const int p = pos[row0 + tid];
+            n = (p >= 0 && p < Lmax && p < P) ? p + 1 : 0;
+        }
+        nv[tid] = n;
+        atomicMax(&s_maxnv, n);
+    }
+    __syncthreads();
+    if (k0 >= s_maxnv) return;                         // tile wholly past every causal end
+
+    // per-head query weights
+    for (int i = tid; i < 64 * kQT; i += 256) {
+        const int h = i / kQT, qi = i - h * kQT;
+        float v = 0.0f;
+        if (h < H && t0 + qi < S) {
+            const int64_t r = row0 + qi;
+            v = w[r * H + h] * qscale[r * H + h];
+        }
+        wqs[h][qi] = v;
+    }
+
+    // the wave's key codes as bf16 B operands (two key tiles x eight K-steps)
+    const int wq_i = wave & 1, wk = wave >> 1;
+    const int hi32 = lane >> 5, l32 = lane & 31;
+    bf16x8 kb[2][8];
+    float ksc[2];
+    const uint8_t* kbase = kcache + static_cast<int64_t>(b) * Lmax * 128;
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-        const int h = hg * 16 + m;
-        if (h < H) {
-            const uint4* src = reinterpret_cast<const uint4*>(
-                q8 + (static_cast<int64_t>(row) * H + h) * 128 + g * 32);
-            const uint4 lo = src[0], hi = src[1];
-            qa[hg][0] = e4m3x8_to_bf16x8(lo.x, lo.y);
-            qa[hg][1] = e4m3x8_to_bf16x8(lo.z, lo.w);
-            qa[hg][2] = e4m3x8_to_bf16x8(hi.x, hi.y);
-            qa[hg][3] = e4m3x8_to_bf16x8(hi.z, hi.w);
-        } else {
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+        int key = k0 + wk * 64 + kt2 * 32 + l32;
+        key = key < Lmax ? key : Lmax - 1;
+        const uint8_t* kr = kbase + static_cast<int64_t>(key) * 128 + 8 * hi32;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint2 c = *reinterpret_cast<const uint2*>(kr + 16 * ks);
+            kb[kt2][ks] = e4m3x8_to_bf16x8(c.x, c.y);
+        }
+        ksc[kt2] = kscale[static_cast<int64_t>(b) * Lmax + key];
+    }
+
+    // staging: thread -> query tid/4, 32 features (tid%4)
+    const int sq = tid >> 2, sc = tid & 3;
+    const bool sq_ok = t0 + sq < S;
+    const uint8_t* qsrc = q8 + (row0 + sq) * H * 128 + 32 * sc;
+    uint4 raw0 = make_uint4(0u, 0u, 0u, 0u), raw1 = raw0;
+    auto fetch_q = [&](int h) {
+        if (sq_ok) {
+            const uint4* src = reinterpret_cast<const uint4*>(qsrc + static_cast<int64_t>(h) * 128);
+            raw0 = src[0];
+            raw1 = src[1];
+        }
+    };
+    auto stage_q = [&](int buf) {
+        uint16_t* dst = &Qs[buf][sq][32 * sc];
+        *reinterpret_cast<bf16x8*>(dst + 0) = e4m3x8_to_bf16x8(raw0.x, raw0.y);
+        *reinterpret_cast<bf16x8*>(dst + 8) = e4m3x8_to_bf16x8(raw0.z, raw0.w);
+        *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16x8(raw1.x, raw1.y);
+        *reinterpret_cast<bf16x8*>(dst + 24) = e4m3x8_to_bf16x8(raw1.z, raw1.w);
+    };
+
+    v16f I0, I1;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qa[hg][kk][e] = static_cast<__bf16>(0.0f);
+    for (int i = 0; i < 16; ++i) {
+        I0[i] = 0.0f;
+        I1[i] = 0.0f;
+    }
+    const uint16_t* arow = &Qs[0][wq_i * 32 + l32][8 * hi32];
+    constexpr int kBufStride = kQT * kQsStride;
+    fetch_q(0);
+    for (int h = 0; h < H; ++h) {
+        const int buf = h & 1;
+        stage_q(buf);
+        if (h + 1 < H) fetch_q(h + 1);
+        __syncthreads();
+        v16f s0, s1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = 0.0f;
+            s1[i] = 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = hg * 16 + 4 * g + i;
-            wq[hg][i] = hh < H ? w[static_cast<int64_t>(row) * H + hh] *
-                                     qscale[static_cast<int64_t>(row) * H + hh]
-                               : 0.0f;
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + buf * kBufStride + 16 * ks);
+            s0 = mfma_bf16_32x32x16(a, kb[0][ks], s0);
+            s1 = mfma_bf16_32x32x16(a, kb[1][ks], s1);
+        }
+        // result rows of lane: 8 r + 4 hi32 + c (r, c < 4); their weights
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 wv = *reinterpret_cast<const float4*>(&wqs[h][wq_i * 32 + 8 * r + 4 * hi32]);
+            const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                I0[4 * r + c] += wr[c] * fmaxf(s0[4 * r + c], 0.0f);
+                I1[4 * r + c] += wr[c] * fmaxf(s1[4 * r + c], 0.0f);
+            }
         }
     }
 
-    const uint8_t* kb = kcache + b * Lmax * 128;
-    const float* ksb = kscale + b * Lmax;
-    float* out = scores + static_cast<int64_t>(row) * ld;
-    const int wkey0 = kblock0 + wave * 16 * U;
-
-    uint4 kraw[U][2];
-    float ks[U];
+    // store the valid prefix of every query row
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        int key = wkey0 + u * 16 + m;
-        key = key < n_valid ? key : n_valid - 1;
-        const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * 128 + g * 32);
-        kraw[u][0] = src[0];
-        kraw[u][1] = src[1];
-        ks[u] = ksb[key];
-    }
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+        const int key = k0 + wk * 64 + kt2 * 32 + l32;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int key0 = wkey0 + u * 16;
-        if (key0 >= n_valid) break;
-        bf16x8 kbf[4];
-        kbf[0] = e4m3x8_to_bf16x8(kraw[u][0].x, kraw[u][0].y);
-        kbf[1] = e4m3x8_to_bf16x8(kraw[u][0].z, kraw[u][0].w);
-        kbf[2] = e4m3x8_to_bf16x8(kraw[u][1].x, kraw[u][1].y);
-        kbf[3] = e4m3x8_to_bf16x8(kraw[u][1].z, kraw[u][1].w);
-        float part = 0.0f;
-#pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part += wq[hg][i] * fmaxf(acc[i], 0.0f);
+        for (int i = 0; i < 16; ++i) {
+            const int qi = wq_i * 32 + 8 * (i >> 2) + 4 * hi32 + (i & 3);
+            if (key < nv[qi]) {
+                const float v = (kt2 == 0 ? I0[i] : I1[i]) * ksc[kt2];
+                scores[(row0 + qi) * ld + key] = v;
+            }
         }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        const int key = key0 + m;
-        if (g == 0 && key < n_valid) out[key] = part * ks[u];
     }
 }
 
@@ -423,24 +493,17 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
     return hipGetLastError();
 }
 
-// Keys per block: 64*U. Pick the largest U that still gives enough blocks to
-// fill the chip (blocks past a row's causal end exit at once).
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
                         hipStream_t stream) {
-    const int64_t rows = static_cast<int64_t>(B) * S;
-    int U = 4;
-    while (U > 1 && rows * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
-    const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)),
-                    static_cast<unsigned>(rows));
-#define DSA_SCORE(UU)                                                                          \
-    hipLaunchKernelGGL((score_kernel<UU>), grid, dim3(256), 0, stream, S, H, Lmax, P, q8, qscale, \
-                       w, pos, kcache, kscale, scores, ld)
-    if (U == 4) DSA_SCORE(4);
-    else if (U == 2) DSA_SCORE(2);
-    else DSA_SCORE(1);
-#undef DSA_SCORE
+    const int nqt = (S + kQT - 1) / kQT;
+    const int nkt = (Lmax + kKT - 1) / kKT;
+    const int64_t qtiles = static_cast<int64_t>(B) * nqt;
+    const int64_t nblocks = ((qtiles + 7) / 8) * 8 * nkt;
+    hipLaunchKernelGGL(score_tile_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0,
+                       stream, B, S, H, Lmax, P, nqt, nkt, q8, qscale, w, pos, kcache, kscale,
+                       scores, ld);
     return hipGetLastError();
 }
 
