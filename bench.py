@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated cache replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill leg (T = 4096 causal queries, per-call TFLOP/s)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -243,6 +245,93 @@ def capture(fn):
     return g
 
 
+# ---------------------------------------------------------- prefill leg --
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+
+
+def prefill_leg(reps=20):
+    """Prefill of T = 4096 causal queries at positions 0..4095 (B = 1, L = 4096,
+    H_I = 64, top-2048, 128 heads): each call timed on its own over graph
+    replays. Inputs: seeded N(0,1) draws made on the GPU (torch generator,
+    seed 3), bf16 activations, w scaled by 64^-0.5 128^-0.5."""
+    import torch
+
+    import sparse_attention_index_amd as dsa
+
+    T, H, Hq, K = 4096, 64, 128, 2048
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev)
+
+    q_raw = randn(1, T, H, 128).to(torch.bfloat16)
+    k_raw = randn(1, T, 128).to(torch.bfloat16)
+    w = randn(1, T, H) * (64 ** -0.5) * (128 ** -0.5)
+    q_mla = randn(1, T, Hq, 576).to(torch.bfloat16)
+    latent = randn(1, T, 512).to(torch.bfloat16)
+    kpe = randn(1, T, 64).to(torch.bfloat16)
+    pos = torch.arange(T, dtype=torch.int32, device=dev)[None].contiguous()
+    cos, sin = dsa.rope_table(T)
+    kc = torch.zeros((1, T, 128), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((1, T), dtype=torch.float32, device=dev)
+    scores = torch.empty((1, T, T), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((1, T, Hq, 512), dtype=torch.bfloat16, device=dev)
+    scale = 192 ** -0.5
+    iargs = dsa.indexer_args(q_raw, w, pos, cos, sin, kc, ks, scores, k_raw=k_raw)
+    iws = torch.empty(max(1, dsa.indexer_workspace_bytes(iargs)), dtype=torch.uint8, device=dev)
+    mws = torch.empty(max(1, dsa.sparse_mla_workspace_bytes(
+        dsa.mla_args(q_mla, latent, kpe, idx, scale, out))), dtype=torch.uint8, device=dev)
+    tws = dsa.topk_workspace(scores, pos, K)
+
+    calls = {
+        "indexer": lambda: dsa.indexer(q_raw, w, pos, cos, sin, kc, ks, scores, k_raw=k_raw,
+                                       workspace=iws),
+        "topk": lambda: dsa.topk(scores, pos, K, idx=idx, workspace=tws),
+        "sparse_mla": lambda: dsa.sparse_mla(q_mla, latent, kpe, idx, scale, out=out,
+                                             workspace=mws),
+    }
+    for c in ("indexer", "topk", "sparse_mla"):
+        calls[c]()
+    torch.cuda.synchronize()
+    us = {}
+    for c, fn in calls.items():
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us[c] = a.elapsed_time(b) * 1000.0 / reps
+    pairs = T * (T + 1) // 2
+    sel = sum(min(K, t + 1) for t in range(T))
+    idx_tflop = 2.0 * H * 128 * pairs / 1e12
+    mla_tflop = 2.0 * Hq * (576 + 512) * sel / 1e12
+    topk_bytes = 4 * pairs + 4 * sel
+    idx_tfs = idx_tflop / (us["indexer"] * 1e-6)
+    mla_tfs = mla_tflop / (us["sparse_mla"] * 1e-6)
+    return {
+        "workload": "prefill T=4096 (B=1, L=4096, H_I=64, top-2048, 128 heads)",
+        "call_us": {k: round(v, 1) for k, v in us.items()},
+        "indexer": {"tflops": round(idx_tfs, 1), "flop": round(idx_tflop * 1e12),
+                    "frac_bf16_mfma": round(idx_tfs / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "frac_fp8_mfma": round(idx_tfs / FP8_MFMA_PEAK_TFLOPS, 4),
+                    "note": "FP8 codes multiplied exactly on the bf16 MFMA; the call includes "
+                            "the key append and query quantisation"},
+        "sparse_mla": {"tflops": round(mla_tfs, 1), "flop": round(mla_tflop * 1e12),
+                       "frac_bf16_mfma": round(mla_tfs / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "topk": {"GBps": round(topk_bytes / (us["topk"] * 1e-6) / 1e9, 1), "bytes": topk_bytes,
+                 "frac_hbm": round(topk_bytes / (us["topk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 # ----------------------------------------------------------- cpu oracle --
 
 def cpu_baseline(wl, x, seconds):
@@ -349,6 +438,7 @@ def main():
         torch.cuda.synchronize()
         avg_us[c] = a.elapsed_time(b) * 1000.0 / (reps_call * R)
 
+    x_host = st["x"]
     n_valid = [int(p) + 1 for p in st["x"]["pos"].reshape(-1)]
     keff = [min(wl.K, n) for n in n_valid]
     ab = algorithmic_bytes(wl, n_valid, keff)
@@ -385,8 +475,12 @@ def main():
                      "avg_launch_us": round(avg_us[dom], 3)},
         "source_hash": srch,
     }
+    if not args.no_prefill:
+        del st, calls, step_graphs, call_graphs
+        torch.cuda.empty_cache()
+        rec["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, st["x"], args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, x_host, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -25,8 +25,13 @@ namespace dsa {
 // ---------------------------------------------------------------------------
 // prepare: RoPE (non-interleaved, first 64 features) + cast + block FP8.
 // Lane l holds features l and l+64 of its row; the rotation pairs feature j
-// (lane j) with j+32 (lane j+32), exchanged with one cross-lane swap.
+// (lane j) with j+32 (lane j+32), exchanged with one cross-lane swap. Each
+// wave handles kPrepRows consecutive rows and issues all their loads (pos,
+// then table entries and inputs) together, so the dependent global round
+// trips are paid once per kPrepRows rows.
 // ---------------------------------------------------------------------------
+constexpr int kPrepRows = 8;
+
 template <bool BF16_IN, bool TO_CACHE>
 __global__ __launch_bounds__(256) void prepare_rows_kernel(
     int64_t nrows, int rows_per_pos, int S, int Lmax, int P, const void* __restrict__ x,
@@ -34,63 +39,80 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
     const float* __restrict__ sin_t, uint8_t* __restrict__ codes_out,
     float* __restrict__ scales_out) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= nrows) return;
-    const int64_t r = row / rows_per_pos;          // query-row index b*S + s
-    const int p = pos[r];
-    if (p < 0 || p >= Lmax || p >= P) return;
-
-    float x0, x1;
-    if (BF16_IN) {
-        const uint16_t* xr = static_cast<const uint16_t*>(x) + row * 128;
-        x0 = bf16_bits_to_float(xr[lane]);
-        x1 = bf16_bits_to_float(xr[lane + 64]);
-    } else {
-        const float* xr = static_cast<const float*>(x) + row * 128;
-        x0 = xr[lane];
-        x1 = xr[lane + 64];
-    }
-    const float other = __shfl_xor(x0, 32);
+    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRows;
+    if (row0 >= nrows) return;
     const int j = lane & 31;
-    const float c = cos_t[static_cast<int64_t>(p) * 32 + j];
-    const float s = sin_t[static_cast<int64_t>(p) * 32 + j];
-    float y0;
-    {
-#pragma clang fp contract(off)
-        // pair (a, b) = (x[j], x[j+32]):  a' = a c - b s,  b' = a s + b c
-        if (lane < 32) {
-            const float ac = x0 * c, bs = other * s;
-            y0 = ac - bs;
+
+    int p[kPrepRows];
+    float x0[kPrepRows], x1[kPrepRows];
+#pragma unroll
+    for (int k = 0; k < kPrepRows; ++k) {
+        const int64_t row = row0 + k;
+        const bool ok = row < nrows;
+        p[k] = ok ? pos[row / rows_per_pos] : -1;
+        if (BF16_IN) {
+            const uint16_t* xr = static_cast<const uint16_t*>(x) + (ok ? row : 0) * 128;
+            x0[k] = bf16_bits_to_float(xr[lane]);
+            x1[k] = bf16_bits_to_float(xr[lane + 64]);
         } else {
-            const float as = other * s, bc = x0 * c;
-            y0 = as + bc;
+            const float* xr = static_cast<const float*>(x) + (ok ? row : 0) * 128;
+            x0[k] = xr[lane];
+            x1[k] = xr[lane + 64];
         }
     }
-    if (BF16_IN) y0 = bf16_bits_to_float(float_to_bf16_bits(y0));   // cast back to bf16
-
-    const float amax = wave_max(fmaxf(fabsf(y0), fabsf(x1)));
-    float scale = amax / 448.0f;
-    if (!(scale > 0.0f)) scale = 1.0f;
-    const uint8_t c0 = e4m3_encode(y0 / scale);
-    const uint8_t c1 = e4m3_encode(x1 / scale);
-
-    int64_t dst;
-    if (TO_CACHE) {
-        const int64_t b = r / S;
-        dst = b * Lmax + p;
-    } else {
-        dst = row;
+    float cs[kPrepRows], sn[kPrepRows];
+#pragma unroll
+    for (int k = 0; k < kPrepRows; ++k) {
+        const bool ok = p[k] >= 0 && p[k] < Lmax && p[k] < P;
+        const int64_t pe = ok ? p[k] : 0;
+        cs[k] = cos_t[pe * 32 + j];
+        sn[k] = sin_t[pe * 32 + j];
     }
-    codes_out[dst * 128 + lane] = c0;
-    codes_out[dst * 128 + lane + 64] = c1;
-    if (lane == 0) scales_out[dst] = scale;
+#pragma unroll
+    for (int k = 0; k < kPrepRows; ++k) {
+        const int64_t row = row0 + k;
+        if (row >= nrows) break;                   // wave-uniform
+        if (!(p[k] >= 0 && p[k] < Lmax && p[k] < P)) continue;
+        const float other = __shfl_xor(x0[k], 32);
+        float y0;
+        {
+#pragma clang fp contract(off)
+            // pair (a, b) = (x[j], x[j+32]):  a' = a c - b s,  b' = a s + b c
+            if (lane < 32) {
+                const float ac = x0[k] * cs[k], bs = other * sn[k];
+                y0 = ac - bs;
+            } else {
+                const float as = other * sn[k], bc = x0[k] * cs[k];
+                y0 = as + bc;
+            }
+        }
+        if (BF16_IN) y0 = bf16_bits_to_float(float_to_bf16_bits(y0));   // cast back to bf16
+
+        const float amax = wave_max_dpp(fmaxf(fabsf(y0), fabsf(x1[k])));
+        float scale = amax / 448.0f;
+        if (!(scale > 0.0f)) scale = 1.0f;
+        const uint8_t c0 = e4m3_encode(y0 / scale);
+        const uint8_t c1 = e4m3_encode(x1[k] / scale);
+
+        int64_t dst;
+        if (TO_CACHE) {
+            const int64_t b = (row / rows_per_pos) / S;
+            dst = b * Lmax + p[k];
+        } else {
+            dst = row;
+        }
+        codes_out[dst * 128 + lane] = c0;
+        codes_out[dst * 128 + lane + 64] = c1;
+        if (lane == 0) scales_out[dst] = scale;
+    }
 }
 
 hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
                           int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
                           const float* sin_t, uint8_t* codes, float* scales, hipStream_t stream) {
     if (nrows <= 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((nrows + 3) / 4)), block(256);
+    const dim3 grid(static_cast<unsigned>((nrows + 4 * kPrepRows - 1) / (4 * kPrepRows))),
+        block(256);
 #define DSA_PREP(B, C)                                                                         \
     hipLaunchKernelGGL((prepare_rows_kernel<B, C>), grid, block, 0, stream, nrows, rows_per_pos, \
                        S, Lmax, P, x, pos, cos_t, sin_t, codes, scales)
