@@ -127,8 +127,8 @@ hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_p
 
 // ---------------------------------------------------------------------------
 // score (many query rows): block = 4 waves, a tile of 64 queries (of one
-// batch row) x 128 keys; wave w covers queries 32 (w & 1) .. +31 and keys
-// 64 (w >> 1) .. +63. Per head h the block's 64 query rows of codes are
+// batch row) x 64 kKW keys; wave w covers queries 32 (w & 1) .. +31 and
+// keys 32 kKW (w >> 1) .. +32 kKW - 1. Per head h the block's 64 query rows of codes are
 // converted to bf16 into LDS (double-buffered: head h+1 is staged while h is
 // multiplied) and each wave runs
 //   S_h = Q_h K^T    bf16 MFMA 32x32x16, M = 32 queries, N = 32 keys (two
@@ -144,14 +144,21 @@ hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_p
 // are reused from that XCD's L2.
 // ---------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
-constexpr int kQT = 64, kKT = 128;          // queries, keys per block tile
+#ifndef DSA_TILE_KW
+#define DSA_TILE_KW 2
+#endif
+#ifndef DSA_TILE_OCC
+#define DSA_TILE_OCC 2
+#endif
+constexpr int kKW = DSA_TILE_KW;            // 32-key tiles per wave
+constexpr int kQT = 64, kKT = 64 * kKW;     // queries, keys per block tile
 constexpr int kQsStride = 128 + 8;          // bf16 per staged query row (bank stagger)
 
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 2) void score_tile_kernel(
+__global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
     int B, int S, int H, int Lmax, int P, int nqt, int nkt, const uint8_t* __restrict__ q8,
     const float* __restrict__ qscale, const float* __restrict__ w,
     const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
@@ -200,12 +207,12 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(
     // the wave's key codes as bf16 B operands (two key tiles x eight K-steps)
     const int wq_i = wave & 1, wk = wave >> 1;
     const int hi32 = lane >> 5, l32 = lane & 31;
-    bf16x8 kb[2][8];
-    float ksc[2];
+    bf16x8 kb[kKW][8];
+    float ksc[kKW];
     const uint8_t* kbase = kcache + static_cast<int64_t>(b) * Lmax * 128;
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-        int key = k0 + wk * 64 + kt2 * 32 + l32;
+    for (int kt2 = 0; kt2 < kKW; ++kt2) {
+        int key = k0 + wk * 32 * kKW + kt2 * 32 + l32;
         key = key < Lmax ? key : Lmax - 1;
         const uint8_t* kr = kbase + static_cast<int64_t>(key) * 128 + 8 * hi32;
 #pragma unroll
@@ -236,12 +243,11 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(
         *reinterpret_cast<bf16x8*>(dst + 24) = e4m3x8_to_bf16x8(raw1.z, raw1.w);
     };
 
-    v16f I0, I1;
+    v16f I[kKW];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        I0[i] = 0.0f;
-        I1[i] = 0.0f;
-    }
+    for (int kt2 = 0; kt2 < kKW; ++kt2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) I[kt2][i] = 0.0f;
     const uint16_t* arow = &Qs[0][wq_i * 32 + l32][8 * hi32];
     constexpr int kBufStride = kQT * kQsStride;
     fetch_q(0);
@@ -250,17 +256,17 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(
         stage_q(buf);
         if (h + 1 < H) fetch_q(h + 1);
         __syncthreads();
-        v16f s0, s1;
+        v16f sacc[kKW];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = 0.0f;
-            s1[i] = 0.0f;
-        }
+        for (int kt2 = 0; kt2 < kKW; ++kt2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kt2][i] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + buf * kBufStride + 16 * ks);
-            s0 = mfma_bf16_32x32x16(a, kb[0][ks], s0);
-            s1 = mfma_bf16_32x32x16(a, kb[1][ks], s1);
+#pragma unroll
+            for (int kt2 = 0; kt2 < kKW; ++kt2)
+                sacc[kt2] = mfma_bf16_32x32x16(a, kb[kt2][ks], sacc[kt2]);
         }
         // result rows of lane: 8 r + 4 hi32 + c (r, c < 4); their weights
 #pragma unroll
@@ -268,22 +274,22 @@ __global__ __launch_bounds__(256, 2) void score_tile_kernel(
             const float4 wv = *reinterpret_cast<const float4*>(&wqs[h][wq_i * 32 + 8 * r + 4 * hi32]);
             const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                I0[4 * r + c] += wr[c] * fmaxf(s0[4 * r + c], 0.0f);
-                I1[4 * r + c] += wr[c] * fmaxf(s1[4 * r + c], 0.0f);
-            }
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int kt2 = 0; kt2 < kKW; ++kt2)
+                    I[kt2][4 * r + c] += wr[c] * fmaxf(sacc[kt2][4 * r + c], 0.0f);
         }
     }
 
     // store the valid prefix of every query row
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-        const int key = k0 + wk * 64 + kt2 * 32 + l32;
+    for (int kt2 = 0; kt2 < kKW; ++kt2) {
+        const int key = k0 + wk * 32 * kKW + kt2 * 32 + l32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int qi = wq_i * 32 + 8 * (i >> 2) + 4 * hi32 + (i & 3);
             if (key < nv[qi]) {
-                const float v = (kt2 == 0 ? I0[i] : I1[i]) * ksc[kt2];
+                const float v = I[kt2][i] * ksc[kt2];
                 scores[(row0 + qi) * ld + key] = v;
             }
         }
