@@ -14,7 +14,8 @@
  *   dsa_topk        per-query causal top-k selection (up to 2048 positions)
  *   dsa_sparse_mla  sparse latent attention in absorbed (MQA) form
  *
- * plus dsa_rope_table, which builds the rotary table the indexer reads.
+ * plus dsa_rope_table, which builds the rotary tables, and dsa_mla_append,
+ * which writes new latent / rotary-key rows into the caches call 3 reads.
  *
  * Conventions shared by every call:
  *  - Every pointer in an args struct is a DEVICE pointer unless stated.
@@ -71,6 +72,8 @@ enum { DSA_DTYPE_F32 = 0, DSA_DTYPE_BF16 = 1 };
 
 /* dsa_indexer_args.flags */
 #define DSA_INDEXER_APPEND_ONLY 1u  /* run step 1 only: append keys, no scores */
+#define DSA_INDEXER_HADAMARD 2u     /* rotate q and k rows by H_128/sqrt(128) before quantising */
+#define DSA_INDEXER_POW2_SCALE 4u   /* round block scales up to a power of two */
 
 /* ------------------------------------------------------------------------
  * Rotary table. Page "RoPE coefficients" (precompute_freqs_cis excerpt):
@@ -103,8 +106,10 @@ dsa_status dsa_rope_table(const dsa_rope_table_args* args, hipStream_t stream);
  * (Indexer.forward: non-interleaved RoPE on the first 64 of 128 features in
  * float32, cast back to the input type, block-FP8 quantisation with one
  * float32 scale per 128-element block, keys written to the cache before
- * scoring). The Hadamard rotation the pages apply before quantisation is not
- * part of this call (it leaves exact scores unchanged).
+ * scoring). Optional per the flags: the Hadamard rotation the pages apply
+ * before quantisation ("Sparse latent attention": q and k times
+ * H_128/sqrt(128); "Rotate first features": rotate_activation), and
+ * power-of-two block scales (the act_quant scale_fmt option).
  *
  * Per query row r = (b, s) at position p = pos[b][s]:
  *  1. if k_raw != NULL: key row k_raw[b][s] is rotated with table row p,
@@ -120,6 +125,15 @@ dsa_status dsa_rope_table(const dsa_rope_table_args* args, hipStream_t stream);
  * call applies none.
  * Codes: OCP E4M3 (max 448), round to nearest even, saturating; scale =
  * amax/448 (float32 division), 1 for an all-zero row.
+ * DSA_INDEXER_HADAMARD: after the RoPE step every q and k row is replaced by
+ * H_128 x / sqrt(128) (fast Walsh-Hadamard transform in float32, butterfly
+ * strides 1, 2, ..., 64, then one multiplication by fl32(128^-0.5)) and
+ * rounded to the activation dtype. Exact scores are unchanged (H/sqrt(128)
+ * is orthonormal); the FP8 codes change.
+ * DSA_INDEXER_POW2_SCALE: scale = the smallest power of two >= amax/448.
+ * With either flag a single-row decode call runs as three launches
+ * (prepare k, prepare q, score) instead of the fused one, and needs the
+ * workspace dsa_indexer_workspace() reports when q_fp8 is not given.
  *
  * Layouts (row-major, contiguous):
  *   q_raw   [B][S][H][128]  act_dtype         k_raw  [B][S][128] act_dtype
@@ -243,6 +257,46 @@ typedef struct dsa_mla_args {
 
 dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* args, size_t* bytes);
 dsa_status dsa_sparse_mla(const dsa_mla_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MLA-side cache append (the step that fills the caches call 3 reads).
+ * Pages: "RoPE coefficients" (MLA prefill excerpt: new latent rows are
+ * written to the latent cache and the rotated rotary keys to the rope cache
+ * at their positions); the aipricedb digest's update note of 2025.11.17
+ * (MLA's rotary embedding pairs features 2j and 2j+1, interleaved, unlike
+ * the indexer's j / j+32).
+ * For query row r = (b, s) at position p = pos[b][s] (rows with p < 0,
+ * p >= Lmax or p >= P are skipped entirely):
+ *   latent[b][p][0:512] = latent_new[b][s][0:512]
+ *   rope[b][p][2j], rope[b][p][2j+1] = bf16(a*c - b*s), bf16(a*s + b*c)
+ *     for j < 32, (a, b) = kpe_new[b][s][2j], kpe_new[b][s][2j+1] and
+ *     (c, s) = (rope_cos[p][j], rope_sin[p][j]); float32 products, each sum
+ *     or difference rounded once (no fused multiply-add), then bf16 (RNE);
+ *   if q != NULL: q[b][s][h][512 + 2j], q[...][512 + 2j + 1] are rotated in
+ *     place the same way for every head h < Hq (q's latent part untouched).
+ * Layouts: latent_new [B][S][512] bf16, kpe_new [B][S][64] bf16, pos [B][S]
+ *   int32, rope_cos/sin [P][32] float32 (dsa_rope_table), the caches as in
+ *   dsa_mla_args (element strides), q [B][S][Hq][576] bf16.
+ * Limits: B, S, Lmax, P >= 1; 1 <= Hq <= 128 when q is given; every
+ * pointer 16-byte aligned, cache strides multiples of 8 elements.
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_mla_append_args {
+    int32_t B, S, Hq, Lmax, P;
+    const uint16_t* latent_new;
+    const uint16_t* kpe_new;
+    const int32_t* pos;
+    const float* rope_cos;
+    const float* rope_sin;
+    uint16_t* latent;            /* in/out */
+    int64_t latent_row_stride;
+    int64_t latent_batch_stride;
+    uint16_t* rope;              /* in/out */
+    int64_t rope_row_stride;
+    int64_t rope_batch_stride;
+    uint16_t* q;                 /* optional, rotated in place */
+} dsa_mla_append_args;
+
+dsa_status dsa_mla_append(const dsa_mla_append_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Helpers.

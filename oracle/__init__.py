@@ -45,6 +45,8 @@ def _load():
         "orc_rope_freqs": (None, [_i32, _f64, _i32, _i32, _f64, _f64, _f64, _ptr]),
         "orc_rope_rows": (None, [_i64, _i32, _i32, _i32, _ptr, _ptr, _ptr, _ptr, _i32, _ptr]),
         "orc_quantize_rows": (None, [_i64, _ptr, _ptr, _ptr]),
+        "orc_quantize_rows_pow2": (None, [_i64, _ptr, _ptr, _ptr]),
+        "orc_hadamard_rows": (None, [_i64, _ptr, _i32, _ptr]),
         "orc_dequantize_rows": (None, [_i64, _ptr, _ptr, _ptr]),
         "orc_indexer_scores": (None, [_i32, _i32, _i32, _i32, _i32, _ptr, _ptr, _ptr, _ptr, _ptr]),
         "orc_topk": (None, [_i64, _i64, _ptr, _ptr, _i32, _ptr]),
@@ -142,15 +144,26 @@ def rope(x, pos, cos, sin, rope_dim=64, interleaved=False, out_bf16=False) -> np
 
 # ------------------------------------------------------------ quantiser --
 
-def quantize(x):
-    """Block FP8: x float32 [..., 128] -> (codes uint8 [..., 128], scales float32 [...])."""
+def quantize(x, pow2=False):
+    """Block FP8: x float32 [..., 128] -> (codes uint8 [..., 128], scales float32 [...]).
+    pow2: scales rounded up to a power of two."""
     a = _c(x, np.float32)
     assert a.shape[-1] == 128
     nrows = a.size // 128
     codes = np.empty(a.shape, np.uint8)
     scales = np.empty(a.shape[:-1], np.float32)
-    _load().orc_quantize_rows(nrows, _p(a), _p(codes), _p(scales))
+    fn = _load().orc_quantize_rows_pow2 if pow2 else _load().orc_quantize_rows
+    fn(nrows, _p(a), _p(codes), _p(scales))
     return codes, scales
+
+
+def hadamard(x, out_bf16=False) -> np.ndarray:
+    """y = H_128 x / sqrt(128) per row of x float32 [..., 128] (float32 FWHT)."""
+    a = _c(x, np.float32)
+    assert a.shape[-1] == 128
+    out = np.empty_like(a)
+    _load().orc_hadamard_rows(a.size // 128, _p(a), int(bool(out_bf16)), _p(out))
+    return out
 
 
 def dequantize(codes, scales) -> np.ndarray:
@@ -162,15 +175,19 @@ def dequantize(codes, scales) -> np.ndarray:
     return out
 
 
-def indexer_prepare(x, pos, cos, sin, bf16_input: bool):
+def indexer_prepare(x, pos, cos, sin, bf16_input: bool, hadamard_rot=False, pow2=False):
     """Indexer q or k rows as the pages prepare them: non-interleaved RoPE on
-    features 0..63 in float32, cast back to the input dtype, block FP8.
+    features 0..63 in float32, cast back to the input dtype, optionally the
+    Hadamard rotation (also cast back), block FP8 (optionally with
+    power-of-two scales).
 
     x: float32 [..., 128] holding the input values (bf16 values when
     bf16_input); pos broadcastable to x.shape[:-1].
     Returns (codes, scales, rotated float32)."""
     rot = rope(x, pos, cos, sin, rope_dim=64, interleaved=False, out_bf16=bf16_input)
-    codes, scales = quantize(rot)
+    if hadamard_rot:
+        rot = hadamard(rot, out_bf16=bf16_input)
+    codes, scales = quantize(rot, pow2=pow2)
     return codes, scales, rot
 
 

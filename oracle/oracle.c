@@ -271,6 +271,80 @@ void orc_quantize_rows(int64_t nrows, const float* x, uint8_t* codes, float* sca
     }
 }
 
+/* ------------------------------------------------------------------------
+ * Power-of-two block scale (the `scale_fmt` variant of act_quant named on
+ * page "Rotate first features", Indexer.forward; the pages do not print its
+ * rule). Reading: the smallest power of two s with s >= fl32(amax / 448),
+ * so no element saturates; s = 1 when amax == 0.
+ * Pinned by: s is a power of two, fl32(amax/448) <= s < 2 fl32(amax/448),
+ * max |x| / s <= 448.
+ * ---------------------------------------------------------------------- */
+static float orc_pow2_ceil(float v) {
+    int e;
+    double m = frexp((double)v, &e);  /* v = m * 2^e, m in [0.5, 1) */
+    if (m == 0.5) return v;
+    return (float)ldexp(1.0, e);
+}
+
+void orc_quantize_rows_pow2(int64_t nrows, const float* x, uint8_t* codes, float* scales) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < nrows; ++r) {
+        const float* xr = x + r * 128;
+        float amax = 0.0f, scale;
+        int d;
+        for (d = 0; d < 128; ++d) {
+            float a = fabsf(xr[d]);
+            if (a > amax) amax = a;
+        }
+        scale = amax / 448.0f;
+        scale = (scale > 0.0f) ? orc_pow2_ceil(scale) : 1.0f;
+        for (d = 0; d < 128; ++d) codes[r * 128 + d] = orc_e4m3_encode(xr[d] / scale);
+        scales[r] = scale;
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * Hadamard rotation of 128-feature rows [page "Sparse latent attention":
+ * the indexer's rotated q and k are multiplied by H_128 / sqrt(128) before
+ * quantisation; page "Rotate first features": rotate_activation(q),
+ * rotate_activation(k) ahead of act_quant]. H_128 is the Sylvester Hadamard
+ * matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), symmetric, so
+ * y = H x / sqrt(128) row by row.
+ * Reading (the order of float32 operations is not on the pages): the fast
+ * Walsh-Hadamard transform in float32 with butterfly strides 1, 2, 4, ...,
+ * 64 (x[i], x[i+s]) -> (x[i] + x[i+s], x[i] - x[i+s]), then one float32
+ * multiplication by fl32(128^-0.5); with out_bf16 the row is rounded to
+ * bfloat16 afterwards, like every step of the indexer's preparation.
+ * Pinned by: a float64 matrix product with scipy's Hadamard matrix (within
+ * the float32 rounding bound of the transform), H e_0 = 128^-0.5 (all
+ * ones), orthonormality (norm preserved, H H x = x).
+ * ---------------------------------------------------------------------- */
+void orc_hadamard_rows(int64_t nrows, const float* x, int out_bf16, float* y) {
+    int64_t r;
+    const float inv = (float)(1.0 / sqrt(128.0));
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < nrows; ++r) {
+        float v[128];
+        int i, s;
+        for (i = 0; i < 128; ++i) v[i] = x[r * 128 + i];
+        for (s = 1; s < 128; s <<= 1) {
+            for (i = 0; i < 128; ++i) {
+                if (i & s) continue;
+                {
+                    float a = v[i], b = v[i + s];
+                    v[i] = a + b;
+                    v[i + s] = a - b;
+                }
+            }
+        }
+        for (i = 0; i < 128; ++i) {
+            float o = v[i] * inv;
+            y[r * 128 + i] = out_bf16 ? orc_round_bf16(o) : o;
+        }
+    }
+}
+
 void orc_dequantize_rows(int64_t nrows, const uint8_t* codes, const float* scales,
                          double* out) {
     int64_t r;

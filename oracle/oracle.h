@@ -59,6 +59,11 @@ void orc_rope_rows(int64_t nrows, int width, int rope_dim, int interleaved,
  * scale per row (scale = amax/448, or 1 when amax == 0) and E4M3 codes of
  * x/scale. */
 void orc_quantize_rows(int64_t nrows, const float* x, uint8_t* codes, float* scales);
+/* As orc_quantize_rows with the scale rounded up to a power of two. */
+void orc_quantize_rows_pow2(int64_t nrows, const float* x, uint8_t* codes, float* scales);
+/* y = H_128 x / sqrt(128) per 128-feature row (fast Walsh-Hadamard transform
+ * in float32, strides 1..64); out_bf16 rounds the result to bfloat16. */
+void orc_hadamard_rows(int64_t nrows, const float* x, int out_bf16, float* y);
 
 /* Dequantise: out[r][d] = decode(codes[r][d]) * scales[r] (double). */
 void orc_dequantize_rows(int64_t nrows, const uint8_t* codes, const float* scales,

@@ -30,6 +30,8 @@ LATENT_DIM = 512
 ROPE_DIM = 64
 MAX_TOPK = 2048
 APPEND_ONLY = 1
+HADAMARD = 2
+POW2_SCALE = 4
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -67,9 +69,17 @@ class MlaArgs(ctypes.Structure):
                 ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
 
 
+class MlaAppendArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("S", _i32), ("Hq", _i32), ("Lmax", _i32), ("P", _i32),
+                ("latent_new", _vp), ("kpe_new", _vp), ("pos", _vp), ("rope_cos", _vp),
+                ("rope_sin", _vp), ("latent", _vp), ("latent_row_stride", _i64),
+                ("latent_batch_stride", _i64), ("rope", _vp), ("rope_row_stride", _i64),
+                ("rope_batch_stride", _i64), ("q", _vp)]
+
+
 EXPORTS = ("dsa_rope_table", "dsa_indexer_workspace", "dsa_indexer", "dsa_topk_workspace",
-           "dsa_topk", "dsa_sparse_mla_workspace", "dsa_sparse_mla", "dsa_status_str",
-           "dsa_abi_version")
+           "dsa_topk", "dsa_sparse_mla_workspace", "dsa_sparse_mla", "dsa_mla_append",
+           "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -152,8 +162,12 @@ def rope_table(P: int, yarn: bool = False, theta: float = 10000.0, orig_len: int
     return cos, sin
 
 
+def _prep_flags(hadamard, pow2_scale):
+    return (HADAMARD if hadamard else 0) | (POW2_SCALE if pow2_scale else 0)
+
+
 def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, q_fp8=None,
-                 q_scale=None, workspace=None) -> IndexerArgs:
+                 q_scale=None, workspace=None, hadamard=False, pow2_scale=False) -> IndexerArgs:
     import torch
     B, S, H, D = q_raw.shape
     Lmax = k_cache.shape[1]
@@ -179,11 +193,12 @@ def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, 
         _need(q_scale, "q_scale", torch.float32, (B, S, H))
     return IndexerArgs(B, S, H, Lmax, cos.shape[0], dt, _ptr(q_raw), _ptr(k_raw), _ptr(pos),
                        _ptr(cos), _ptr(sin), _ptr(w), _ptr(k_cache), _ptr(k_scale),
-                       _ptr(q_fp8), _ptr(q_scale), _ptr(scores), scores.stride(1), 0,
-                       _ptr(workspace), 0 if workspace is None else workspace.numel())
+                       _ptr(q_fp8), _ptr(q_scale), _ptr(scores), scores.stride(1),
+                       _prep_flags(hadamard, pow2_scale), _ptr(workspace),
+                       0 if workspace is None else workspace.numel())
 
 
-def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale):
+def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale, hadamard=False, pow2_scale=False):
     """Call 1 with DSA_INDEXER_APPEND_ONLY: rotate, quantise and write the
     key rows k_raw [B, S, 128] into k_cache/k_scale at pos [B, S]."""
     import torch
@@ -200,7 +215,7 @@ def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale):
     _need(k_scale, "k_scale", torch.float32, (B, Lmax))
     a = IndexerArgs(B, S, 1, Lmax, cos.shape[0], dt, None, _ptr(k_raw), _ptr(pos), _ptr(cos),
                     _ptr(sin), None, _ptr(k_cache), _ptr(k_scale), None, None, None, Lmax,
-                    APPEND_ONLY, None, 0)
+                    APPEND_ONLY | _prep_flags(hadamard, pow2_scale), None, 0)
     _check(lib().dsa_indexer(ctypes.byref(a), _stream()))
 
 
@@ -216,7 +231,7 @@ def _workspace(nbytes, device):
 
 
 def indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, scores=None, k_raw=None, q_fp8=None,
-            q_scale=None, workspace=None):
+            q_scale=None, workspace=None, hadamard=False, pow2_scale=False):
     """Call 1: append k_raw rows (if given) and score every causal key.
     Returns scores [B, S, Lmax] float32 (entries past each row's position
     are left as they were)."""
@@ -225,7 +240,7 @@ def indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, scores=None, k_raw=None, 
     if scores is None:
         scores = torch.empty((B, S, k_cache.shape[1]), dtype=torch.float32, device=q_raw.device)
     a = indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw, q_fp8, q_scale,
-                     workspace)
+                     workspace, hadamard, pow2_scale)
     need = indexer_workspace_bytes(a)
     if need and (workspace is None or workspace.numel() < need):
         workspace = _workspace(need, q_raw.device)
@@ -325,6 +340,35 @@ def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(lib().dsa_sparse_mla(ctypes.byref(a), _stream()))
     return (out, lse) if return_lse else out
+
+
+def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None):
+    """Write latent_new [B, S, 512] and the interleaved-RoPE-rotated kpe_new
+    [B, S, 64] into the caches latent / rope ([B, Lmax, 512] / [B, Lmax, 64]
+    views with unit inner stride) at pos [B, S]; if q [B, S, Hq, 576] is
+    given, its rope part is rotated in place."""
+    import torch
+    B, S = pos.shape
+    _need(pos, "pos", torch.int32, (B, S))
+    _need(latent_new, "latent_new", torch.bfloat16, (B, S, LATENT_DIM))
+    _need(kpe_new, "kpe_new", torch.bfloat16, (B, S, ROPE_DIM))
+    _need(cos, "cos", torch.float32)
+    _need(sin, "sin", torch.float32, cos.shape)
+    for name, t, d in (("latent", latent, LATENT_DIM), ("rope", rope, ROPE_DIM)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != B \
+                or t.shape[2] != d or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor [B, Lmax, {d}] "
+                             "with unit inner stride")
+    if latent.shape[1] != rope.shape[1]:
+        raise ValueError("latent and rope must have the same Lmax")
+    Hq = 0
+    if q is not None:
+        Hq = q.shape[2]
+        _need(q, "q", torch.bfloat16, (B, S, Hq, LATENT_DIM + ROPE_DIM))
+    a = MlaAppendArgs(B, S, Hq, latent.shape[1], cos.shape[0], _ptr(latent_new), _ptr(kpe_new),
+                      _ptr(pos), _ptr(cos), _ptr(sin), _ptr(latent), latent.stride(1),
+                      latent.stride(0), _ptr(rope), rope.stride(1), rope.stride(0), _ptr(q))
+    _check(lib().dsa_mla_append(ctypes.byref(a), _stream()))
 
 
 def softmax_scale(qk_head_dim: int = 192, yarn: bool = False, rope_factor: float = 40.0,

@@ -13,7 +13,8 @@ hipError_t launch_rope_table(int P, int npairs, double base, int yarn, double lo
                              double factor, float* cos_out, float* sin_out, hipStream_t stream);
 hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
                           int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
-                          const float* sin_t, uint8_t* codes, float* scales, hipStream_t stream);
+                          const float* sin_t, uint8_t* codes, float* scales, bool hadamard,
+                          bool pow2, hipStream_t stream);
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
@@ -33,6 +34,11 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
                              const int32_t* idx, float scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream);
+hipError_t launch_mla_append(int B, int S, int Hq, int Lmax, int P, const uint16_t* latent_new,
+                             const uint16_t* kpe_new, const int32_t* pos, const float* cos_t,
+                             const float* sin_t, uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
+                             uint16_t* rope, int64_t rope_rs, int64_t rope_bs, uint16_t* q,
+                             hipStream_t stream);
 }  // namespace dsa
 
 namespace {
@@ -54,7 +60,8 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
     if (static_cast<int64_t>(a->B) * a->Lmax > (int64_t(1) << 40)) return DSA_ERR_SHAPE;
     if (a->ld_scores < a->Lmax) return DSA_ERR_SHAPE;
     if (a->act_dtype != DSA_DTYPE_F32 && a->act_dtype != DSA_DTYPE_BF16) return DSA_ERR_UNSUPPORTED;
-    if ((a->flags & ~DSA_INDEXER_APPEND_ONLY) != 0) return DSA_ERR_UNSUPPORTED;
+    if ((a->flags & ~(DSA_INDEXER_APPEND_ONLY | DSA_INDEXER_HADAMARD | DSA_INDEXER_POW2_SCALE)) != 0)
+        return DSA_ERR_UNSUPPORTED;
     const size_t esz = a->act_dtype == DSA_DTYPE_BF16 ? 2 : 4;
     const bool append_only = (a->flags & DSA_INDEXER_APPEND_ONLY) != 0;
     if (!a->pos || !a->rope_cos || !a->rope_sin || !a->k_cache || !a->k_scale) return DSA_ERR_NULL;
@@ -76,8 +83,14 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
     return DSA_OK;
 }
 
+// the fused single-row decode launch covers the plain preparation only
+bool fused_decode(const dsa_indexer_args* a) {
+    return a->S == 1 &&
+           !(a->flags & (DSA_INDEXER_APPEND_ONLY | DSA_INDEXER_HADAMARD | DSA_INDEXER_POW2_SCALE));
+}
+
 size_t indexer_ws(const dsa_indexer_args* a) {
-    if (a->q_fp8 != nullptr || (a->flags & DSA_INDEXER_APPEND_ONLY) || a->S == 1) return 0;
+    if (a->q_fp8 != nullptr || (a->flags & DSA_INDEXER_APPEND_ONLY) || fused_decode(a)) return 0;
     const size_t rows = static_cast<size_t>(a->B) * a->S * a->H;
     return round_up(rows * 128, 256) + round_up(rows * sizeof(float), 256);
 }
@@ -111,6 +124,27 @@ dsa_status check_mla(const dsa_mla_args* a) {
     if (!a->q || !a->latent || !a->rope || !a->idx || !a->out) return DSA_ERR_NULL;
     if (!aligned16(a->q) || !aligned16(a->latent) || !aligned16(a->rope) || !aligned16(a->out) ||
         !aligned4(a->idx) || (a->lse && !aligned4(a->lse)))
+        return DSA_ERR_ALIGN;
+    if ((a->latent_row_stride % 8) || (a->latent_batch_stride % 8) || (a->rope_row_stride % 8) ||
+        (a->rope_batch_stride % 8))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+dsa_status check_mla_append(const dsa_mla_append_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->S < 1 || a->Lmax < 1 || a->P < 1) return DSA_ERR_SHAPE;
+    if (a->q != nullptr && (a->Hq < 1 || a->Hq > DSA_MAX_ATTN_HEADS)) return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(a->B) * a->S > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
+    if (a->latent_row_stride < DSA_LATENT_DIM || a->rope_row_stride < DSA_ROPE_DIM ||
+        a->latent_batch_stride < 0 || a->rope_batch_stride < 0)
+        return DSA_ERR_SHAPE;
+    if (!a->latent_new || !a->kpe_new || !a->pos || !a->rope_cos || !a->rope_sin || !a->latent ||
+        !a->rope)
+        return DSA_ERR_NULL;
+    if (!aligned16(a->latent_new) || !aligned16(a->kpe_new) || !aligned16(a->latent) ||
+        !aligned16(a->rope) || (a->q && !aligned16(a->q)) || !aligned4(a->pos) ||
+        !aligned4(a->rope_cos) || !aligned4(a->rope_sin))
         return DSA_ERR_ALIGN;
     if ((a->latent_row_stride % 8) || (a->latent_batch_stride % 8) || (a->rope_row_stride % 8) ||
         (a->rope_batch_stride % 8))
@@ -193,7 +227,9 @@ dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
     const bool bf16 = a->act_dtype == DSA_DTYPE_BF16;
     const int64_t qrows = static_cast<int64_t>(a->B) * a->S * a->H;
     hipError_t e = hipSuccess;
-    if (a->S == 1 && !(a->flags & DSA_INDEXER_APPEND_ONLY)) {
+    const bool had = (a->flags & DSA_INDEXER_HADAMARD) != 0;
+    const bool pow2 = (a->flags & DSA_INDEXER_POW2_SCALE) != 0;
+    if (fused_decode(a)) {
         // decode: one fused launch (quantise q, append the new key, score)
         e = dsa::launch_decode_score(bf16, a->B, a->H, a->Lmax, a->P, a->q_raw, a->k_raw, a->pos,
                                      a->rope_cos, a->rope_sin, a->w, a->k_cache, a->k_scale,
@@ -203,12 +239,12 @@ dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
     if (a->k_raw != nullptr) {
         e = dsa::launch_prepare(bf16, true, static_cast<int64_t>(a->B) * a->S, 1, a->S, a->Lmax,
                                 a->P, a->k_raw, a->pos, a->rope_cos, a->rope_sin, a->k_cache,
-                                a->k_scale, stream);
+                                a->k_scale, had, pow2, stream);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     if (a->flags & DSA_INDEXER_APPEND_ONLY) return DSA_OK;
     e = dsa::launch_prepare(bf16, false, qrows, a->H, a->S, a->Lmax, a->P, a->q_raw, a->pos,
-                            a->rope_cos, a->rope_sin, q8, qs, stream);
+                            a->rope_cos, a->rope_sin, q8, qs, had, pow2, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
     e = dsa::launch_score(a->B, a->S, a->H, a->Lmax, a->P, q8, qs, a->w, a->pos, a->k_cache,
                           a->k_scale, a->scores, a->ld_scores, stream);
@@ -255,6 +291,15 @@ dsa_status dsa_sparse_mla(const dsa_mla_args* a, hipStream_t stream) {
         a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->latent, a->latent_row_stride,
         a->latent_batch_stride, a->rope, a->rope_row_stride, a->rope_batch_stride, a->idx,
         a->scale, a->out, a->lse, a->workspace, stream));
+}
+
+dsa_status dsa_mla_append(const dsa_mla_append_args* a, hipStream_t stream) {
+    const dsa_status st = check_mla_append(a);
+    if (st != DSA_OK) return st;
+    return hip_status(dsa::launch_mla_append(
+        a->B, a->S, a->q ? a->Hq : 0, a->Lmax, a->P, a->latent_new, a->kpe_new, a->pos,
+        a->rope_cos, a->rope_sin, a->latent, a->latent_row_stride, a->latent_batch_stride,
+        a->rope, a->rope_row_stride, a->rope_batch_stride, a->q, stream));
 }
 
 }  // extern "C"

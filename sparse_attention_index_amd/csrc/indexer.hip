@@ -29,15 +29,42 @@ namespace dsa {
 // wave handles kPrepRows consecutive rows and issues all their loads (pos,
 // then table entries and inputs) together, so the dependent global round
 // trips are paid once per kPrepRows rows.
+// Options: `had` replaces the rotated row by H_128 x / sqrt(128) (fast
+// Walsh-Hadamard transform in float32, butterfly strides 1..32 across lanes
+// and 64 inside the lane, then a multiplication by fl32(128^-0.5), rounded
+// to the activation dtype); `pow2` rounds the block scale up to a power of
+// two.
 // ---------------------------------------------------------------------------
 constexpr int kPrepRows = 8;
+constexpr float kInvSqrt128 = 0.088388347648318440550f;   // fl32(128^-0.5)
+
+// smallest power of two >= v (v > 0, finite)
+__device__ __forceinline__ float pow2_ceil(float v) {
+    uint32_t u = __float_as_uint(v);
+    const uint32_t e = u >> 23, m = u & 0x7FFFFFu;
+    if (e == 0u) {                                  // subnormal
+        if (m & (m - 1u)) u = 1u << (32 - __clz(static_cast<int>(m)));
+    } else if (m != 0u) {
+        u = (e + 1u) << 23;
+    }
+    return __uint_as_float(u);
+}
+
+// one stride of the Walsh-Hadamard butterfly on features lane (a) and
+// lane + 64 (c): (x[i], x[i+s]) -> (x[i] + x[i+s], x[i] - x[i+s])
+__device__ __forceinline__ void wht_step(float& a, float& c, int lane, int s) {
+    const float pa = __shfl_xor(a, s), pc = __shfl_xor(c, s);
+    const bool upper = (lane & s) != 0;
+    a = upper ? pa - a : a + pa;
+    c = upper ? pc - c : c + pc;
+}
 
 template <bool BF16_IN, bool TO_CACHE>
 __global__ __launch_bounds__(256) void prepare_rows_kernel(
     int64_t nrows, int rows_per_pos, int S, int Lmax, int P, const void* __restrict__ x,
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, uint8_t* __restrict__ codes_out,
-    float* __restrict__ scales_out) {
+    float* __restrict__ scales_out, int had, int pow2) {
     const int lane = threadIdx.x & 63;
     const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRows;
     if (row0 >= nrows) return;
@@ -87,12 +114,26 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
             }
         }
         if (BF16_IN) y0 = bf16_bits_to_float(float_to_bf16_bits(y0));   // cast back to bf16
+        float y1 = x1[k];
+        if (had) {
+#pragma unroll
+            for (int st = 1; st < 64; st <<= 1) wht_step(y0, y1, lane, st);
+            const float t = y0 + y1;
+            y1 = y0 - y1;
+            y0 = t * kInvSqrt128;
+            y1 = y1 * kInvSqrt128;
+            if (BF16_IN) {
+                y0 = bf16_bits_to_float(float_to_bf16_bits(y0));
+                y1 = bf16_bits_to_float(float_to_bf16_bits(y1));
+            }
+        }
 
-        const float amax = wave_max_dpp(fmaxf(fabsf(y0), fabsf(x1[k])));
+        const float amax = wave_max_dpp(fmaxf(fabsf(y0), fabsf(y1)));
         float scale = amax / 448.0f;
-        if (!(scale > 0.0f)) scale = 1.0f;
+        if (pow2) scale = scale > 0.0f ? pow2_ceil(scale) : 1.0f;
+        else if (!(scale > 0.0f)) scale = 1.0f;
         const uint8_t c0 = e4m3_encode(y0 / scale);
-        const uint8_t c1 = e4m3_encode(x1[k] / scale);
+        const uint8_t c1 = e4m3_encode(y1 / scale);
 
         int64_t dst;
         if (TO_CACHE) {
@@ -109,13 +150,15 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
 
 hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
                           int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
-                          const float* sin_t, uint8_t* codes, float* scales, hipStream_t stream) {
+                          const float* sin_t, uint8_t* codes, float* scales, bool hadamard,
+                          bool pow2, hipStream_t stream) {
     if (nrows <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((nrows + 4 * kPrepRows - 1) / (4 * kPrepRows))),
         block(256);
 #define DSA_PREP(B, C)                                                                         \
     hipLaunchKernelGGL((prepare_rows_kernel<B, C>), grid, block, 0, stream, nrows, rows_per_pos, \
-                       S, Lmax, P, x, pos, cos_t, sin_t, codes, scales)
+                       S, Lmax, P, x, pos, cos_t, sin_t, codes, scales, hadamard ? 1 : 0,       \
+                       pow2 ? 1 : 0)
     if (bf16_in) {
         if (to_cache) DSA_PREP(true, true); else DSA_PREP(true, false);
     } else {

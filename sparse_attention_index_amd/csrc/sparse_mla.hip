@@ -399,12 +399,13 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
 }
 
 // Split plan: enough (row, split) blocks to occupy the chip, each split a
-// whole number of 32-key tiles and at least four of them (so the gather of
-// the next tile has a tile of MFMA work to hide behind), at most kMaxSplits.
+// whole number of 32-key tiles and at least two of them (fewer, longer splits
+// cost more per block than the extra partials cost the merge; measured at
+// 16K and 128K context), at most kMaxSplits.
 void mla_plan(int rows, int K, int* nsplit, int* slots_per_split) {
     const int tiles = (K + kTile - 1) / kTile;
     int ns = (256 + rows - 1) / rows;
-    int cap = tiles / 4;
+    int cap = tiles / 2;
     if (cap > kMaxSplits) cap = kMaxSplits;
     if (ns > cap) ns = cap;
     if (ns < 1) ns = 1;

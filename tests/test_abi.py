@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -46,6 +46,7 @@ STRUCTS = {
     "dsa_indexer_args": dsa.IndexerArgs,
     "dsa_topk_args": dsa.TopkArgs,
     "dsa_mla_args": dsa.MlaArgs,
+    "dsa_mla_append_args": dsa.MlaAppendArgs,
 }
 
 
@@ -93,7 +94,7 @@ def test_indexer_validation():
     assert n.value == 0                         # q_fp8/q_scale given -> no workspace
     cases = [
         (dict(H=65), 2), (dict(H=0), 2), (dict(B=0), 2), (dict(Lmax=0), 2), (dict(P=0), 2),
-        (dict(ld_scores=100), 2), (dict(act_dtype=7), 3), (dict(flags=2), 3),
+        (dict(ld_scores=100), 2), (dict(act_dtype=7), 3), (dict(flags=8), 3),
         (dict(flags=1, k_raw=None), 1), (dict(flags=1, k_raw=FAKE + 1), 5),
         (dict(q_raw=None), 1), (dict(scores=None), 1), (dict(q_scale=None), 1),
         (dict(k_cache=FAKE + 8), 5), (dict(B=300, S=300), 2),
@@ -170,3 +171,25 @@ def test_rope_table_validation():
     assert call(L.dsa_rope_table, a) == 3
     a = dsa.RopeTableArgs(10, 0, 4096, 10000.0, 40.0, 32.0, 1.0, None, FAKE)
     assert call(L.dsa_rope_table, a) == 1
+
+
+def good_append(q=None):
+    return dsa.MlaAppendArgs(2, 3, 128, 1024, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 512,
+                             512 * 1024, FAKE, 64, 64 * 1024, q)
+
+
+def test_mla_append_validation():
+    L = dsa.lib()
+    for change, code in [(dict(B=0), 2), (dict(P=0), 2), (dict(latent_row_stride=500), 2),
+                         (dict(rope_batch_stride=-8), 2), (dict(latent_row_stride=520), 0),
+                         (dict(rope_row_stride=66), 5), (dict(latent_new=None), 1),
+                         (dict(rope=None), 1), (dict(kpe_new=FAKE + 4), 5),
+                         (dict(pos=FAKE + 2), 5), (dict(q=FAKE, Hq=0), 2),
+                         (dict(q=FAKE, Hq=129), 2), (dict(q=FAKE + 8), 5)]:
+        a = good_append()
+        for k, v in change.items():
+            setattr(a, k, v)
+        if code == 0:
+            continue                 # valid arguments would launch: GPU tests cover them
+        assert call(L.dsa_mla_append, a) == code, change
+    assert L.dsa_mla_append(None, None) == 1

@@ -30,7 +30,8 @@ def test_rope_table_matches_oracle(P, yarn):
         assert np.mean(~same) < 1e-4
 
 
-def run_indexer(B, S, H, Lmax, pos, act_bf16, seed, yarn=False, w_scale=None):
+def run_indexer(B, S, H, Lmax, pos, act_bf16, seed, yarn=False, w_scale=None, had=False,
+                pow2=False):
     """Fill the whole cache with the append-only call, then score with the
     call's own key rows appended again (identical values)."""
     import torch
@@ -48,24 +49,27 @@ def run_indexer(B, S, H, Lmax, pos, act_bf16, seed, yarn=False, w_scale=None):
     kc = torch.zeros((B, Lmax, 128), dtype=torch.uint8, device="cuda")
     ks = torch.zeros((B, Lmax), dtype=torch.float32, device="cuda")
     all_pos = np.broadcast_to(np.arange(Lmax, dtype=np.int32), (B, Lmax)).copy()
-    dsa.indexer_append(dev_act(k_all, act_bf16), dev(all_pos), dcos, dsin, kc, ks)
+    dsa.indexer_append(dev_act(k_all, act_bf16), dev(all_pos), dcos, dsin, kc, ks,
+                       hadamard=had, pow2_scale=pow2)
     k_call = np.stack([k_all[b, pos[b]] for b in range(B)])          # [B,S,128]
     scores = torch.full((B, S, Lmax), float("nan"), dtype=torch.float32, device="cuda")
     q8 = torch.empty((B, S, H, 128), dtype=torch.uint8, device="cuda")
     qs = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
     dsa.indexer(dev_act(q_raw, act_bf16), dev(w), dev(pos), dcos, dsin, kc, ks, scores,
-                k_raw=dev_act(k_call, act_bf16), q_fp8=q8, q_scale=qs)
+                k_raw=dev_act(k_call, act_bf16), q_fp8=q8, q_scale=qs, hadamard=had,
+                pow2_scale=pow2)
     torch.cuda.synchronize()
     return dict(q_raw=q_raw, k_all=k_all, w=w, pos=pos, cos=cos, sin=sin, kc=host(kc),
                 ks=host(ks), q8=host(q8), qs=host(qs), scores=host(scores))
 
 
-def oracle_indexer(r, act_bf16):
+def oracle_indexer(r, act_bf16, had=False, pow2=False):
     B, Lmax = r["k_all"].shape[:2]
     kpos = np.broadcast_to(np.arange(Lmax, dtype=np.int32), (B, Lmax))
-    k8, ks, _ = oracle.indexer_prepare(r["k_all"], kpos, r["cos"], r["sin"], act_bf16)
+    k8, ks, _ = oracle.indexer_prepare(r["k_all"], kpos, r["cos"], r["sin"], act_bf16,
+                                       hadamard_rot=had, pow2=pow2)
     q8, qs, _ = oracle.indexer_prepare(r["q_raw"], r["pos"][..., None], r["cos"], r["sin"],
-                                       act_bf16)
+                                       act_bf16, hadamard_rot=had, pow2=pow2)
     sc = oracle.indexer_scores(oracle.dequantize(q8, qs), r["w"], oracle.dequantize(k8, ks),
                                r["pos"] + 1)
     return dict(k8=k8, ks=ks, q8=q8, qs=qs, scores=sc)
@@ -159,3 +163,61 @@ def test_positions_out_of_range_are_skipped():
     torch.cuda.synchronize()
     assert np.all(host(scores) == 7.0)
     assert np.all(host(kc) == 0) and np.all(host(ks) == 0)
+
+
+FLAG_CASES = [
+    # name, B, S, H, Lmax, positions, bf16, seed, hadamard, pow2 scales
+    ("had-ragged-bf16", 3, 2, 20, 1000, [[999, 5], [0, 640], [63, 64]], True, 111, True, False),
+    ("had-f32", 1, 3, 64, 700, [[699, 100, 1]], False, 112, True, False),
+    ("pow2-ragged", 2, 2, 64, 300, [[299, 10], [150, 0]], True, 113, False, True),
+    ("had-pow2-tail", 2, 1, 64, 4133, [[4132], [2000]], True, 114, True, True),
+    ("had-decode", 1, 1, 64, 2048, [[2047]], True, 115, True, False),
+]
+
+
+@pytest.mark.parametrize("name,B,S,H,Lmax,pos,bf16,seed,had,pow2", FLAG_CASES,
+                         ids=[c[0] for c in FLAG_CASES])
+def test_indexer_hadamard_pow2_parity(name, B, S, H, Lmax, pos, bf16, seed, had, pow2):
+    """The optional Hadamard rotation and power-of-two scales: codes and
+    scales bit-identical to the oracle's, scores within the tolerance."""
+    say(f"indexer flags case {name}: B={B} S={S} H={H} Lmax={Lmax} had={had} pow2={pow2}")
+    r = run_indexer(B, S, H, Lmax, pos, bf16, seed, had=had, pow2=pow2)
+    o = oracle_indexer(r, bf16, had=had, pow2=pow2)
+    assert np.array_equal(r["q8"], o["q8"]) and np.array_equal(r["qs"], o["qs"])
+    assert np.array_equal(r["kc"], o["k8"]) and np.array_equal(r["ks"], o["ks"])
+    if pow2:
+        m, _ = np.frexp(r["qs"].astype(np.float64))
+        assert np.all(m == 0.5)
+    n_valid = r["pos"] + 1
+    gs = r["scores"].reshape(B * S, Lmax)
+    worst = check_scores(gs, o["scores"].reshape(B * S, Lmax), n_valid, name)
+    say(f"  worst normalised score error {worst:.2e}")
+    for row, n in enumerate(n_valid.reshape(-1)):
+        assert np.all(np.isnan(gs[row, n:])), "entries past the causal end were written"
+
+
+def test_pow2_scales_of_tiny_rows():
+    """Rows so small that amax/448 is a float32 subnormal: the power-of-two
+    scale is still the oracle's (and zero rows keep scale 1)."""
+    import torch
+    B, S, H, Lmax = 1, 1, 8, 16
+    g = synth.rng(17)
+    q_raw = g.standard_normal((B, S, H, 128)).astype(np.float32)
+    q_raw[0, 0, 0] *= np.float32(1e-37)
+    q_raw[0, 0, 1] *= np.float32(3e-39)
+    q_raw[0, 0, 2] = 0.0
+    q_raw[0, 0, 3] *= np.float32(1e-30)
+    cos, sin = oracle.rope_table(Lmax)
+    pos = np.array([[Lmax - 1]], np.int32)
+    kc = torch.zeros((B, Lmax, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, Lmax), dtype=torch.float32, device="cuda")
+    dsa.indexer_append(dev(g.standard_normal((B, Lmax, 128)).astype(np.float32)),
+                       dev(np.arange(Lmax, dtype=np.int32)[None]), dev(cos), dev(sin), kc, ks,
+                       pow2_scale=True)
+    q8 = torch.empty((B, S, H, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, S, H), dtype=torch.float32, device="cuda")
+    dsa.indexer(dev(q_raw), dev(np.ones((B, S, H), np.float32)), dev(pos), dev(cos), dev(sin),
+                kc, ks, q_fp8=q8, q_scale=qs, pow2_scale=True)
+    oq8, oqs, _ = oracle.indexer_prepare(q_raw, pos[..., None], cos, sin, False, pow2=True)
+    assert np.array_equal(host(qs), oqs) and np.array_equal(host(q8), oq8)
+    assert host(qs)[0, 0, 2] == 1.0

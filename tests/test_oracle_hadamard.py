@@ -1,0 +1,79 @@
+"""Pins of the oracle's Hadamard rotation and power-of-two block scales
+(page "Sparse latent attention": the indexer's q and k are multiplied by
+H_128 / sqrt(128) before quantisation; page "Rotate first features":
+rotate_activation ahead of act_quant with its scale_fmt option)."""
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+
+
+
+def _rows(seed, n, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal((n, 128)) * scale).astype(np.float32)
+
+
+def test_hadamard_matches_library_matrix_product():
+    # scipy's Sylvester Hadamard matrix, float64 product, against the float32
+    # transform: each output is a 128-term signed sum, rounded at 7 levels
+    x = _rows(0, 64)
+    ref = x.astype(np.float64) @ scipy.linalg.hadamard(128).astype(np.float64).T / np.sqrt(128.0)
+    got = oracle.hadamard(x).astype(np.float64)
+    bound = 8 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / np.sqrt(128)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+
+
+def test_hadamard_unit_vectors_and_signs():
+    e = np.eye(128, dtype=np.float32)
+    got = oracle.hadamard(e).astype(np.float64) * np.sqrt(128.0)
+    # row i of the result is column i of H_128 = (-1)^popcount(i & j)
+    j = np.arange(128)
+    expect = np.array([[(-1.0) ** bin(i & jj).count("1") for jj in j] for i in range(128)])
+    np.testing.assert_allclose(got, expect, rtol=0, atol=1e-6)
+    # e_0 maps to the constant vector 128^-0.5
+    np.testing.assert_allclose(oracle.hadamard(e[:1]), np.full((1, 128), 128 ** -0.5), rtol=1e-7)
+
+
+def test_hadamard_is_orthonormal_involution():
+    x = _rows(1, 32, 3.0)
+    y = oracle.hadamard(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+    np.testing.assert_allclose(oracle.hadamard(y), x, rtol=0, atol=1e-5 * np.abs(x).max())
+
+
+def test_hadamard_bf16_output_is_rounded_float32_result():
+    x = _rows(2, 16)
+    np.testing.assert_array_equal(oracle.hadamard(x, out_bf16=True),
+                                  oracle.round_bf16(oracle.hadamard(x)))
+
+
+def test_hadamard_leaves_exact_indexer_scores_unchanged():
+    # orthonormal: q.k is preserved, so ReLU(q.k) and the score are too
+    q, k = _rows(3, 8).astype(np.float64), _rows(4, 8).astype(np.float64)
+    H = scipy.linalg.hadamard(128) / np.sqrt(128.0)
+    np.testing.assert_allclose((q @ H.T) @ (k @ H.T).T, q @ k.T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("scale", [1e-6, 0.3, 1.0, 17.0, 3e4])
+def test_pow2_scales(scale):
+    x = _rows(5, 256, scale)
+    x[0] = 0.0
+    codes, s = oracle.quantize(x, pow2=True)
+    amax = np.abs(x).max(axis=1)
+    base = (amax / np.float32(448.0)).astype(np.float32)
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)                                   # powers of two
+    nz = amax > 0
+    assert np.all(s[nz] >= base[nz]) and np.all(s[nz] < 2 * base[nz])
+    assert s[0] == 1.0
+    assert np.all(np.abs(x[nz]) / s[nz, None] <= 448.0)
+    # codes are the E4M3 encodings of the exact quotients
+    np.testing.assert_array_equal(codes, oracle.e4m3_encode(x / s[:, None]))
+
+
+def test_pow2_scale_of_exact_power_of_two_is_itself():
+    x = np.zeros((1, 128), np.float32)
+    x[0, 5] = 448.0 * 2.0 ** -3
+    _, s = oracle.quantize(x, pow2=True)
+    assert s[0] == 2.0 ** -3
