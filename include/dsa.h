@@ -32,6 +32,20 @@
  *  - dsa_status 0 means success. A failed launch reports DSA_ERR_HIP.
  *    Device-side faults surface at the caller's next synchronisation.
  *  - bf16 data is passed as uint16 bit patterns.
+ *  - Paged caches. Every call that reads or writes a per-position cache
+ *    (k_cache/k_scale, latent/rope) takes the same four optional fields:
+ *      block_table  int32 [B][max_pages] (NULL: dense caches)
+ *      page_size    positions per page, a power of two in [1, 65536]
+ *      max_pages    row length of block_table, >= ceil(Lmax / page_size)
+ *      num_pages    pages in the pool, >= 1
+ *    Position p of batch row b then lives in pool row
+ *    block_table[b][p / page_size] * page_size + p % page_size, and the
+ *    cache pointers address the pool (batch strides are ignored). A table
+ *    entry outside [0, num_pages) marks the page as not present: the
+ *    indexer scores such a key -inf and appends nothing there, the attention
+ *    skips it, dsa_mla_append writes nothing there. The pages name paged
+ *    variants of the indexer kernels without giving their layout; this is
+ *    the plain block-table reading.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -45,7 +59,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /* Fixed head geometry (page "Sparse latent attention": 64 indexer heads of
  * 128 features, one shared 128-feature key per position, a 512-feature
@@ -174,6 +188,8 @@ typedef struct dsa_indexer_args {
     uint32_t flags;              /* 0 or DSA_INDEXER_APPEND_ONLY */
     void* workspace;
     size_t workspace_bytes;
+    const int32_t* block_table;  /* paged k_cache/k_scale (see the conventions) */
+    int32_t page_size, max_pages, num_pages;
 } dsa_indexer_args;
 
 dsa_status dsa_indexer_workspace(const dsa_indexer_args* args, size_t* bytes);
@@ -253,6 +269,8 @@ typedef struct dsa_mla_args {
     float* lse;                  /* optional */
     void* workspace;
     size_t workspace_bytes;
+    const int32_t* block_table;  /* paged latent/rope (see the conventions) */
+    int32_t page_size, max_pages, num_pages;
 } dsa_mla_args;
 
 dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* args, size_t* bytes);
@@ -294,6 +312,8 @@ typedef struct dsa_mla_append_args {
     int64_t rope_row_stride;
     int64_t rope_batch_stride;
     uint16_t* q;                 /* optional, rotated in place */
+    const int32_t* block_table;  /* paged latent/rope (see the conventions) */
+    int32_t page_size, max_pages, num_pages;
 } dsa_mla_append_args;
 
 dsa_status dsa_mla_append(const dsa_mla_append_args* args, hipStream_t stream);

@@ -52,7 +52,7 @@ class IndexerArgs(ctypes.Structure):
                 ("rope_cos", _vp), ("rope_sin", _vp), ("w", _vp), ("k_cache", _vp),
                 ("k_scale", _vp), ("q_fp8", _vp), ("q_scale", _vp), ("scores", _vp),
                 ("ld_scores", _i64), ("flags", ctypes.c_uint32), ("workspace", _vp),
-                ("workspace_bytes", _sz)]
+                ("workspace_bytes", _sz), ("block_table", _vp), ("page_size", _i32), ("max_pages", _i32), ("num_pages", _i32)]
 
 
 class TopkArgs(ctypes.Structure):
@@ -66,7 +66,8 @@ class MlaArgs(ctypes.Structure):
                 ("q", _vp), ("latent", _vp), ("latent_row_stride", _i64),
                 ("latent_batch_stride", _i64), ("rope", _vp), ("rope_row_stride", _i64),
                 ("rope_batch_stride", _i64), ("idx", _vp), ("scale", _f32), ("out", _vp),
-                ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+                ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
+                ("block_table", _vp), ("page_size", _i32), ("max_pages", _i32), ("num_pages", _i32)]
 
 
 class MlaAppendArgs(ctypes.Structure):
@@ -74,7 +75,8 @@ class MlaAppendArgs(ctypes.Structure):
                 ("latent_new", _vp), ("kpe_new", _vp), ("pos", _vp), ("rope_cos", _vp),
                 ("rope_sin", _vp), ("latent", _vp), ("latent_row_stride", _i64),
                 ("latent_batch_stride", _i64), ("rope", _vp), ("rope_row_stride", _i64),
-                ("rope_batch_stride", _i64), ("q", _vp)]
+                ("rope_batch_stride", _i64), ("q", _vp),
+                ("block_table", _vp), ("page_size", _i32), ("max_pages", _i32), ("num_pages", _i32)]
 
 
 EXPORTS = ("dsa_rope_table", "dsa_indexer_workspace", "dsa_indexer", "dsa_topk_workspace",
@@ -162,15 +164,45 @@ def rope_table(P: int, yarn: bool = False, theta: float = 10000.0, orig_len: int
     return cos, sin
 
 
+class Paging:
+    """A paged cache layout: block_table int32 [B, max_pages] (device) maps
+    page p // page_size of batch row b to a page of a pool of num_pages
+    pages; the caches passed with it are pools [num_pages, page_size, ...]."""
+
+    def __init__(self, block_table, page_size: int, num_pages: int):
+        import torch
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                not block_table.is_contiguous() or not block_table.is_cuda:
+            raise ValueError("block_table must be a contiguous int32 device tensor [B, max_pages]")
+        self.block_table, self.page_size, self.num_pages = block_table, int(page_size), int(num_pages)
+        self.max_pages = block_table.shape[1]
+
+    @property
+    def lmax(self) -> int:
+        return self.max_pages * self.page_size
+
+    def set_fields(self, a):
+        a.block_table = _ptr(self.block_table)
+        a.page_size, a.max_pages, a.num_pages = self.page_size, self.max_pages, self.num_pages
+
+
+def _cache_rows(t, paging, B):
+    """(Lmax, leading shape) of a dense [B, Lmax, ...] cache or a pool."""
+    if paging is None:
+        return t.shape[1], (B, t.shape[1])
+    return paging.lmax, (paging.num_pages, paging.page_size)
+
+
 def _prep_flags(hadamard, pow2_scale):
     return (HADAMARD if hadamard else 0) | (POW2_SCALE if pow2_scale else 0)
 
 
 def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, q_fp8=None,
-                 q_scale=None, workspace=None, hadamard=False, pow2_scale=False) -> IndexerArgs:
+                 q_scale=None, workspace=None, hadamard=False, pow2_scale=False,
+                 paging=None) -> IndexerArgs:
     import torch
     B, S, H, D = q_raw.shape
-    Lmax = k_cache.shape[1]
+    Lmax, lead = _cache_rows(k_cache, paging, B)
     dt = {torch.float32: DSA_DTYPE_F32, torch.bfloat16: DSA_DTYPE_BF16}.get(q_raw.dtype)
     if dt is None:
         raise TypeError("q_raw must be float32 or bfloat16")
@@ -179,8 +211,8 @@ def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, 
     _need(pos, "pos", torch.int32, (B, S))
     _need(cos, "cos", torch.float32)
     _need(sin, "sin", torch.float32, cos.shape)
-    _need(k_cache, "k_cache", torch.uint8, (B, Lmax, INDEX_DIM))
-    _need(k_scale, "k_scale", torch.float32, (B, Lmax))
+    _need(k_cache, "k_cache", torch.uint8, lead + (INDEX_DIM,))
+    _need(k_scale, "k_scale", torch.float32, lead)
     if scores.dim() != 3 or scores.shape[:2] != (B, S) or scores.stride(2) != 1 \
             or scores.stride(0) != S * scores.stride(1):
         raise ValueError("scores must be [B, S, >=Lmax] with unit inner stride")
@@ -191,19 +223,23 @@ def indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw=None, 
     if q_fp8 is not None:
         _need(q_fp8, "q_fp8", torch.uint8, (B, S, H, INDEX_DIM))
         _need(q_scale, "q_scale", torch.float32, (B, S, H))
-    return IndexerArgs(B, S, H, Lmax, cos.shape[0], dt, _ptr(q_raw), _ptr(k_raw), _ptr(pos),
-                       _ptr(cos), _ptr(sin), _ptr(w), _ptr(k_cache), _ptr(k_scale),
-                       _ptr(q_fp8), _ptr(q_scale), _ptr(scores), scores.stride(1),
-                       _prep_flags(hadamard, pow2_scale), _ptr(workspace),
-                       0 if workspace is None else workspace.numel())
+    a = IndexerArgs(B, S, H, Lmax, cos.shape[0], dt, _ptr(q_raw), _ptr(k_raw), _ptr(pos),
+                    _ptr(cos), _ptr(sin), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                    _ptr(q_fp8), _ptr(q_scale), _ptr(scores), scores.stride(1),
+                    _prep_flags(hadamard, pow2_scale), _ptr(workspace),
+                    0 if workspace is None else workspace.numel())
+    if paging is not None:
+        paging.set_fields(a)
+    return a
 
 
-def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale, hadamard=False, pow2_scale=False):
+def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale, hadamard=False, pow2_scale=False,
+                   paging=None):
     """Call 1 with DSA_INDEXER_APPEND_ONLY: rotate, quantise and write the
     key rows k_raw [B, S, 128] into k_cache/k_scale at pos [B, S]."""
     import torch
     B, S = pos.shape
-    Lmax = k_cache.shape[1]
+    Lmax, lead = _cache_rows(k_cache, paging, B)
     dt = {torch.float32: DSA_DTYPE_F32, torch.bfloat16: DSA_DTYPE_BF16}.get(k_raw.dtype)
     if dt is None:
         raise TypeError("k_raw must be float32 or bfloat16")
@@ -211,11 +247,13 @@ def indexer_append(k_raw, pos, cos, sin, k_cache, k_scale, hadamard=False, pow2_
     _need(pos, "pos", torch.int32, (B, S))
     _need(cos, "cos", torch.float32)
     _need(sin, "sin", torch.float32, cos.shape)
-    _need(k_cache, "k_cache", torch.uint8, (B, Lmax, INDEX_DIM))
-    _need(k_scale, "k_scale", torch.float32, (B, Lmax))
+    _need(k_cache, "k_cache", torch.uint8, lead + (INDEX_DIM,))
+    _need(k_scale, "k_scale", torch.float32, lead)
     a = IndexerArgs(B, S, 1, Lmax, cos.shape[0], dt, None, _ptr(k_raw), _ptr(pos), _ptr(cos),
                     _ptr(sin), None, _ptr(k_cache), _ptr(k_scale), None, None, None, Lmax,
                     APPEND_ONLY | _prep_flags(hadamard, pow2_scale), None, 0)
+    if paging is not None:
+        paging.set_fields(a)
     _check(lib().dsa_indexer(ctypes.byref(a), _stream()))
 
 
@@ -231,16 +269,17 @@ def _workspace(nbytes, device):
 
 
 def indexer(q_raw, w, pos, cos, sin, k_cache, k_scale, scores=None, k_raw=None, q_fp8=None,
-            q_scale=None, workspace=None, hadamard=False, pow2_scale=False):
+            q_scale=None, workspace=None, hadamard=False, pow2_scale=False, paging=None):
     """Call 1: append k_raw rows (if given) and score every causal key.
     Returns scores [B, S, Lmax] float32 (entries past each row's position
     are left as they were)."""
     import torch
     B, S = q_raw.shape[:2]
     if scores is None:
-        scores = torch.empty((B, S, k_cache.shape[1]), dtype=torch.float32, device=q_raw.device)
+        L = k_cache.shape[1] if paging is None else paging.lmax
+        scores = torch.empty((B, S, L), dtype=torch.float32, device=q_raw.device)
     a = indexer_args(q_raw, w, pos, cos, sin, k_cache, k_scale, scores, k_raw, q_fp8, q_scale,
-                     workspace, hadamard, pow2_scale)
+                     workspace, hadamard, pow2_scale, paging)
     need = indexer_workspace_bytes(a)
     if need and (workspace is None or workspace.numel() < need):
         workspace = _workspace(need, q_raw.device)
@@ -296,7 +335,22 @@ def topk(scores, pos, K: int, idx=None, count=None, workspace=None):
     return idx
 
 
-def mla_args(q, latent, rope, idx, scale, out, lse=None, workspace=None) -> MlaArgs:
+def _check_latent_caches(latent, rope, paging, B):
+    import torch
+    for name, t, d in (("latent", latent, LATENT_DIM), ("rope", rope, ROPE_DIM)):
+        lead = B if paging is None else paging.num_pages
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != lead \
+                or t.shape[2] != d or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor [{'B, Lmax' if paging is None else 'num_pages, page_size'}, {d}] "
+                             "with unit inner stride")
+        if paging is not None and t.shape[1] != paging.page_size:
+            raise ValueError(f"{name} pool pages must hold page_size rows")
+    if latent.shape[1] != rope.shape[1]:
+        raise ValueError("latent and rope must have the same number of rows")
+    return latent.shape[1] if paging is None else paging.lmax
+
+
+def mla_args(q, latent, rope, idx, scale, out, lse=None, workspace=None, paging=None) -> MlaArgs:
     import torch
     B, S, Hq, Dq = q.shape
     K = idx.shape[-1]
@@ -305,17 +359,14 @@ def mla_args(q, latent, rope, idx, scale, out, lse=None, workspace=None) -> MlaA
     _need(out, "out", torch.bfloat16, (B, S, Hq, LATENT_DIM))
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, S, Hq))
-    for name, t, d in (("latent", latent, LATENT_DIM), ("rope", rope, ROPE_DIM)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != B \
-                or t.shape[2] != d or t.stride(2) != 1:
-            raise ValueError(f"{name} must be a bf16 device tensor [B, Lmax, {d}] "
-                             "with unit inner stride")
-    if latent.shape[1] != rope.shape[1]:
-        raise ValueError("latent and rope must have the same Lmax")
-    return MlaArgs(B, S, Hq, latent.shape[1], K, _ptr(q), _ptr(latent), latent.stride(1),
-                   latent.stride(0), _ptr(rope), rope.stride(1), rope.stride(0), _ptr(idx),
-                   float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                   0 if workspace is None else workspace.numel())
+    Lmax = _check_latent_caches(latent, rope, paging, B)
+    a = MlaArgs(B, S, Hq, Lmax, K, _ptr(q), _ptr(latent), latent.stride(1),
+                latent.stride(0), _ptr(rope), rope.stride(1), rope.stride(0), _ptr(idx),
+                float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                0 if workspace is None else workspace.numel())
+    if paging is not None:
+        paging.set_fields(a)
+    return a
 
 
 def sparse_mla_workspace_bytes(args: MlaArgs) -> int:
@@ -325,7 +376,7 @@ def sparse_mla_workspace_bytes(args: MlaArgs) -> int:
 
 
 def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace=None,
-               return_lse: bool = False):
+               return_lse: bool = False, paging=None):
     """Call 3: absorbed sparse MLA; returns out [B, S, Hq, 512] bf16 (and lse)."""
     import torch
     B, S, Hq, _ = q.shape
@@ -333,7 +384,7 @@ def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace
         out = torch.empty((B, S, Hq, LATENT_DIM), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device)
-    a = mla_args(q, latent, rope, idx, scale, out, lse, workspace)
+    a = mla_args(q, latent, rope, idx, scale, out, lse, workspace, paging)
     need = sparse_mla_workspace_bytes(a)
     if need and (workspace is None or workspace.numel() < need):
         workspace = _workspace(need, q.device)
@@ -342,7 +393,7 @@ def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace
     return (out, lse) if return_lse else out
 
 
-def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None):
+def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None, paging=None):
     """Write latent_new [B, S, 512] and the interleaved-RoPE-rotated kpe_new
     [B, S, 64] into the caches latent / rope ([B, Lmax, 512] / [B, Lmax, 64]
     views with unit inner stride) at pos [B, S]; if q [B, S, Hq, 576] is
@@ -354,20 +405,16 @@ def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None):
     _need(kpe_new, "kpe_new", torch.bfloat16, (B, S, ROPE_DIM))
     _need(cos, "cos", torch.float32)
     _need(sin, "sin", torch.float32, cos.shape)
-    for name, t, d in (("latent", latent, LATENT_DIM), ("rope", rope, ROPE_DIM)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.shape[0] != B \
-                or t.shape[2] != d or t.stride(2) != 1:
-            raise ValueError(f"{name} must be a bf16 device tensor [B, Lmax, {d}] "
-                             "with unit inner stride")
-    if latent.shape[1] != rope.shape[1]:
-        raise ValueError("latent and rope must have the same Lmax")
+    Lmax = _check_latent_caches(latent, rope, paging, B)
     Hq = 0
     if q is not None:
         Hq = q.shape[2]
         _need(q, "q", torch.bfloat16, (B, S, Hq, LATENT_DIM + ROPE_DIM))
-    a = MlaAppendArgs(B, S, Hq, latent.shape[1], cos.shape[0], _ptr(latent_new), _ptr(kpe_new),
+    a = MlaAppendArgs(B, S, Hq, Lmax, cos.shape[0], _ptr(latent_new), _ptr(kpe_new),
                       _ptr(pos), _ptr(cos), _ptr(sin), _ptr(latent), latent.stride(1),
                       latent.stride(0), _ptr(rope), rope.stride(1), rope.stride(0), _ptr(q))
+    if paging is not None:
+        paging.set_fields(a)
     _check(lib().dsa_mla_append(ctypes.byref(a), _stream()))
 
 

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "dsa_common.h"
+
 #include <cmath>
 #include <cstdint>
 
@@ -14,16 +16,16 @@ hipError_t launch_rope_table(int P, int npairs, double base, int yarn, double lo
 hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
                           int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
                           const float* sin_t, uint8_t* codes, float* scales, bool hadamard,
-                          bool pow2, hipStream_t stream);
+                          bool pow2, CacheMap cmap, hipStream_t stream);
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
-                        hipStream_t stream);
+                        CacheMap cmap, hipStream_t stream);
 hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, const void* q_raw,
                                const void* k_raw, const int32_t* pos, const float* cos_t,
                                const float* sin_t, const float* w, uint8_t* kcache,
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
-                               int64_t ld, hipStream_t stream);
+                               int64_t ld, CacheMap cmap, hipStream_t stream);
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
                        const int32_t* pos, int32_t* idx, int32_t* count, void* workspace,
                        hipStream_t stream);
@@ -33,12 +35,12 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
                              const int32_t* idx, float scale, uint16_t* out, float* lse,
-                             void* workspace, hipStream_t stream);
+                             void* workspace, CacheMap cmap, hipStream_t stream);
 hipError_t launch_mla_append(int B, int S, int Hq, int Lmax, int P, const uint16_t* latent_new,
                              const uint16_t* kpe_new, const int32_t* pos, const float* cos_t,
                              const float* sin_t, uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              uint16_t* rope, int64_t rope_rs, int64_t rope_bs, uint16_t* q,
-                             hipStream_t stream);
+                             CacheMap cmap, hipStream_t stream);
 }  // namespace dsa
 
 namespace {
@@ -48,6 +50,32 @@ constexpr int64_t kMaxGridY = 65535;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// paged-cache fields (shared by every call that touches a per-position cache)
+dsa_status check_paging(const int32_t* table, int32_t page_size, int32_t max_pages,
+                        int32_t num_pages, int32_t Lmax) {
+    if (table == nullptr) return DSA_OK;
+    if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0 ||
+        num_pages < 1 || max_pages < 1)
+        return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(max_pages) * page_size < Lmax) return DSA_ERR_SHAPE;
+    if (static_cast<int64_t>(num_pages) * page_size > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
+    if (!aligned4(table)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+dsa::CacheMap make_map(const int32_t* table, int32_t page_size, int32_t max_pages,
+                       int32_t num_pages, int64_t batch_rows) {
+    dsa::CacheMap m{};
+    m.table = table;
+    m.batch_rows = batch_rows;
+    m.max_pages = max_pages;
+    m.num_pages = num_pages;
+    int sh = 0;
+    while (table != nullptr && (1 << sh) < page_size) ++sh;
+    m.page_shift = sh;
+    return m;
+}
 
 // ------------------------------------------------------------- indexer ---
 dsa_status check_indexer(const dsa_indexer_args* a) {
@@ -80,7 +108,7 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
         ((reinterpret_cast<uintptr_t>(a->q_raw) & amask) || (a->q_fp8 && !aligned16(a->q_fp8)) ||
          !aligned4(a->scores) || !aligned4(a->w) || (a->q_scale && !aligned4(a->q_scale))))
         return DSA_ERR_ALIGN;
-    return DSA_OK;
+    return check_paging(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
 }
 
 // the fused single-row decode launch covers the plain preparation only
@@ -128,7 +156,7 @@ dsa_status check_mla(const dsa_mla_args* a) {
     if ((a->latent_row_stride % 8) || (a->latent_batch_stride % 8) || (a->rope_row_stride % 8) ||
         (a->rope_batch_stride % 8))
         return DSA_ERR_ALIGN;
-    return DSA_OK;
+    return check_paging(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
 }
 
 dsa_status check_mla_append(const dsa_mla_append_args* a) {
@@ -149,7 +177,7 @@ dsa_status check_mla_append(const dsa_mla_append_args* a) {
     if ((a->latent_row_stride % 8) || (a->latent_batch_stride % 8) || (a->rope_row_stride % 8) ||
         (a->rope_batch_stride % 8))
         return DSA_ERR_ALIGN;
-    return DSA_OK;
+    return check_paging(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
 }
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
@@ -229,25 +257,27 @@ dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
     hipError_t e = hipSuccess;
     const bool had = (a->flags & DSA_INDEXER_HADAMARD) != 0;
     const bool pow2 = (a->flags & DSA_INDEXER_POW2_SCALE) != 0;
+    const dsa::CacheMap cmap =
+        make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
     if (fused_decode(a)) {
         // decode: one fused launch (quantise q, append the new key, score)
         e = dsa::launch_decode_score(bf16, a->B, a->H, a->Lmax, a->P, a->q_raw, a->k_raw, a->pos,
                                      a->rope_cos, a->rope_sin, a->w, a->k_cache, a->k_scale,
-                                     a->q_fp8, a->q_scale, a->scores, a->ld_scores, stream);
+                                     a->q_fp8, a->q_scale, a->scores, a->ld_scores, cmap, stream);
         return hip_status(e);
     }
     if (a->k_raw != nullptr) {
         e = dsa::launch_prepare(bf16, true, static_cast<int64_t>(a->B) * a->S, 1, a->S, a->Lmax,
                                 a->P, a->k_raw, a->pos, a->rope_cos, a->rope_sin, a->k_cache,
-                                a->k_scale, had, pow2, stream);
+                                a->k_scale, had, pow2, cmap, stream);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     if (a->flags & DSA_INDEXER_APPEND_ONLY) return DSA_OK;
     e = dsa::launch_prepare(bf16, false, qrows, a->H, a->S, a->Lmax, a->P, a->q_raw, a->pos,
-                            a->rope_cos, a->rope_sin, q8, qs, had, pow2, stream);
+                            a->rope_cos, a->rope_sin, q8, qs, had, pow2, cmap, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
     e = dsa::launch_score(a->B, a->S, a->H, a->Lmax, a->P, q8, qs, a->w, a->pos, a->k_cache,
-                          a->k_scale, a->scores, a->ld_scores, stream);
+                          a->k_scale, a->scores, a->ld_scores, cmap, stream);
     return hip_status(e);
 }
 
@@ -290,7 +320,8 @@ dsa_status dsa_sparse_mla(const dsa_mla_args* a, hipStream_t stream) {
     return hip_status(dsa::launch_sparse_mla(
         a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->latent, a->latent_row_stride,
         a->latent_batch_stride, a->rope, a->rope_row_stride, a->rope_batch_stride, a->idx,
-        a->scale, a->out, a->lse, a->workspace, stream));
+        a->scale, a->out, a->lse, a->workspace,
+        make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, 0), stream));
 }
 
 dsa_status dsa_mla_append(const dsa_mla_append_args* a, hipStream_t stream) {
@@ -299,7 +330,8 @@ dsa_status dsa_mla_append(const dsa_mla_append_args* a, hipStream_t stream) {
     return hip_status(dsa::launch_mla_append(
         a->B, a->S, a->q ? a->Hq : 0, a->Lmax, a->P, a->latent_new, a->kpe_new, a->pos,
         a->rope_cos, a->rope_sin, a->latent, a->latent_row_stride, a->latent_batch_stride,
-        a->rope, a->rope_row_stride, a->rope_batch_stride, a->q, stream));
+        a->rope, a->rope_row_stride, a->rope_batch_stride, a->q,
+        make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, 0), stream));
 }
 
 }  // extern "C"

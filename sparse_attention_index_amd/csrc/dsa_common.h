@@ -124,4 +124,23 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Where position p of batch row b lives in a cache. Dense caches: row
+// b * batch_rows + p. Paged caches: page table[b][p >> page_shift] of a pool
+// of num_pages pages of 2^page_shift rows; row page << page_shift | offset.
+// A page index outside [0, num_pages) means "not present" (row -1).
+struct CacheMap {
+    const int32_t* table;       // nullptr: dense
+    int64_t batch_rows;         // dense: rows per batch row
+    int32_t max_pages;          // table row length
+    int32_t page_shift;
+    int32_t num_pages;
+
+    __device__ __forceinline__ int64_t row(int64_t b, int p) const {
+        if (table == nullptr) return b * batch_rows + p;
+        const int pg = table[b * max_pages + (p >> page_shift)];
+        if (pg < 0 || pg >= num_pages) return -1;
+        return (static_cast<int64_t>(pg) << page_shift) | (p & ((1 << page_shift) - 1));
+    }
+};
+
 }  // namespace dsa

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
     int64_t nrows, int rows_per_pos, int S, int Lmax, int P, const void* __restrict__ x,
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, uint8_t* __restrict__ codes_out,
-    float* __restrict__ scales_out, int had, int pow2) {
+    float* __restrict__ scales_out, int had, int pow2, CacheMap cmap) {
     const int lane = threadIdx.x & 63;
     const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRows;
     if (row0 >= nrows) return;
@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
         int64_t dst;
         if (TO_CACHE) {
             const int64_t b = (row / rows_per_pos) / S;
-            dst = b * Lmax + p[k];
+            dst = cmap.row(b, p[k]);
+            if (dst < 0) continue;                  // page not present: nothing to write
         } else {
             dst = row;
         }
@@ -151,14 +152,14 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
 hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_per_pos, int S,
                           int Lmax, int P, const void* x, const int32_t* pos, const float* cos_t,
                           const float* sin_t, uint8_t* codes, float* scales, bool hadamard,
-                          bool pow2, hipStream_t stream) {
+                          bool pow2, CacheMap cmap, hipStream_t stream) {
     if (nrows <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>((nrows + 4 * kPrepRows - 1) / (4 * kPrepRows))),
         block(256);
 #define DSA_PREP(B, C)                                                                         \
     hipLaunchKernelGGL((prepare_rows_kernel<B, C>), grid, block, 0, stream, nrows, rows_per_pos, \
                        S, Lmax, P, x, pos, cos_t, sin_t, codes, scales, hadamard ? 1 : 0,       \
-                       pow2 ? 1 : 0)
+                       pow2 ? 1 : 0, cmap)
     if (bf16_in) {
         if (to_cache) DSA_PREP(true, true); else DSA_PREP(true, false);
     } else {
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
     int B, int S, int H, int Lmax, int P, int nqt, int nkt, const uint8_t* __restrict__ q8,
     const float* __restrict__ qscale, const float* __restrict__ w,
     const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
-    const float* __restrict__ kscale, float* __restrict__ scores, int64_t ld) {
+    const float* __restrict__ kscale, float* __restrict__ scores, int64_t ld, CacheMap cmap) {
     __shared__ __align__(16) uint16_t Qs[2][kQT][kQsStride];
     __shared__ __align__(16) float wqs[64][kQT];       // [head][query] w * q_scale
     __shared__ int nv[kQT];                            // n_valid per query of the tile
@@ -251,19 +252,19 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
     const int wq_i = wave & 1, wk = wave >> 1;
     const int hi32 = lane >> 5, l32 = lane & 31;
     bf16x8 kb[kKW][8];
-    float ksc[kKW];
-    const uint8_t* kbase = kcache + static_cast<int64_t>(b) * Lmax * 128;
+    float ksc[kKW];            // key scale; -inf marks a key whose page is not present
 #pragma unroll
     for (int kt2 = 0; kt2 < kKW; ++kt2) {
         int key = k0 + wk * 32 * kKW + kt2 * 32 + l32;
         key = key < Lmax ? key : Lmax - 1;
-        const uint8_t* kr = kbase + static_cast<int64_t>(key) * 128 + 8 * hi32;
+        const int64_t krow = cmap.row(b, key);
+        const uint8_t* kr = kcache + (krow >= 0 ? krow : 0) * 128 + 8 * hi32;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const uint2 c = *reinterpret_cast<const uint2*>(kr + 16 * ks);
             kb[kt2][ks] = e4m3x8_to_bf16x8(c.x, c.y);
         }
-        ksc[kt2] = kscale[static_cast<int64_t>(b) * Lmax + key];
+        ksc[kt2] = krow >= 0 ? kscale[krow] : -INFINITY;
     }
 
     // staging: thread -> query tid/4, 32 features (tid%4)
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
         for (int i = 0; i < 16; ++i) {
             const int qi = wq_i * 32 + 8 * (i >> 2) + 4 * hi32 + (i & 3);
             if (key < nv[qi]) {
-                const float v = I[kt2][i] * ksc[kt2];
+                const float v = ksc[kt2] == -INFINITY ? -INFINITY : I[kt2][i] * ksc[kt2];
                 scores[(row0 + qi) * ld + key] = v;
             }
         }
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, const float* __restrict__ w, uint8_t* __restrict__ kcache,
     float* __restrict__ kscale, uint8_t* __restrict__ q8_out, float* __restrict__ qs_out,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, CacheMap cmap) {
     __shared__ __align__(16) uint8_t qcodes[64 * 128];
     __shared__ float qscale[64];
     __shared__ __align__(16) uint8_t kcodes[128];
@@ -383,22 +384,24 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t b = row;
-    const uint8_t* kb = kcache + b * Lmax * 128;
-    const float* ksb = kscale + b * Lmax;
     const int wkey0 = kblock0 + wave * 16 * U;
-    const bool has_new = k_raw != nullptr && kblock0 + 64 * U > p;   // block covers key p
+    const int64_t prow = cmap.row(b, p);                              // the new key's row
+    const bool has_new = k_raw != nullptr && prow >= 0 && kblock0 + 64 * U > p;
 
-    // 1. key loads first (the new key, if any, is taken from LDS later)
+    // 1. key loads first (the new key, if any, is taken from LDS later);
+    // ks = -inf marks a key whose page is not present
     uint4 kraw[U][2];
     float ks[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int key = wkey0 + u * 16 + m;
         key = key < n_valid ? key : n_valid - 1;
-        const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * 128 + g * 32);
+        const int64_t krow = cmap.row(b, key);
+        const uint4* src =
+            reinterpret_cast<const uint4*>(kcache + (krow >= 0 ? krow : 0) * 128 + g * 32);
         kraw[u][0] = src[0];
         kraw[u][1] = src[1];
-        ks[u] = ksb[key];
+        ks[u] = krow >= 0 ? kscale[krow] : -INFINITY;
     }
 
     // 2. quantise the row's query heads into LDS
@@ -478,12 +481,12 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
         const uint8_t c0 = e4m3_encode(y0 / scale), c1 = e4m3_encode(x1 / scale);
         kcodes[lane] = c0;
         kcodes[lane + 64] = c1;
-        uint8_t* kdst = kcache + (b * Lmax + p) * 128;
+        uint8_t* kdst = kcache + prow * 128;
         kdst[lane] = c0;
         kdst[lane + 64] = c1;
         if (lane == 0) {
             kscale_new = scale;
-            kscale[b * Lmax + p] = scale;
+            kscale[prow] = scale;
         }
     }
     __syncthreads();
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
         }
         part += __shfl_xor(part, 16);
         part += __shfl_xor(part, 32);
-        if (g == 0 && key < n_valid) out[key] = part * ksc;
+        if (g == 0 && key < n_valid) out[key] = ksc == -INFINITY ? -INFINITY : part * ksc;
     }
 }
 
@@ -547,14 +550,14 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                                const void* k_raw, const int32_t* pos, const float* cos_t,
                                const float* sin_t, const float* w, uint8_t* kcache,
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
-                               int64_t ld, hipStream_t stream) {
+                               int64_t ld, CacheMap cmap, hipStream_t stream) {
     int U = 4;
     while (U > 1 && static_cast<int64_t>(B) * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
     const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)), static_cast<unsigned>(B));
 #define DSA_DEC(UU, BF)                                                                          \
     hipLaunchKernelGGL((decode_score_kernel<UU, BF>), grid, dim3(256), 0, stream, H, Lmax, P,    \
                        q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out, qs_out,     \
-                       scores, ld)
+                       scores, ld, cmap)
     if (bf16_in) {
         if (U == 4) DSA_DEC(4, true); else if (U == 2) DSA_DEC(2, true); else DSA_DEC(1, true);
     } else {
@@ -567,14 +570,14 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
-                        hipStream_t stream) {
+                        CacheMap cmap, hipStream_t stream) {
     const int nqt = (S + kQT - 1) / kQT;
     const int nkt = (Lmax + kKT - 1) / kKT;
     const int64_t qtiles = static_cast<int64_t>(B) * nqt;
     const int64_t nblocks = ((qtiles + 7) / 8) * 8 * nkt;
     hipLaunchKernelGGL(score_tile_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0,
                        stream, B, S, H, Lmax, P, nqt, nkt, q8, qscale, w, pos, kcache, kscale,
-                       scores, ld);
+                       scores, ld, cmap);
     return hipGetLastError();
 }
 

@@ -34,23 +34,34 @@ __global__ __launch_bounds__(256) void mla_append_kernel(
     const uint16_t* __restrict__ kpe_new, const int32_t* __restrict__ pos,
     const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ latent, int64_t lat_rs, int64_t lat_bs, uint16_t* __restrict__ rope,
-    int64_t rope_rs, int64_t rope_bs, uint16_t* __restrict__ q) {
+    int64_t rope_rs, int64_t rope_bs, uint16_t* __restrict__ q, CacheMap cmap) {
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
     const int p = pos[r];
     if (p < 0 || p >= Lmax || p >= P) return;
     const int64_t b = r / S;
-    if (tid < 64) {
+    // cache row of (b, p): dense strides, or the pool row of p's page
+    int64_t lat_off, rope_off;
+    bool present = true;
+    if (cmap.table == nullptr) {
+        lat_off = b * lat_bs + static_cast<int64_t>(p) * lat_rs;
+        rope_off = b * rope_bs + static_cast<int64_t>(p) * rope_rs;
+    } else {
+        const int64_t prow = cmap.row(b, p);
+        present = prow >= 0;                         // no page: no cache write
+        lat_off = prow * lat_rs;
+        rope_off = prow * rope_rs;
+    }
+    if (present && tid < 64) {
         const uint4 v = reinterpret_cast<const uint4*>(latent_new + r * 512)[tid];
-        reinterpret_cast<uint4*>(latent + b * lat_bs + static_cast<int64_t>(p) * lat_rs)[tid] = v;
+        reinterpret_cast<uint4*>(latent + lat_off)[tid] = v;
     }
     const float* cr = cos_t + static_cast<int64_t>(p) * 32;
     const float* sr = sin_t + static_cast<int64_t>(p) * 32;
-    if (tid >= 64 && tid < 96) {
+    if (present && tid >= 64 && tid < 96) {
         const int j = tid - 64;
         const uint32_t ab = reinterpret_cast<const uint32_t*>(kpe_new + r * 64)[j];
-        reinterpret_cast<uint32_t*>(rope + b * rope_bs + static_cast<int64_t>(p) * rope_rs)[j] =
-            rotate_pair_bf16(ab, cr[j], sr[j]);
+        reinterpret_cast<uint32_t*>(rope + rope_off)[j] = rotate_pair_bf16(ab, cr[j], sr[j]);
     }
     if (q != nullptr) {
         for (int i = tid; i < Hq * 32; i += 256) {
@@ -65,11 +76,11 @@ hipError_t launch_mla_append(int B, int S, int Hq, int Lmax, int P, const uint16
                              const uint16_t* kpe_new, const int32_t* pos, const float* cos_t,
                              const float* sin_t, uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              uint16_t* rope, int64_t rope_rs, int64_t rope_bs, uint16_t* q,
-                             hipStream_t stream) {
+                             CacheMap cmap, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(B) * S;
     hipLaunchKernelGGL(mla_append_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream,
                        S, Hq, Lmax, P, latent_new, kpe_new, pos, cos_t, sin_t, latent, lat_rs,
-                       lat_bs, rope, rope_rs, rope_bs, q);
+                       lat_bs, rope, rope_rs, rope_bs, q, cmap);
     return hipGetLastError();
 }
 

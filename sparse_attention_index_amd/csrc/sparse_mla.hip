@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
     const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml, CacheMap cmap) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);
     int* sidx = reinterpret_cast<int*>(Kt + kTile * kKtStride);
@@ -97,11 +97,17 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const int j_end = min(K, j_begin + slots_per_split);
     const int count = j_end - j_begin;
     const int ntiles = count > 0 ? (count + kTile - 1) / kTile : 0;
+    // selected slots -> cache rows: the position itself (dense caches, batch
+    // offset added below) or the pool row of its page (paged caches); -1 for
+    // unselected slots and positions whose page is not present
+    const bool paged = cmap.table != nullptr;
     {
         const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
         for (int i = tid; i < ntiles * kTile; i += kMlaThreads) {
             const int p = i < count ? irow[i] : -1;
-            sidx[i] = (p >= 0 && p < Lmax) ? p : -1;
+            int v = -1;
+            if (p >= 0 && p < Lmax) v = paged ? static_cast<int>(cmap.row(b, p)) : p;
+            sidx[i] = v;
         }
     }
 
@@ -124,8 +130,8 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     // values that actually weight the latent rows (for the normalisation).
     float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
 
-    const uint16_t* lat_b = latent + b * lat_bs;
-    const uint16_t* rope_b = rope + b * rope_bs;
+    const uint16_t* lat_b = latent + (paged ? 0 : b * lat_bs);
+    const uint16_t* rope_b = rope + (paged ? 0 : b * rope_bs);
     __syncthreads();                               // sidx ready
 
     // Gather mapping: 8 threads per key row (wave w loads keys 8w..8w+7);
@@ -431,7 +437,8 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
                                     const uint16_t* q, const uint16_t* latent, int64_t lat_rs,
                                     int64_t lat_bs, const uint16_t* rope, int64_t rope_rs,
                                     int64_t rope_bs, const int32_t* idx, float scale_log2,
-                                    uint16_t* out, float* lse, float* ws_o, float* ws_ml) {
+                                    uint16_t* out, float* lse, float* ws_o, float* ws_ml,
+                                    CacheMap cmap) {
     // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE>),
@@ -439,7 +446,7 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(sparse_mla_kernel<PIPE>, grid, dim3(kMlaThreads), kMlaLdsBytes, stream, S,
                        Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
-                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml);
+                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
     return hipGetLastError();
 }
 
@@ -447,7 +454,7 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
                              const int32_t* idx, float scale, uint16_t* out, float* lse,
-                             void* workspace, hipStream_t stream) {
+                             void* workspace, CacheMap cmap, hipStream_t stream) {
     const int rows = B * S;
     int ns, sps;
     mla_plan(rows, K, &ns, &sps);
@@ -467,11 +474,11 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     hipError_t e = pipe ? launch_mla_kernel<true>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
                                                   nitems, hgroups, q, latent, lat_rs, lat_bs,
                                                   rope, rope_rs, rope_bs, idx, scale_log2, out,
-                                                  lse, ws_o, ws_ml)
+                                                  lse, ws_o, ws_ml, cmap)
                         : launch_mla_kernel<false>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
                                                    nitems, hgroups, q, latent, lat_rs, lat_bs,
                                                    rope, rope_rs, rope_bs, idx, scale_log2, out,
-                                                   lse, ws_o, ws_ml);
+                                                   lse, ws_o, ws_ml, cmap);
     if (e != hipSuccess) return e;
     if (ns > 1) {
         hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,

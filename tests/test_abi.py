@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = dsa.lib()
-    assert L.dsa_abi_version() == 1
+    assert L.dsa_abi_version() == 2
     for code in range(7):
         assert dsa.status_str(code).startswith("DSA_")
     assert dsa.status_str(99) == "unknown dsa_status"
@@ -193,3 +193,20 @@ def test_mla_append_validation():
             continue                 # valid arguments would launch: GPU tests cover them
         assert call(L.dsa_mla_append, a) == code, change
     assert L.dsa_mla_append(None, None) == 1
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(page_size=3), 2), (dict(page_size=0), 2), (dict(page_size=131072), 2),
+    (dict(num_pages=0), 2), (dict(max_pages=1), 2), (dict(num_pages=1 << 30), 2),
+    (dict(block_table=FAKE + 2), 5)])
+def test_paging_validation(fields, code):
+    """The paged-cache fields are checked the same way by every call that
+    takes them (here Lmax = 16384 or 1024, page_size 64 -> max_pages >= 256 / 16)."""
+    L = dsa.lib()
+    for make, fn in ((good_indexer, L.dsa_indexer), (good_mla, L.dsa_sparse_mla),
+                     (good_append, L.dsa_mla_append)):
+        a = make()
+        a.block_table, a.page_size, a.max_pages, a.num_pages = FAKE, 64, 256, 1000
+        for k, v in fields.items():
+            setattr(a, k, v)
+        assert call(fn, a) == code, (make.__name__, fields)
