@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated cache replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the paged-cache / Hadamard / cache-append measurements")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (T = 4096 causal queries, per-call TFLOP/s)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -245,6 +247,108 @@ def capture(fn):
     return g
 
 
+# --------------------------------------------------------- variants leg --
+
+def _graph_us(fn, reps):
+    """Average device time of fn() over graph replays of `reps` calls."""
+    import torch
+    g = capture(lambda: [fn(r) for r in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1000.0 / (3 * reps)
+
+
+def variants_leg(wl, st, page=64):
+    """The same decode step on paged caches (a random page permutation of a
+    page pool per replica), the indexer call with the Hadamard rotation and
+    power-of-two scales, and the MLA-side cache append."""
+    import torch
+
+    import sparse_attention_index_amd as dsa
+
+    dev = torch.device("cuda")
+    R, L = st["R"], wl.Lmax
+    B = wl.B
+    max_pages = (L + page - 1) // page
+    num_pages = B * max_pages
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(7)
+    table = torch.randperm(num_pages, generator=gen).to(torch.int32).reshape(B, max_pages)
+    paging = dsa.Paging(table.to(dev), page, num_pages)
+    flat = table.reshape(-1).long().to(dev)
+    pools = []
+    for rep in st["reps"]:
+        kc = torch.empty((num_pages, page, 128), dtype=torch.uint8, device=dev)
+        ks = torch.empty((num_pages, page), dtype=torch.float32, device=dev)
+        lr = torch.empty((num_pages, page, 576), dtype=torch.bfloat16, device=dev)
+        kc[flat] = rep["kc"].reshape(B * max_pages, page, 128)
+        ks[flat] = rep["ks"].reshape(B * max_pages, page)
+        lr[flat, :, :512] = rep["latent"].reshape(B * max_pages, page, 512)
+        lr[flat, :, 512:] = rep["kpe"].reshape(B * max_pages, page, 64)
+        pools.append((kc, ks, lr))
+    scores_p = torch.empty((B, wl.S, paging.lmax), dtype=torch.float32, device=dev)
+
+    def paged_step(r):
+        kc, ks, lr = pools[r % R]
+        dsa.indexer(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], kc, ks, scores_p,
+                    k_raw=st["k_new"], q_fp8=st["q8"], q_scale=st["qs"], paging=paging)
+        dsa.topk(scores_p, st["pos"], wl.K, idx=st["idx"], workspace=st["topk_ws"])
+        dsa.sparse_mla(st["q_mla"], lr[..., :512], lr[..., 512:], st["idx"], wl.softmax_scale,
+                       out=st["out"], workspace=st["mla_ws"], paging=paging)
+
+    paged_us = _graph_us(paged_step, R)
+
+    def dense_step(r):
+        for c in ("indexer", "topk", "sparse_mla"):
+            st["calls"][c](r)
+
+    chained_us = _graph_us(dense_step, R)
+
+    def had_idx(r):
+        rep = st["reps"][r % R]
+        dsa.indexer(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], rep["kc"], rep["ks"],
+                    st["scores"], k_raw=st["k_new"], q_fp8=st["q8"], q_scale=st["qs"],
+                    hadamard=True, pow2_scale=True)
+
+    had_us = _graph_us(had_idx, R)
+
+    lat_new = torch.randn((B, wl.S, 512), device=dev).to(torch.bfloat16)
+    kpe_new = torch.randn((B, wl.S, 64), device=dev).to(torch.bfloat16)
+    q_app = st["q_mla"].clone()
+
+    def append(r):
+        rep = st["reps"][r % R]
+        dsa.mla_append(lat_new, kpe_new, st["pos"], st["cos"], st["sin"], rep["latent"],
+                       rep["kpe"], q=q_app)
+
+    app_us = _graph_us(append, R)
+    for kc, ks, lr in pools:
+        del kc, ks, lr
+    return {
+        "chained_decode": {"us_per_step": round(chained_us, 2),
+                           "value": round(B * wl.S / (chained_us * 1e-6), 1),
+                           "unit": "queries/s",
+                           "note": "the same dense step, one graph holding one step per "
+                                   "replica back to back (no per-step graph launch)"},
+        "paged_decode": {"workload": f"{wl.name} on paged caches (page_size {page}, permuted "
+                                    f"pool of {num_pages} pages)",
+                         "value": round(B * wl.S / (paged_us * 1e-6), 1), "unit": "queries/s",
+                         "us_per_step": round(paged_us, 2),
+                         "note": "timed like chained_decode"},
+        "indexer_hadamard_pow2": {"avg_us": round(had_us, 2),
+                                  "note": "three launches (prepare k, prepare q, score)"},
+        "mla_append": {"avg_us": round(app_us, 2),
+                       "bytes": int(B * wl.S * (1024 * 2 + 128 * 2 + wl.Hq * 128 * 2)),
+                       "note": "latent row copy, rotary key and 128 query rope parts"},
+    }
+
+
 # ---------------------------------------------------------- prefill leg --
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -396,6 +500,7 @@ def main():
     torch.cuda.set_device(0)
     st = setup(wl, args.replica_bytes)
     calls = make_calls(wl, st)
+    st["calls"] = calls
     R = st["R"]
 
     def step(r):
@@ -475,6 +580,8 @@ def main():
                      "avg_launch_us": round(avg_us[dom], 3)},
         "source_hash": srch,
     }
+    if not args.no_variants:
+        rec["variants"] = variants_leg(wl, st)
     if not args.no_prefill:
         del st, calls, step_graphs, call_graphs
         torch.cuda.empty_cache()

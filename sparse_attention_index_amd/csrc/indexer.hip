@@ -11,6 +11,8 @@
 //   prepare_rows_kernel  one wave per 128-feature row: RoPE, cast, amax,
 //                        scale, E4M3 encode; q rows go to q_fp8/q_scale,
 //                        k rows are appended to k_cache/k_scale at pos.
+//   score_rows_kernel    few query rows per batch row: one block per (row,
+//                        key block), q codes of the row in registers.
 //   score_tile_kernel    many query rows: 64 queries x 128 keys per block,
 //                        per-head GEMM tiles on the bf16 MFMA with the key
 //                        codes held in registers across all heads.
@@ -167,6 +169,100 @@ hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_p
     }
 #undef DSA_PREP
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// score (few query rows per batch row): block = 4 waves, covers 64*U
+// consecutive keys of one query row. MFMA 16x16x32 bf16, M = 16 heads,
+// N = 16 keys, K = 32 features; four K-steps cover the 128 features and four
+// head groups cover 64 heads. Operand lane layout: lane (m = l%16, g = l/16)
+// supplies row m, feature chunk g; both operands use feature 32g + 8kk + j
+// for MFMA kk, element j. Result lane layout: lane (n = l%16, g) holds heads
+// 4g..4g+3 of key n.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void score_rows_kernel(
+    int S, int H, int Lmax, int P, const uint8_t* __restrict__ q8,
+    const float* __restrict__ qscale, const float* __restrict__ w,
+    const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
+    const float* __restrict__ kscale, float* __restrict__ scores, int64_t ld, CacheMap cmap) {
+    const int row = blockIdx.y;
+    const int p = pos[row];
+    if (p < 0 || p >= Lmax || p >= P) return;
+    const int n_valid = p + 1;
+    const int kblock0 = blockIdx.x * (64 * U);
+    if (kblock0 >= n_valid) return;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t b = row / S;
+    const int wkey0 = kblock0 + wave * 16 * U;
+
+    // key loads first; ks = -inf marks a key whose page is not present
+    uint4 kraw[U][2];
+    float ks[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int key = wkey0 + u * 16 + m;
+        key = key < n_valid ? key : n_valid - 1;
+        const int64_t krow = cmap.row(b, key);
+        const uint4* src =
+            reinterpret_cast<const uint4*>(kcache + (krow >= 0 ? krow : 0) * 128 + g * 32);
+        kraw[u][0] = src[0];
+        kraw[u][1] = src[1];
+        ks[u] = krow >= 0 ? kscale[krow] : -INFINITY;
+    }
+    bf16x8 qa[4][4];
+    float wq[4][4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+        const int h = hg * 16 + m;
+        if (h < H) {
+            const uint4* src = reinterpret_cast<const uint4*>(
+                q8 + (static_cast<int64_t>(row) * H + h) * 128 + g * 32);
+            const uint4 lo = src[0], hi = src[1];
+            qa[hg][0] = e4m3x8_to_bf16x8(lo.x, lo.y);
+            qa[hg][1] = e4m3x8_to_bf16x8(lo.z, lo.w);
+            qa[hg][2] = e4m3x8_to_bf16x8(hi.x, hi.y);
+            qa[hg][3] = e4m3x8_to_bf16x8(hi.z, hi.w);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qa[hg][kk][e] = static_cast<__bf16>(0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = hg * 16 + 4 * g + i;
+            wq[hg][i] = hh < H ? w[static_cast<int64_t>(row) * H + hh] *
+                                     qscale[static_cast<int64_t>(row) * H + hh]
+                               : 0.0f;
+        }
+    }
+    float* out = scores + static_cast<int64_t>(row) * ld;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int key0 = wkey0 + u * 16;
+        if (key0 >= n_valid) break;
+        bf16x8 kbf[4];
+        kbf[0] = e4m3x8_to_bf16x8(kraw[u][0].x, kraw[u][0].y);
+        kbf[1] = e4m3x8_to_bf16x8(kraw[u][0].z, kraw[u][0].w);
+        kbf[2] = e4m3x8_to_bf16x8(kraw[u][1].x, kraw[u][1].y);
+        kbf[3] = e4m3x8_to_bf16x8(kraw[u][1].z, kraw[u][1].w);
+        float part = 0.0f;
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += wq[hg][i] * fmaxf(acc[i], 0.0f);
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        const int key = key0 + m;
+        if (g == 0 && key < n_valid) out[key] = ks[u] == -INFINITY ? -INFINITY : part * ks[u];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -567,10 +663,30 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
     return hipGetLastError();
 }
 
+// Few queries per batch row (decode-like calls): one block per (row, 64*U
+// keys), U the largest that still gives enough blocks to fill the chip.
+// More: 64-query x 128-key tiles.
+constexpr int kRowsPathMaxS = 8;
+
 hipError_t launch_score(int B, int S, int H, int Lmax, int P, const uint8_t* q8,
                         const float* qscale, const float* w, const int32_t* pos,
                         const uint8_t* kcache, const float* kscale, float* scores, int64_t ld,
                         CacheMap cmap, hipStream_t stream) {
+    if (S <= kRowsPathMaxS) {
+        const int64_t rows = static_cast<int64_t>(B) * S;
+        int U = 4;
+        while (U > 1 && rows * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
+        const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)),
+                        static_cast<unsigned>(rows));
+#define DSA_ROWS(UU)                                                                           \
+    hipLaunchKernelGGL((score_rows_kernel<UU>), grid, dim3(256), 0, stream, S, H, Lmax, P, q8, \
+                       qscale, w, pos, kcache, kscale, scores, ld, cmap)
+        if (U == 4) DSA_ROWS(4);
+        else if (U == 2) DSA_ROWS(2);
+        else DSA_ROWS(1);
+#undef DSA_ROWS
+        return hipGetLastError();
+    }
     const int nqt = (S + kQT - 1) / kQT;
     const int nkt = (Lmax + kKT - 1) / kKT;
     const int64_t qtiles = static_cast<int64_t>(B) * nqt;

@@ -82,6 +82,8 @@ CASES = [
     ("one-key", 1, 1, 64, 17, [[0]], True, 102),
     ("tail", 2, 1, 64, 4133, [[4132], [2000]], True, 103),
     ("f32", 1, 3, 64, 700, [[699, 100, 1]], False, 104),
+    # more than eight queries per batch row: the 64-query x 128-key tile path
+    ("tiles", 2, 70, 64, 400, [list(range(330, 400)), list(range(0, 140, 2))], True, 105),
 ]
 
 
@@ -172,6 +174,7 @@ FLAG_CASES = [
     ("pow2-ragged", 2, 2, 64, 300, [[299, 10], [150, 0]], True, 113, False, True),
     ("had-pow2-tail", 2, 1, 64, 4133, [[4132], [2000]], True, 114, True, True),
     ("had-decode", 1, 1, 64, 2048, [[2047]], True, 115, True, False),
+    ("had-pow2-tiles", 1, 20, 64, 300, [list(range(280, 300))], True, 116, True, True),
 ]
 
 

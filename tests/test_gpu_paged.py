@@ -45,7 +45,7 @@ def scatter_pool(dense, table, page, num_pages):
     return pool
 
 
-@pytest.mark.parametrize("S,page", [(1, 64), (1, 16), (3, 128)])
+@pytest.mark.parametrize("S,page", [(1, 64), (1, 16), (3, 128), (20, 32)])
 def test_indexer_paged_matches_dense(S, page):
     import torch
     B, H, Lmax = 2, 64, 1000
@@ -54,7 +54,7 @@ def test_indexer_paged_matches_dense(S, page):
     q_raw = synth.bf16_bits_to_f32(synth.to_bf16_bits(g.standard_normal((B, S, H, 128), dtype=np.float32)))
     k_all = synth.bf16_bits_to_f32(synth.to_bf16_bits(g.standard_normal((B, Lmax, 128), dtype=np.float32)))
     w = (g.standard_normal((B, S, H), dtype=np.float32) * np.float32(64 ** -0.5 * 128 ** -0.5))
-    pos = np.array([[Lmax - 1 - 7 * s for s in range(S)], [500 + s for s in range(S)]], np.int32)
+    pos = np.array([[Lmax - 1 - 7 * s for s in range(S)], [480 + s for s in range(S)]], np.int32)
     cos, sin = oracle.rope_table(Lmax)
     dcos, dsin = dev(cos), dev(sin)
     table, num_pages = make_table(401, B, Lmax, page, hole=(1, 3))
