@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the paged-cache / Hadamard / cache-append measurements")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the prefill leg and print its JSON object (for profiling)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (T = 4096 causal queries, per-call TFLOP/s)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -495,6 +497,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only_prefill:
+        torch.cuda.set_device(0)
+        print(json.dumps(prefill_leg()), flush=True)
         return
     wl = synth.workload(args.workload)
     torch.cuda.set_device(0)
