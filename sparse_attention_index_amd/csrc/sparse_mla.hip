@@ -36,9 +36,11 @@
 // the LDS operand reads run several MFMAs ahead; with more blocks, two
 // blocks share a CU and hide each other's latencies instead.
 // With several splits per row the unnormalised partials (O, m, l) go to the
-// workspace, each wave's 16 x 512 block stored exactly as its registers
-// hold it (every store instruction writes 1 KiB of consecutive bytes), and
-// combine_kernel merges them with the log-sum-exp rule.
+// workspace, each wave's 16 x 512 block of O stored exactly as its registers
+// hold it, rounded to bf16 (every store instruction writes 512 consecutive
+// bytes; halving the partials' bytes shortens the call more than the extra
+// rounding, at most 2^-9 of the split's weighted |latent|, costs), and
+// combine_kernel merges them in float32 with the log-sum-exp rule.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
     const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ ws_o, float* __restrict__ ws_ml, CacheMap cmap) {
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml, CacheMap cmap) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);
     int* sidx = reinterpret_cast<int*>(Kt + kTile * kKtStride);
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     // 128 contiguous bytes per 8 lanes. Unselected slots read row 0 and are
     // zeroed (no divergent branches).
     const int gkey = tid >> 3, gsub = tid & 7;
-    uint4 G[9];
-    auto fetch_tile = [&](int t) {
+    uint4 GA[9];
+    auto fetch_tile = [&](int t, uint4 (&G)[9]) {
         const int p = sidx[t * kTile + gkey];
         const int pc = p >= 0 ? p : 0;
         const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
         for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
         G[8] = *reinterpret_cast<const uint4*>(rrow);
     };
-    auto store_tile = [&](int t) {
+    auto store_tile = [&](int t, uint4 (&G)[9]) {
         if (sidx[t * kTile + gkey] < 0) {
 #pragma unroll
             for (int i = 0; i < 9; ++i) G[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -179,14 +181,16 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     // LDS operand reads in flight ahead of their MFMAs
     constexpr int kPipe = PIPE ? 4 : 2;       // S: K-operand pairs
     constexpr int kPipeV = PIPE ? 6 : 3;      // O: V^T operands
-    if (PIPE && ntiles > 0) fetch_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
+    // PIPE: the gather of the next tile is in flight in registers while the
+    // current one is computed
+    if (PIPE && ntiles > 0) fetch_tile(0, GA);
+    auto tile_step = [&](int t, uint4 (&G)[9]) {
         __syncthreads();                           // previous tile fully consumed
-        if (!PIPE) fetch_tile(t);
-        store_tile(t);
+        if (!PIPE) fetch_tile(t, G);
+        store_tile(t, G);
         __syncthreads();
-        if (PIPE && t + 1 < ntiles) fetch_tile(t + 1);
-        if (!active) continue;
+        if (PIPE && t + 1 < ntiles) fetch_tile(t + 1, G);
+        if (!active) return;
 
         // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
         // Even and odd k-steps accumulate separately (four MFMA chains).
@@ -272,7 +276,8 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
                 DSA_SCHED_GROUP(kSchedDsRead, 2);
             }
         }
-    }
+    };
+    for (int t = 0; t < ntiles; ++t) tile_step(t, GA);
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
@@ -296,14 +301,18 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
             lse[static_cast<int64_t>(row) * Hq + h] =
                 l_tot > 0.0f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
     } else {
-        // partial block of (row, split, 16-head group): [t2][lane] float4
+        // partial block of (row, split, 16-head group): [t2][lane] 4 x bf16
         const int nwg = (Hq + 15) / 16;
         const int64_t blk = (static_cast<int64_t>(row) * nsplit + split) * nwg + wg;
-        float* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
+        uint16_t* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
 #pragma unroll
-        for (int t2 = 0; t2 < kT2; ++t2)
-            *reinterpret_cast<float4*>(wo + t2 * 256) =
-                make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][0])) |
+                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][1])) << 16);
+            const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][2])) |
+                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][3])) << 16);
+            *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
+        }
         if (g == 0 && h < Hq)
             *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
                 make_float4(m_run, l_tot, lr_tot, 0.0f);
@@ -327,13 +336,13 @@ __device__ __forceinline__ float wave_incl_sum_f(float v) {
 // 512 features), 256 threads: wave w covers feature tiles t2 = 8 quarter +
 // 2 w + {0, 1}; lane l = 16 g + m reads exactly what lane l of the producing
 // wave stored (head m, features 16 t2 + 4 g .. +3), so each partial load of
-// a wave is 1 KiB of consecutive bytes. Per head, wave w first turns the
+// a wave is 512 consecutive bytes. Per head, wave w first turns the
 // (m, l, lr) triples of all splits (one split per lane) into weights
 // 2^(m_s - M) in LDS and the totals L, Lr.
 constexpr int kCombineQuarters = 4;
 
 __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
-                                                      const float* __restrict__ ws_o,
+                                                      const uint16_t* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
@@ -368,14 +377,18 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
     const int m = lane & 15, g = lane >> 4;
     const int h = wg * 16 + m;
     const int t2a = quarter * (kT2 / kCombineQuarters) + 2 * wave;
-    const float* base = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + lane * 4;
+    const uint16_t* base = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + lane * 4;
     const int64_t sstride = static_cast<int64_t>(nwg) * kT2 * 64 * 4;
     float4 a0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a1 = a0;
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
         const float e = wgt[s][m];
-        const float4 v0 = *reinterpret_cast<const float4*>(base + s * sstride + t2a * 256);
-        const float4 v1 = *reinterpret_cast<const float4*>(base + s * sstride + (t2a + 1) * 256);
+        const uint2 u0 = *reinterpret_cast<const uint2*>(base + s * sstride + t2a * 256);
+        const uint2 u1 = *reinterpret_cast<const uint2*>(base + s * sstride + (t2a + 1) * 256);
+        const float4 v0 = make_float4(__uint_as_float(u0.x << 16), __uint_as_float(u0.x & 0xFFFF0000u),
+                                      __uint_as_float(u0.y << 16), __uint_as_float(u0.y & 0xFFFF0000u));
+        const float4 v1 = make_float4(__uint_as_float(u1.x << 16), __uint_as_float(u1.x & 0xFFFF0000u),
+                                      __uint_as_float(u1.y << 16), __uint_as_float(u1.y & 0xFFFF0000u));
         a0.x += e * v0.x;
         a0.y += e * v0.y;
         a0.z += e * v0.z;
@@ -428,7 +441,7 @@ size_t mla_workspace_bytes(int rows, int Hq, int K) {
     const size_t nwg = static_cast<size_t>((Hq + 15) / 16);
     const size_t blocks = static_cast<size_t>(rows) * ns * nwg;
     const size_t slots = static_cast<size_t>(rows) * ns * Hq;
-    return blocks * kT2 * 64 * 4 * sizeof(float) + slots * 4 * sizeof(float) + 256;
+    return blocks * kT2 * 64 * 4 * sizeof(uint16_t) + slots * 4 * sizeof(float) + 256;
 }
 
 template <bool PIPE>
@@ -437,7 +450,7 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
                                     const uint16_t* q, const uint16_t* latent, int64_t lat_rs,
                                     int64_t lat_bs, const uint16_t* rope, int64_t rope_rs,
                                     int64_t rope_bs, const int32_t* idx, float scale_log2,
-                                    uint16_t* out, float* lse, float* ws_o, float* ws_ml,
+                                    uint16_t* out, float* lse, uint16_t* ws_o, float* ws_ml,
                                     CacheMap cmap) {
     // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
     static const hipError_t attr = hipFuncSetAttribute(
@@ -458,12 +471,12 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     const int rows = B * S;
     int ns, sps;
     mla_plan(rows, K, &ns, &sps);
-    float* ws_o = nullptr;
+    uint16_t* ws_o = nullptr;
     float* ws_ml = nullptr;
     const int nwg = (Hq + 15) / 16;
     if (ns > 1) {
-        ws_o = static_cast<float*>(workspace);
-        ws_ml = ws_o + static_cast<size_t>(rows) * ns * nwg * kT2 * 64 * 4;
+        ws_o = static_cast<uint16_t*>(workspace);
+        ws_ml = reinterpret_cast<float*>(ws_o + static_cast<size_t>(rows) * ns * nwg * kT2 * 64 * 4);
     }
     const float scale_log2 = scale * 1.4426950408889634f;
     const int nitems = rows * ns;
