@@ -8,12 +8,14 @@ is decode at L = 16384 (B = 1), the configuration the headline metric is
 quoted on; --workload selects another one (batch32, decode128k).
 
 Inputs are resident in HBM before the timed region. Every step reads its
-caches from one of R replicas (R * footprint >= 1 GiB) so the 256 MiB
-Infinity Cache cannot serve them; scores/idx/out buffers are reused like a
-serving loop's workspace. HIP events on the launch stream bracket the timed
+caches from one of R replicas (R * footprint >= 1 GiB and R * bytes touched
+per step >= 1 GiB) so the 256 MiB Infinity Cache cannot serve them;
+scores/idx/out buffers are reused like a serving loop's workspace. HIP events on the launch stream bracket the timed
 region. Each call's device time is then measured the same way over a graph
 that runs that call once per replica, back to back; the call with the
-largest average is the "dominant kernel" of the roofline object.
+largest average is the "dominant kernel" of the roofline object. The
+batched decode (32 rows) and the long-context decode (4 rows at L = 131072)
+are measured the same way under "other_workloads".
 
 Prints ONE JSON line. `cpu_baseline` is the CPU oracle (oracle/) timed on
 the host's cores on a bounded sample of the same workload.
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=float(1 << 30),
                     help="minimum total bytes of rotated cache replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the batched and long-context decode workloads")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the paged-cache / Hadamard / cache-append measurements")
     ap.add_argument("--only-prefill", action="store_true",
@@ -67,7 +71,7 @@ def parse():
 # kernels launched by each call of the path (substrings of rocprofv3 kernel names)
 KERNELS_OF_CALL = {
     "indexer": ["decode_score_kernel"],
-    "topk": ["topk_kernel"],
+    "topk": ["topk_select_kernel"],
     "sparse_mla": ["sparse_mla_kernel", "combine_kernel"],
 }
 
@@ -200,7 +204,12 @@ def setup(wl, replica_bytes):
     q_mla = bf16(x["q_mla"])
     del k_all
     per_replica = kc.numel() + ks.numel() * 4 + latent.numel() * 2 + kpe.numel() * 2
-    R = max(2, int(np.ceil(replica_bytes / per_replica)))
+    # replicas: R * footprint >= replica_bytes, and also R * (bytes one step
+    # touches) >= replica_bytes, so that the rotation's touched set alone is
+    # several times the Infinity Cache
+    n_valid = [int(p) + 1 for p in pos_np.reshape(-1)]
+    touched = algorithmic_bytes(wl, n_valid, [min(wl.K, n) for n in n_valid])["step"]
+    R = max(2, int(np.ceil(replica_bytes / per_replica)), int(np.ceil(replica_bytes / touched)))
     reps = [dict(kc=kc, ks=ks, latent=latent, kpe=kpe)]
     for _ in range(R - 1):
         reps.append(dict(kc=kc.clone(), ks=ks.clone(), latent=latent.clone(), kpe=kpe.clone()))
@@ -247,6 +256,99 @@ def capture(fn):
     with torch.cuda.graph(g):
         fn()
     return g
+
+
+# ------------------------------------------------------------- timing --
+
+def measure(wl, st, steps, warmup):
+    """Time `steps` steps (one captured graph per replica, replayed in
+    rotation) and each call's average device time; returns the figures of
+    the bench record."""
+    import torch
+
+    calls = make_calls(wl, st)
+    st["calls"] = calls
+    R = st["R"]
+
+    def step(r):
+        for c in ("indexer", "topk", "sparse_mla"):
+            calls[c](r)
+
+    # eager warm-up (one-time kernel attribute set-up happens here), then one
+    # graph per replica for the step and one graph per call covering all
+    # replicas back to back
+    for r in range(min(R, 3)):
+        step(r)
+    torch.cuda.synchronize()
+    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    call_graphs = {c: capture(lambda c=c: [calls[c](r) for r in range(R)]) for c in calls}
+    for i in range(warmup):
+        step_graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step_graphs[i % R].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+
+    # per-call device time: each call graph runs the call once per replica
+    reps_call = max(1, (steps + R - 1) // R)
+    avg_us = {}
+    for c, g in call_graphs.items():
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps_call):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        avg_us[c] = a.elapsed_time(b) * 1000.0 / (reps_call * R)
+    del step_graphs, call_graphs
+
+    n_valid = [int(p) + 1 for p in st["x"]["pos"].reshape(-1)]
+    keff = [min(wl.K, n) for n in n_valid]
+    ab = algorithmic_bytes(wl, n_valid, keff)
+    dom = max(avg_us, key=avg_us.get)
+    ms_per_step = total_ms / steps
+    return dict(ab=ab, dom=dom, avg_us=avg_us, ms_per_step=ms_per_step,
+                achieved=ab[dom] / (avg_us[dom] * 1e-6) / 1e9,
+                value=wl.B * wl.S * steps / (total_ms / 1000.0),
+                step_hbm_frac=round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def other_workloads_leg(args):
+    """The same measurement on the batched decode (32 rows of ragged length
+    2048..16384) and the long-context decode (4 rows at L = 131072)."""
+    import torch
+
+    import synth
+
+    out = {}
+    for name in ("batch32", "decode128k"):
+        wl = synth.workload(name)
+        st = setup(wl, args.replica_bytes)
+        m = measure(wl, st, args.steps, args.warmup)
+        dom = m["dom"]
+        out[name] = {
+            "value": round(m["value"], 1), "unit": "queries/s",
+            "ms_per_step": round(m["ms_per_step"], 5),
+            "config": {"B": wl.B, "L": wl.Lmax, "topk": wl.K, "replicas": st["R"],
+                       "replica_bytes": st["per_replica"]},
+            "step_algorithmic_bytes": m["ab"]["step"],
+            "step_hbm_frac": m["step_hbm_frac"],
+            "call_avg_us": {k: round(v, 2) for k, v in m["avg_us"].items()},
+            "dominant": {"kernel": dom, "achieved_gbs": round(m["achieved"], 1),
+                         "frac": round(m["achieved"] / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": m["ab"][dom]},
+        }
+        del st, m
+        torch.cuda.empty_cache()
+    return out
 
 
 # --------------------------------------------------------- variants leg --
@@ -505,61 +607,15 @@ def main():
     wl = synth.workload(args.workload)
     torch.cuda.set_device(0)
     st = setup(wl, args.replica_bytes)
-    calls = make_calls(wl, st)
-    st["calls"] = calls
-    R = st["R"]
-
-    def step(r):
-        for c in ("indexer", "topk", "sparse_mla"):
-            calls[c](r)
-
-    # eager warm-up (one-time kernel attribute set-up happens here), then one
-    # graph per replica for the step and one graph per call covering all
-    # replicas back to back
-    for r in range(min(R, 3)):
-        step(r)
-    torch.cuda.synchronize()
-    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
-    call_graphs = {c: capture(lambda c=c: [calls[c](r) for r in range(R)]) for c in calls}
-    for i in range(args.warmup):
-        step_graphs[i % R].replay()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        step_graphs[i % R].replay()
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-
-    # per-call device time: each call graph runs the call once per replica
-    reps_call = max(1, (K + R - 1) // R)
-    avg_us = {}
-    for c, g in call_graphs.items():
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps_call):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        avg_us[c] = a.elapsed_time(b) * 1000.0 / (reps_call * R)
-
+    m = measure(wl, st, args.steps, args.warmup)
     x_host = st["x"]
-    n_valid = [int(p) + 1 for p in st["x"]["pos"].reshape(-1)]
-    keff = [min(wl.K, n) for n in n_valid]
-    ab = algorithmic_bytes(wl, n_valid, keff)
-    dom = max(avg_us, key=avg_us.get)
-    achieved = ab[dom] / (avg_us[dom] * 1e-6) / 1e9
+    K = args.steps
+    ab, dom, avg_us = m["ab"], m["dom"], m["avg_us"]
+    achieved = m["achieved"]
     srch = source_hash()
     traffic = load_traffic(dom, srch)
-    ms_per_step = total_ms / K
-    queries = wl.B * wl.S
-    value = queries * K / (total_ms / 1000.0)
+    ms_per_step = m["ms_per_step"]
+    value = m["value"]
 
     rec = {
         "metric": "decode queries/s (indexer+top-2048+sparse MLA) at L=16K; % HBM roofline",
@@ -578,7 +634,7 @@ def main():
                    "attn_heads": wl.Hq, "topk": wl.K, "replicas": st["R"],
                    "replica_bytes": st["per_replica"], "launch": "one HIP graph per step"},
         "step_algorithmic_bytes": ab["step"],
-        "step_hbm_frac": round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_hbm_frac": m["step_hbm_frac"],
         "call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -588,9 +644,11 @@ def main():
     }
     if not args.no_variants:
         rec["variants"] = variants_leg(wl, st)
+    del st, m
+    torch.cuda.empty_cache()
+    if not args.no_others:
+        rec["other_workloads"] = other_workloads_leg(args)
     if not args.no_prefill:
-        del st, calls, step_graphs, call_graphs
-        torch.cuda.empty_cache()
         rec["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, x_host, args.cpu_seconds)

@@ -209,12 +209,14 @@ dsa_status dsa_indexer(const dsa_indexer_args* args, hipStream_t stream);
  * Scores must be finite (NaN is not ordered).
  * Layouts: scores row r at scores + r*ld_scores (ld_scores >= Lmax),
  *   pos [B][S] int32, idx [B][S][K] int32, count [B][S] int32 (optional).
- * Limits: 1 <= K <= 2048, B, S, Lmax >= 1.
- * Workspace: dsa_topk_workspace() bytes (0 for short rows), 256-byte
- * aligned. It carries per-row histograms and counters between the call's
- * launches and MUST be zero-filled before its first use; every call leaves
- * it zero-filled again, so a workspace can be reused across calls on one
- * stream without clearing. Calls that overlap in time need their own.
+ * Limits: 1 <= K <= 2048, B, S >= 1, 1 <= Lmax <= 2^21, and
+ *   B*S*ceil(Lmax/16384) < 2^31.
+ * Workspace: dsa_topk_workspace() bytes (0 when Lmax <= 16384), 256-byte
+ * aligned. Rows longer than 16,384 are selected in levels (the top k of each
+ * 16,384-score chunk, then of merged groups of those lists); the workspace
+ * carries the intermediate candidate lists between the call's launches. Its
+ * contents on entry do not matter and are left undefined. Calls that
+ * overlap in time need their own.
  * ---------------------------------------------------------------------- */
 typedef struct dsa_topk_args {
     int32_t B, S, Lmax, K;

@@ -310,18 +310,18 @@ def topk_workspace_bytes(args: TopkArgs) -> int:
 
 
 def topk_workspace(scores, pos, K: int):
-    """A zero-filled workspace for topk() on these shapes (reusable across
-    calls on one stream: every call leaves it zero-filled)."""
+    """A workspace for topk() on these shapes (reusable across calls on one
+    stream; its contents between calls do not matter)."""
     import torch
     B, S = pos.shape
     idx = torch.empty((B, S, K), dtype=torch.int32, device=scores.device)
     n = topk_workspace_bytes(topk_args(scores, pos, K, idx))
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=scores.device)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=scores.device)
 
 
 def topk(scores, pos, K: int, idx=None, count=None, workspace=None):
     """Call 2: causal top-K of every score row; returns idx [B, S, K] int32.
-    `workspace` must come from topk_workspace() (zero-filled) when given."""
+    `workspace` (from topk_workspace()) is allocated per call when omitted."""
     import torch
     B, S = pos.shape
     if idx is None:
@@ -329,7 +329,7 @@ def topk(scores, pos, K: int, idx=None, count=None, workspace=None):
     a = topk_args(scores, pos, K, idx, count, workspace)
     need = topk_workspace_bytes(a)
     if need and (workspace is None or workspace.numel() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(lib().dsa_topk(ctypes.byref(a), _stream()))
     return idx

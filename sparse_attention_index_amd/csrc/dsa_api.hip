@@ -29,7 +29,8 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
                        const int32_t* pos, int32_t* idx, int32_t* count, void* workspace,
                        hipStream_t stream);
-size_t topk_workspace_bytes(int rows, int Lmax);
+size_t topk_workspace_bytes(int rows, int Lmax, int K);
+int64_t topk_max_blocks(int rows, int Lmax);
 size_t mla_workspace_bytes(int rows, int Hq, int K);
 hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
@@ -131,6 +132,7 @@ dsa_status check_topk(const dsa_topk_args* a) {
     if (static_cast<int64_t>(a->B) * a->S > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
     if (a->ld_scores < a->Lmax) return DSA_ERR_SHAPE;
     if (a->Lmax > (1 << 21)) return DSA_ERR_SHAPE;
+    if (dsa::topk_max_blocks(a->B * a->S, a->Lmax) > (int64_t(1) << 31) - 1) return DSA_ERR_SHAPE;
     if (!a->scores || !a->pos || !a->idx) return DSA_ERR_NULL;
     if (!aligned4(a->scores) || !aligned4(a->pos) || !aligned4(a->idx) ||
         (a->count && !aligned4(a->count)))
@@ -285,14 +287,14 @@ dsa_status dsa_topk_workspace(const dsa_topk_args* a, size_t* bytes) {
     if (bytes == nullptr) return DSA_ERR_NULL;
     const dsa_status st = check_topk(a);
     if (st != DSA_OK) return st;
-    *bytes = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax);
+    *bytes = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax, a->K);
     return DSA_OK;
 }
 
 dsa_status dsa_topk(const dsa_topk_args* a, hipStream_t stream) {
     const dsa_status st = check_topk(a);
     if (st != DSA_OK) return st;
-    const size_t need = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax);
+    const size_t need = dsa::topk_workspace_bytes(a->B * a->S, a->Lmax, a->K);
     if (need > 0) {
         if (a->workspace == nullptr || a->workspace_bytes < need) return DSA_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return DSA_ERR_ALIGN;

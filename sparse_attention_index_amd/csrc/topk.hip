@@ -7,26 +7,38 @@
 // k_eff = min(K, n_valid) of them under (score desc, position asc), written
 // in ascending position order and padded with -1.
 //
-// Rows of up to 16,384 scores: one block per row, the row held in
-// registers (16 scores per thread; wave w owns the contiguous run
-// [1024 w, 1024 w + 1024), lane l item j at 1024 w + 64 j + l).
-//  1. Load (adding +0.0 folds -0.0 into +0.0) and the row's min/max.
+// The selection block: up to 16,384 items held in registers (16 per thread;
+// wave w owns the contiguous run [1024 w, 1024 w + 1024), lane l item j at
+// 1024 w + 64 j + l), of which the valid ones are ranked; it keeps
+// k = min(K, valid count) of them.
+//  1. Load (adding +0.0 folds -0.0 into +0.0) and the min/max of the valid
+//     items.
 //  2. Bucket pass: bucket(v) = floor((v - min) * 2048 / (max - min)), a
 //     monotone non-decreasing map, so every score in a higher bucket is
 //     larger than every score in a lower one. An LDS histogram, scanned by
-//     one wave with DPP prefix sums, gives the bucket b* holding the
-//     k_eff-th largest score and the count G above it.
-//  3. Threshold key T (the k_eff-th largest order key, counted with
+//     one wave with DPP prefix sums, gives the bucket b* holding the k-th
+//     largest score and the count G above it.
+//  3. Threshold key T (the k-th largest order key, counted with
 //     multiplicity): when b* holds at most 64 scores one wave ranks them;
 //     otherwise an exact three-pass radix select (11/11/10-bit digits of the
-//     order key) runs over the scores of b*. Rows whose min/max give no
-//     usable bucket map (all equal, infinities) run it over the whole row.
+//     order key) runs over the scores of b*. Blocks whose min/max give no
+//     usable bucket map (all equal, infinities) run it over all items.
 //     Every key above T is taken, and of the keys equal to T the ones with
-//     the lowest positions, as many as k_eff leaves.
+//     the lowest item indices, as many as k leaves.
 //  4. Ordered compaction: per-wave counts of keys above / equal to T (taken
 //     during step 3 when one wave ranked b*, else by a ballot pass) give each
-//     wave its output start, and each wave writes its taken positions in
-//     order. Ascending output falls out of the position order of the runs.
+//     wave its output start, and each wave writes its taken items in item
+//     order.
+//
+// Rows of up to 16,384 scores: one selection block per row over the row
+// itself. Longer rows: a tournament. Level 0 splits the row into chunks of
+// 16,384 scores and keeps each chunk's top k as a candidate list (score,
+// position) in ascending position order; each further level merges groups of
+// consecutive lists (16,384 items per block) into one list, and the last
+// level writes the row's indices. A key of the row's top k is in the top k
+// of every subset that holds it (fewer keys of the subset beat it), so no
+// level drops it. Item order equals position order at every level, so the
+// tie rule (lower position first) and the ascending output carry through.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -34,7 +46,7 @@ namespace dsa {
 constexpr int kRegItems = 16;                           // scores per thread
 constexpr int kRegMaxThreads = 1024;
 constexpr int kRegMaxWaves = kRegMaxThreads / kWave;
-constexpr int kLdsKeys = kRegItems * kRegMaxThreads;    // longest row of the one-block path
+constexpr int kBlockItems = kRegItems * kRegMaxThreads; // items of one selection block
 constexpr int kBuckets = 2048;
 constexpr int kRankCap = kWave;                         // bucket sizes ranked by one wave
 
@@ -44,6 +56,7 @@ struct alignas(16) RegShared {
     int cand_wave[kRankCap];
     int wa[kRegMaxWaves];                   // per wave: keys above T
     int wb[kRegMaxWaves];                   // per wave: keys equal to T
+    int wn[kRegMaxWaves];                   // per wave: valid items
     float wmin[kRegMaxWaves];
     float wmax[kRegMaxWaves];
     uint32_t digit;
@@ -100,62 +113,134 @@ __device__ __forceinline__ int bucket_of(float v, float vmin, float scale) {
     return b < kBuckets - 1 ? b : kBuckets - 1;
 }
 
-// blockDim.x: a power of two from 64 to 1024 with 16 * blockDim.x >= Lmax.
-// speculative: issue the score loads of the whole row before pos[row] is
-// known (lower latency for a few rows; rows that turn out to keep all their
-// keys waste the loads, so many-row launches pass false).
-__global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
-    int Lmax, int K, int speculative, const float* __restrict__ scores, int64_t ld,
-    const int32_t* __restrict__ pos, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+// Arguments of one selection launch. Block x covers part x % nparts of row
+// x / nparts: a chunk of blockDim.x * 16 scores of the row (score source) or
+// a group of consecutive candidate lists (candidate source).
+struct SelectArgs {
+    int Lmax, K;
+    int nparts;                 // blocks per row
+    int speculative;            // score source: load before pos[row] is known
+    int kp_shift;               // candidate list stride Kp = 2^kp_shift >= K
+    // score source
+    const float* scores;
+    int64_t ld;
+    const int32_t* pos;
+    // candidate source: row r's list s at ((r * in_lists + s) << kp_shift)
+    const float* in_key;
+    const int32_t* in_pos;
+    const int32_t* in_cnt;      // [rows][in_lists]
+    int in_lists;
+    // index output
+    int32_t* idx;
+    int32_t* count;
+    // candidate output: list (row, part), nparts lists per row
+    float* out_key;
+    int32_t* out_pos;
+    int32_t* out_cnt;
+};
+
+// blockDim.x: a power of two from 64 to 1024; with the score source the row
+// chunk of part x starts at x * blockDim.x * 16 and 16 * blockDim.x >= Lmax
+// when nparts == 1.
+template <bool CAND_IN, bool CAND_OUT>
+__global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs a) {
     __shared__ RegShared sh;
-    const int row = blockIdx.x;
+    const int row = static_cast<int>(blockIdx.x) / a.nparts;
+    const int part = static_cast<int>(blockIdx.x) - row * a.nparts;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = static_cast<int>(blockDim.x) >> 6;
+    const int nitems = static_cast<int>(blockDim.x) * kRegItems;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const float* srow = scores + static_cast<int64_t>(row) * ld;
     const int base = wave * (kWave * kRegItems) + lane;
+    const int kps = a.kp_shift;
+    const int K = a.K;
 
-    // 1. load the scores (speculatively: every in-row score, before pos is
-    // known; scores past the causal end are masked below), min/max of the
-    // causal ones
+    // 1. load the items
     float v[kRegItems];
-    if (speculative) {
+    uint32_t vmask = 0u;                     // candidate source: bit j = item j is valid
+    int M = 0;                               // valid items of the block
+    int start = 0;                           // score source: chunk start in the row
+    int64_t cbase = 0;                       // candidate source: first item of the group
+    if constexpr (!CAND_IN) {
+        start = part * nitems;
+        const float* src = a.scores + static_cast<int64_t>(row) * a.ld + start;
+        const int lim = min(a.Lmax - start, nitems);
+        if (a.speculative) {
+#pragma unroll
+            for (int j = 0; j < kRegItems; ++j) {
+                const int i = base + kWave * j;
+                v[j] = i < lim ? src[i] : 0.0f;
+            }
+        }
+        const int p = a.pos[row];
+        const int n = (p >= 0 && p < a.Lmax) ? p + 1 : 0;
+        M = min(max(n - start, 0), nitems);
+        const int keff0 = M < K ? M : K;
+        if (keff0 == M) {                    // every valid item is selected
+            if constexpr (CAND_OUT) {
+                const int64_t ob = (static_cast<int64_t>(row) * a.nparts + part) << kps;
+                for (int i = tid; i < M; i += blockDim.x) {
+                    a.out_key[ob + i] = src[i] + 0.0f;
+                    a.out_pos[ob + i] = start + i;
+                }
+                if (tid == 0) a.out_cnt[static_cast<int64_t>(row) * a.nparts + part] = M;
+            } else {
+                int32_t* out = a.idx + static_cast<int64_t>(row) * K;
+                for (int i = tid; i < K; i += blockDim.x) out[i] = i < M ? i : -1;
+                if (a.count != nullptr && tid == 0) a.count[row] = M;
+            }
+            return;
+        }
+        if (!a.speculative) {
+#pragma unroll
+            for (int j = 0; j < kRegItems; ++j) {
+                const int i = base + kWave * j;
+                v[j] = i < M ? src[i] : 0.0f;
+            }
+        }
+    } else {
+        const int kpm = (1 << kps) - 1;
+        const int slot0 = part * (nitems >> kps);
+        const int nsl = min(nitems >> kps, a.in_lists - slot0);   // lists in the group
+        cbase = (static_cast<int64_t>(row) * a.in_lists + slot0) << kps;
+        const int32_t* cnt = a.in_cnt + static_cast<int64_t>(row) * a.in_lists + slot0;
 #pragma unroll
         for (int j = 0; j < kRegItems; ++j) {
             const int i = base + kWave * j;
-            v[j] = i < Lmax ? srow[i] : 0.0f;
+            const int s = i >> kps;
+            v[j] = 0.0f;
+            if (s < nsl) {
+                v[j] = a.in_key[cbase + i];
+                vmask |= (i & kpm) < cnt[s] ? (1u << j) : 0u;
+            }
         }
     }
-    const int p = pos[row];
-    const int n = (p >= 0 && p < Lmax) ? p + 1 : 0;
-    const int keff = n < K ? n : K;
-    int32_t* out = idx + static_cast<int64_t>(row) * K;
-    if (count != nullptr && tid == 0) count[row] = keff;
-    if (keff == n) {                        // everything causal is selected
-        for (int i = tid; i < K; i += blockDim.x) out[i] = i < n ? i : -1;
-        return;
-    }
-    if (!speculative) {
-#pragma unroll
-        for (int j = 0; j < kRegItems; ++j) {
-            const int i = base + kWave * j;
-            v[j] = i < n ? srow[i] : 0.0f;
-        }
-    }
+    // item j of this thread is valid: a prefix of the chunk (score source,
+    // one compare against M) or the per-list counts (candidate source)
+    auto valid = [&](int j) -> bool {
+        if constexpr (CAND_IN) return (vmask >> j) & 1u;
+        else return base + kWave * j < M;
+    };
     float vmin = INFINITY, vmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kRegItems; ++j) {
         v[j] = v[j] + 0.0f;
-        if (base + kWave * j < n) {
+        if (valid(j)) {
             vmin = fminf(vmin, v[j]);
             vmax = fmaxf(vmax, v[j]);
         }
     }
     vmin = wave_min_dpp(vmin);
     vmax = wave_max_dpp(vmax);
+    int wn = 0;
+    if constexpr (CAND_IN) {
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) wn += __popcll(__ballot(valid(j)));
+    }
     if (lane == 0) {
         sh.wmin[wave] = vmin;
         sh.wmax[wave] = vmax;
+        sh.wn[wave] = wn;
         sh.wa[wave] = 0;
         sh.wb[wave] = 0;
     }
@@ -164,15 +249,21 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
     __syncthreads();
     vmin = sh.wmin[0];
     vmax = sh.wmax[0];
+    if constexpr (CAND_IN) M = sh.wn[0];
     for (int w = 1; w < nw; ++w) {
         vmin = fminf(vmin, sh.wmin[w]);
         vmax = fmaxf(vmax, sh.wmax[w]);
+        if constexpr (CAND_IN) M += sh.wn[w];
     }
+    const int keff = M < K ? M : K;
 
     uint32_t T;                             // threshold order key
     int eq_take;                            // keys equal to T that are taken
     bool counted = false;                   // sh.wa / sh.wb already hold the per-wave counts
-    if (!(vmax > vmin)) {                   // all causal scores equal
+    if (keff == M) {                        // every valid item is selected (keys >= 0)
+        T = 0u;
+        eq_take = M;
+    } else if (!(vmax > vmin)) {            // all valid scores equal
         T = float_order_key(vmax);
         eq_take = keff;
     } else {
@@ -182,11 +273,11 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
         int want = keff;
         int bstar = -1;
         if (bucketed) {
-            // 2. bucket histogram, threshold bucket (-1: not causal)
+            // 2. bucket histogram, threshold bucket (-1: not valid)
             int bk[kRegItems];
 #pragma unroll
             for (int j = 0; j < kRegItems; ++j) {
-                bk[j] = base + kWave * j < n ? bucket_of(v[j], vmin, scale) : -1;
+                bk[j] = valid(j) ? bucket_of(v[j], vmin, scale) : -1;
                 if (bk[j] >= 0) atomicAdd(&sh.hist[bk[j]], 1u);
             }
             __syncthreads();
@@ -247,11 +338,11 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
             }
         }
         if (!counted) {
-            // 3b. radix select over the scores of b* (or of the whole row)
+            // 3b. radix select over the scores of b* (or over all valid items)
             uint32_t memb = 0u;
 #pragma unroll
             for (int j = 0; j < kRegItems; ++j) {
-                const bool in = base + kWave * j < n &&
+                const bool in = valid(j) &&
                                 (bstar < 0 || bucket_of(v[j], vmin, scale) == bstar);
                 memb |= in ? (1u << j) : 0u;
             }
@@ -289,7 +380,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
         int gtw = 0, eqw = 0;
 #pragma unroll
         for (int j = 0; j < kRegItems; ++j) {
-            const bool ok = base + kWave * j < n;
+            const bool ok = valid(j);
             const uint32_t uk = float_order_key(v[j]);
             gtw += __popcll(__ballot(ok && uk > T));
             eqw += __popcll(__ballot(ok && uk == T));
@@ -307,10 +398,14 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
     }
     int o = gp + (ep < eq_take ? ep : eq_take);
     int e = ep;
+    int32_t* out = nullptr;
+    int64_t ob = 0;
+    if constexpr (CAND_OUT) ob = (static_cast<int64_t>(row) * a.nparts + part) << kps;
+    else out = a.idx + static_cast<int64_t>(row) * K;
 #pragma unroll
     for (int j = 0; j < kRegItems; ++j) {
         const int i = base + kWave * j;
-        const bool ok = i < n;
+        const bool ok = valid(j);
         const uint32_t uk = float_order_key(v[j]);
         const bool eq = ok && uk == T;
         const uint64_t eqm = __ballot(eq);
@@ -318,382 +413,132 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_kernel(
         e += __popcll(eqm);
         const uint64_t tm = __ballot(take);
         const int slot = o + __popcll(tm & lt_mask);
-        if (take && slot < K) out[slot] = i;
+        if (take && slot < keff) {
+            int32_t p;
+            if constexpr (CAND_IN) p = a.in_pos[cbase + i];
+            else p = start + i;
+            if constexpr (CAND_OUT) {
+                a.out_key[ob + slot] = v[j];
+                a.out_pos[ob + slot] = p;
+            } else {
+                out[slot] = p;
+            }
+        }
         o += __popcll(tm);
     }
-    for (int i = keff + tid; i < K; i += blockDim.x) out[i] = -1;
+    if constexpr (CAND_OUT) {
+        if (tid == 0) a.out_cnt[static_cast<int64_t>(row) * a.nparts + part] = keff;
+    } else {
+        for (int i = keff + tid; i < K; i += blockDim.x) out[i] = -1;
+        if (a.count != nullptr && tid == 0) a.count[row] = keff;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Multi-block path for long rows: chunks of kChunk scores, one 256-thread
-// block per (chunk, row), three launches:
-//   T1  per-chunk LDS histogram of the top 11 bits of the order key, added to
-//       the row's global histogram; the last chunk to finish (atomic counter
-//       after a fence) finds the bucket b* holding the k_eff-th largest key
-//       and the count above it.
-//   T2  per chunk: count of keys in buckets above b*; keys of bucket b* are
-//       appended (key, position) to the row's candidate list. The last chunk
-//       selects exactly among the candidates (radix select; a whole-row radix
-//       select when the list overflowed), derives for every chunk how many
-//       of its keys are taken and where its output run starts, and clears the
-//       row's histogram and counters for the next call.
-//   T3  per chunk: ordered compaction of its taken positions into idx.
-// Workspace per row (zero on the first call, left zero by every call):
-//   hist[2048] | state[8] | per-chunk gt/eq/off/eqb | candidates[kCandRow] x2
+// Tournament plan for rows longer than one selection block. Candidate lists
+// have stride Kp = K rounded up to a power of two; a merge block takes
+// 16,384 / Kp consecutive lists. Buffer A holds the level-0 lists (one per
+// 16,384-score chunk), buffer B the level-1 lists; later levels alternate.
+// Each buffer: keys [rows][lists][Kp] f32 | positions (same) i32 |
+// counts [rows][lists] i32, each part 256-byte aligned. No initial contents
+// are needed: every list a launch reads was written by the previous one.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 2048;
-constexpr int kMbThreads = 256;
-constexpr int kMbPer = kChunk / kMbThreads;     // 8 scores per thread
-constexpr int kCandRow = 8192;                  // candidate list capacity per row
-constexpr int kMbMinLmax = kLdsKeys + 1;       // rows longer than the LDS row cache
-constexpr int kCandLds = 4096;                  // candidates staged in LDS by the last chunk
-constexpr int kMaxChunks = 1024;                // chunks per row (rows up to 2M keys)
-
-struct MbLayout {
-    int nch;                 // chunks per row (Lmax / kChunk rounded up)
-    size_t row_bytes;        // bytes per row
-    size_t off_state, off_gt, off_eq, off_off, off_eqb, off_ckey, off_cpos;
+struct TourPlan {
+    int kp_shift, group, lists0, lists1;
+    size_t a_key, a_pos, a_cnt, b_key, b_pos, b_cnt, bytes;
 };
 
-__host__ __device__ inline MbLayout mb_layout(int Lmax) {
-    MbLayout L;
-    L.nch = (Lmax + kChunk - 1) / kChunk;
-    size_t o = 2048 * 4;
-    L.off_state = o; o += 8 * 4;
-    L.off_gt = o; o += static_cast<size_t>(L.nch) * 4;
-    L.off_eq = o; o += static_cast<size_t>(L.nch) * 4;
-    L.off_off = o; o += static_cast<size_t>(L.nch) * 4;
-    L.off_eqb = o; o += static_cast<size_t>(L.nch) * 4;
-    o = (o + 15) & ~static_cast<size_t>(15);
-    L.off_ckey = o; o += static_cast<size_t>(kCandRow) * 4;
-    L.off_cpos = o; o += static_cast<size_t>(kCandRow) * 4;
-    L.row_bytes = (o + 255) & ~static_cast<size_t>(255);
-    return L;
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static TourPlan tour_plan(int rows, int Lmax, int K) {
+    TourPlan t;
+    t.kp_shift = 0;
+    while ((1 << t.kp_shift) < K) ++t.kp_shift;
+    t.group = kBlockItems >> t.kp_shift;
+    t.lists0 = (Lmax + kBlockItems - 1) / kBlockItems;
+    t.lists1 = t.lists0 > t.group ? (t.lists0 + t.group - 1) / t.group : 0;
+    const size_t r = static_cast<size_t>(rows);
+    const size_t kp = static_cast<size_t>(1) << t.kp_shift;
+    size_t o = 0;
+    t.a_key = o; o += align256(r * t.lists0 * kp * 4);
+    t.a_pos = o; o += align256(r * t.lists0 * kp * 4);
+    t.a_cnt = o; o += align256(r * t.lists0 * 4);
+    t.b_key = o; o += align256(r * t.lists1 * kp * 4);
+    t.b_pos = o; o += align256(r * t.lists1 * kp * 4);
+    t.b_cnt = o; o += align256(r * t.lists1 * 4);
+    t.bytes = o;
+    return t;
 }
 
-enum { ST_DONE1 = 0, ST_DONE2, ST_NCAND, ST_BSTAR, ST_ABOVE, ST_T, ST_REM };
-
-struct MbRow {
-    uint32_t* hist; int* st; int* gt; int* eq; int* off; int* eqb; uint32_t* ckey; int* cpos;
-};
-
-__device__ __forceinline__ MbRow mb_row(unsigned char* ws, const MbLayout& L, int row) {
-    unsigned char* base = ws + static_cast<size_t>(row) * L.row_bytes;
-    MbRow R;
-    R.hist = reinterpret_cast<uint32_t*>(base);
-    R.st = reinterpret_cast<int*>(base + L.off_state);
-    R.gt = reinterpret_cast<int*>(base + L.off_gt);
-    R.eq = reinterpret_cast<int*>(base + L.off_eq);
-    R.off = reinterpret_cast<int*>(base + L.off_off);
-    R.eqb = reinterpret_cast<int*>(base + L.off_eqb);
-    R.ckey = reinterpret_cast<uint32_t*>(base + L.off_ckey);
-    R.cpos = reinterpret_cast<int*>(base + L.off_cpos);
-    return R;
+size_t topk_workspace_bytes(int rows, int Lmax, int K) {
+    if (Lmax <= kBlockItems) return 0;
+    return tour_plan(rows, Lmax, K).bytes;
 }
 
-// exclusive scan across a 256-thread block; `ws` holds 4 ints
-__device__ __forceinline__ int block256_scan(int v, int* ws, int& total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) ws[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        before += i < wave ? ws[i] : 0;
-        total += ws[i];
-    }
-    __syncthreads();
-    return before + incl - v;
-}
-
-__device__ __forceinline__ int row_nvalid(const int32_t* pos, int row, int Lmax) {
-    const int p = pos[row];
-    return (p >= 0 && p < Lmax) ? p + 1 : 0;
-}
-
-// Bucket b and count above it from a 2048-bin histogram (descending scan),
-// for the want-th largest (1 <= want <= total count).
-__device__ void find_bucket(const uint32_t* hist, int want, int* ws, int* s_b, int* s_above) {
-    const int tid = threadIdx.x;
-    int c[8];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {             // thread t owns digits 2047-8t-j
-        c[j] = static_cast<int>(hist[2047 - 8 * tid - j]);
-        sum += c[j];
-    }
-    int tot;
-    int above = block256_scan(sum, ws, tot);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (above < want && above + c[j] >= want) {
-            *s_b = 2047 - 8 * tid - j;
-            *s_above = above;
-        }
-        above += c[j];
-    }
-    __syncthreads();
-}
-
-__global__ __launch_bounds__(kMbThreads) void topk_mb_hist(int Lmax, int K,
-                                                           const float* __restrict__ scores,
-                                                           int64_t ld, const int32_t* __restrict__ pos,
-                                                           unsigned char* __restrict__ ws) {
-    __shared__ uint32_t lh[2048];
-    __shared__ int wsc[4];
-    __shared__ int s_last, s_b, s_above;
-    const int row = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-    const int n = row_nvalid(pos, row, Lmax);
-    const int keff = n < K ? n : K;
-    if (keff == n || ch * kChunk >= n) return;
-    const MbLayout L = mb_layout(Lmax);
-    const MbRow R = mb_row(ws, L, row);
-    const int nch = (n + kChunk - 1) / kChunk;
-    for (int i = tid; i < 2048; i += kMbThreads) lh[i] = 0u;
-    __syncthreads();
-    const float* src = scores + static_cast<int64_t>(row) * ld + ch * kChunk;
-    const int lim = min(kChunk, n - ch * kChunk);
-#pragma unroll
-    for (int j = 0; j < kMbPer; ++j) {
-        const int i = tid + j * kMbThreads;
-        if (i < lim) atomicAdd(&lh[float_order_key(src[i]) >> 21], 1u);
-    }
-    __syncthreads();
-    for (int i = tid; i < 2048; i += kMbThreads)
-        if (lh[i]) atomicAdd(&R.hist[i], lh[i]);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&R.st[ST_DONE1], 1) == nch - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    find_bucket(R.hist, keff, wsc, &s_b, &s_above);
-    if (tid == 0) {
-        R.st[ST_BSTAR] = s_b;
-        R.st[ST_ABOVE] = s_above;
-    }
-}
-
-__global__ __launch_bounds__(kMbThreads) void topk_mb_cand(int Lmax, int K,
-                                                           const float* __restrict__ scores,
-                                                           int64_t ld, const int32_t* __restrict__ pos,
-                                                           unsigned char* __restrict__ ws) {
-    __shared__ int wsc[4];
-    __shared__ int s_last;
-    __shared__ uint32_t hist[2048];
-    __shared__ int s_b, s_above;
-    __shared__ uint32_t ckey_l[kCandLds];
-    __shared__ uint8_t cch_l[kCandLds];
-    const int row = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int n = row_nvalid(pos, row, Lmax);
-    const int keff = n < K ? n : K;
-    if (keff == n || ch * kChunk >= n) return;
-    const MbLayout L = mb_layout(Lmax);
-    const MbRow R = mb_row(ws, L, row);
-    const int nch = (n + kChunk - 1) / kChunk;
-    const uint32_t bstar = static_cast<uint32_t>(R.st[ST_BSTAR]);
-    const float* srow = scores + static_cast<int64_t>(row) * ld;
-    const float* src = srow + ch * kChunk;
-    const int lim = min(kChunk, n - ch * kChunk);
-    int gt = 0;
-#pragma unroll
-    for (int j = 0; j < kMbPer; ++j) {
-        const int i = tid + j * kMbThreads;
-        const uint32_t u = i < lim ? float_order_key(src[i]) : 0u;
-        const uint32_t d = u >> 21;
-        gt += (i < lim && d > bstar) ? 1 : 0;
-        const bool c = i < lim && d == bstar;
-        const uint64_t m = __ballot(c);
-        int base = 0;
-        if (lane == 0 && m) base = atomicAdd(&R.st[ST_NCAND], __popcll(m));
-        base = __shfl(base, 0);
-        const int slot = base + __popcll(m & lt_mask);
-        if (c && slot < kCandRow) {
-            R.ckey[slot] = u;
-            R.cpos[slot] = ch * kChunk + i;
-        }
-    }
-    int tot;
-    block256_scan(gt, wsc, tot);
-    if (tid == 0) R.gt[ch] = tot;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&R.st[ST_DONE2], 1) == nch - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // ---- last chunk of the row: exact threshold among the candidates ----
-    const int ncand = R.st[ST_NCAND];
-    const int rem = keff - R.st[ST_ABOVE];
-    uint32_t prefix = 0, mask = 0;
-    int remaining = rem;
-    const bool from_list = ncand <= kCandRow;
-    const int nsrc = from_list ? ncand : n;
-    if (!from_list) remaining = keff;              // overflow: whole-row select
-    const bool in_lds = from_list && ncand <= kCandLds;
-    if (in_lds)
-        for (int i = tid; i < ncand; i += kMbThreads) {
-            ckey_l[i] = R.ckey[i];
-            cch_l[i] = static_cast<uint8_t>(R.cpos[i] / kChunk);
-        }
-    auto getk = [&](int i) -> uint32_t {
-        return in_lds ? ckey_l[i] : (from_list ? R.ckey[i] : float_order_key(srow[i]));
-    };
-    auto getc = [&](int i) -> int {
-        return in_lds ? static_cast<int>(cch_l[i]) : (from_list ? R.cpos[i] / kChunk : i / kChunk);
-    };
-    const int shifts[3] = {21, 10, 0};
-    const uint32_t dmasks[3] = {0x7FFu, 0x7FFu, 0x3FFu};
-    if (from_list) {                               // the list shares bucket b*'s 11 bits
-        prefix = static_cast<uint32_t>(R.st[ST_BSTAR]) << 21;
-        mask = 0x7FFu << 21;
-    }
-    for (int pass = from_list ? 1 : 0; pass < 3; ++pass) {
-        const int shift = shifts[pass];
-        const uint32_t dmask = dmasks[pass];
-        for (int i = tid; i < 2048; i += kMbThreads) hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < nsrc; i += kMbThreads) {
-            const uint32_t u = getk(i);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        find_bucket(hist, remaining, wsc, &s_b, &s_above);
-        prefix |= static_cast<uint32_t>(s_b) << shift;
-        mask |= dmask << shift;
-        remaining -= s_above;
-        __syncthreads();
-    }
-    const uint32_t T = prefix;
-    // per chunk: taken = (keys above T) + (keys equal to T, lowest positions
-    // first); counted in LDS from the candidates (every key >= T outside the
-    // buckets above b* is one) or, after an overflow, from the whole row
-    int* c_gt = reinterpret_cast<int*>(hist);          // hist is free now
-    int* c_eq = c_gt + kMaxChunks;
-    for (int c2 = tid; c2 < 2 * kMaxChunks; c2 += kMbThreads) c_gt[c2] = 0;
-    __syncthreads();
-    for (int i = tid; i < nsrc; i += kMbThreads) {
-        const uint32_t u = getk(i);
-        if (u > T) atomicAdd(&c_gt[getc(i)], 1);
-        else if (u == T) atomicAdd(&c_eq[getc(i)], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int o = 0, eb = 0;
-        for (int c2 = 0; c2 < nch; ++c2) {
-            const int gtc = (from_list ? R.gt[c2] : 0) + c_gt[c2];
-            const int eqc = c_eq[c2];
-            const int take_eq = min(max(remaining - eb, 0), eqc);
-            R.eqb[c2] = eb;                    // keys equal to T in earlier chunks
-            R.off[c2] = o;                     // output start of the chunk
-            o += gtc + take_eq;
-            eb += eqc;
-        }
-        R.st[ST_T] = static_cast<int>(T);
-        R.st[ST_REM] = remaining;
-        R.st[ST_DONE1] = 0;
-        R.st[ST_DONE2] = 0;
-        R.st[ST_NCAND] = 0;
-    }
-    for (int i = tid; i < 2048; i += kMbThreads) R.hist[i] = 0u;
-}
-
-__global__ __launch_bounds__(kMbThreads) void topk_mb_write(int Lmax, int K,
-                                                            const float* __restrict__ scores,
-                                                            int64_t ld, const int32_t* __restrict__ pos,
-                                                            unsigned char* __restrict__ ws,
-                                                            int32_t* __restrict__ idx,
-                                                            int32_t* __restrict__ count) {
-    __shared__ int wsc[4];
-    const int row = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int n = row_nvalid(pos, row, Lmax);
-    const int keff = n < K ? n : K;
-    int32_t* out = idx + static_cast<int64_t>(row) * K;
-    if (ch == 0) {
-        for (int i = keff + tid; i < K; i += kMbThreads) out[i] = -1;
-        if (count != nullptr && tid == 0) count[row] = keff;
-    }
-    if (ch * kChunk >= n) return;
-    const int lim = min(kChunk, n - ch * kChunk);
-    if (keff == n) {                               // every causal key is taken
-        for (int i = tid; i < lim; i += kMbThreads) out[ch * kChunk + i] = ch * kChunk + i;
-        return;
-    }
-    const MbLayout L = mb_layout(Lmax);
-    const MbRow R = mb_row(ws, L, row);
-    const uint32_t T = static_cast<uint32_t>(R.st[ST_T]);
-    const int remaining = R.st[ST_REM];
-    const float* src = scores + static_cast<int64_t>(row) * ld + ch * kChunk;
-    // thread t owns scores [8t, 8t+8) of the chunk (position order)
-    uint32_t u[kMbPer];
-    int eqn = 0, seln = 0;
-#pragma unroll
-    for (int j = 0; j < kMbPer; ++j) {
-        const int i = tid * kMbPer + j;
-        u[j] = i < lim ? float_order_key(src[i]) : 0u;
-        eqn += (i < lim && u[j] == T) ? 1 : 0;
-    }
-    int tot;
-    int e = R.eqb[ch] + block256_scan(eqn, wsc, tot);
-#pragma unroll
-    for (int j = 0; j < kMbPer; ++j) {
-        const int i = tid * kMbPer + j;
-        if (i < lim) {
-            if (u[j] > T) ++seln;
-            else if (u[j] == T) { if (e < remaining) ++seln; ++e; }
-        }
-    }
-    int o = R.off[ch] + block256_scan(seln, wsc, tot);
-    e = R.eqb[ch] + block256_scan(eqn, wsc, tot);
-#pragma unroll
-    for (int j = 0; j < kMbPer; ++j) {
-        const int i = tid * kMbPer + j;
-        if (i < lim) {
-            bool take = false;
-            if (u[j] > T) take = true;
-            else if (u[j] == T) { take = e < remaining; ++e; }
-            if (take && o < keff) out[o++] = ch * kChunk + i;
-        }
-    }
-    (void)lt_mask;
-}
-
-size_t topk_workspace_bytes(int rows, int Lmax) {
-    if (Lmax < kMbMinLmax) return 0;
-    return static_cast<size_t>(rows) * mb_layout(Lmax).row_bytes;
+// Blocks of the largest launch (level 0), for the grid-size check.
+int64_t topk_max_blocks(int rows, int Lmax) {
+    return static_cast<int64_t>(rows) * ((Lmax + kBlockItems - 1) / kBlockItems);
 }
 
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
                        const int32_t* pos, int32_t* idx, int32_t* count, void* workspace,
                        hipStream_t stream) {
-    if (Lmax >= kMbMinLmax) {
-        unsigned char* ws = static_cast<unsigned char*>(workspace);
-        const dim3 grid((Lmax + kChunk - 1) / kChunk, rows);
-        hipLaunchKernelGGL(topk_mb_hist, grid, dim3(kMbThreads), 0, stream, Lmax, K, scores, ld,
-                           pos, ws);
-        hipLaunchKernelGGL(topk_mb_cand, grid, dim3(kMbThreads), 0, stream, Lmax, K, scores, ld,
-                           pos, ws);
-        hipLaunchKernelGGL(topk_mb_write, grid, dim3(kMbThreads), 0, stream, Lmax, K, scores, ld,
-                           pos, ws, idx, count);
+    SelectArgs a{};
+    a.Lmax = Lmax;
+    a.K = K;
+    a.scores = scores;
+    a.ld = ld;
+    a.pos = pos;
+    a.idx = idx;
+    a.count = count;
+    a.speculative = rows <= 256 ? 1 : 0;
+    if (Lmax <= kBlockItems) {
+        int nt = kWave;
+        while (nt * kRegItems < Lmax) nt <<= 1;
+        a.nparts = 1;
+        hipLaunchKernelGGL((topk_select_kernel<false, false>), dim3(rows), dim3(nt), 0, stream, a);
         return hipGetLastError();
     }
+    const TourPlan t = tour_plan(rows, Lmax, K);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* key[2] = {reinterpret_cast<float*>(ws + t.a_key), reinterpret_cast<float*>(ws + t.b_key)};
+    int32_t* cpos[2] = {reinterpret_cast<int32_t*>(ws + t.a_pos),
+                        reinterpret_cast<int32_t*>(ws + t.b_pos)};
+    int32_t* cnt[2] = {reinterpret_cast<int32_t*>(ws + t.a_cnt),
+                       reinterpret_cast<int32_t*>(ws + t.b_cnt)};
+    a.kp_shift = t.kp_shift;
+    // level 0: row chunks -> candidate lists in A
+    a.nparts = t.lists0;
+    a.out_key = key[0];
+    a.out_pos = cpos[0];
+    a.out_cnt = cnt[0];
+    hipLaunchKernelGGL((topk_select_kernel<false, true>), dim3(rows * t.lists0),
+                       dim3(kRegMaxThreads), 0, stream, a);
+    int cur = 0, lists = t.lists0;
+    while (lists > t.group) {                // merge levels
+        const int nout = (lists + t.group - 1) / t.group;
+        a.in_key = key[cur];
+        a.in_pos = cpos[cur];
+        a.in_cnt = cnt[cur];
+        a.in_lists = lists;
+        a.nparts = nout;
+        a.out_key = key[cur ^ 1];
+        a.out_pos = cpos[cur ^ 1];
+        a.out_cnt = cnt[cur ^ 1];
+        hipLaunchKernelGGL((topk_select_kernel<true, true>), dim3(rows * nout),
+                           dim3(kRegMaxThreads), 0, stream, a);
+        cur ^= 1;
+        lists = nout;
+    }
+    // last level: the row's remaining lists -> indices
+    a.in_key = key[cur];
+    a.in_pos = cpos[cur];
+    a.in_cnt = cnt[cur];
+    a.in_lists = lists;
+    a.nparts = 1;
     int nt = kWave;
-    while (nt * kRegItems < Lmax) nt <<= 1;
-    const int speculative = rows <= 256 ? 1 : 0;
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(nt), 0, stream, Lmax, K, speculative, scores,
-                       ld, pos, idx, count);
+    while (nt * kRegItems < (lists << t.kp_shift)) nt <<= 1;
+    hipLaunchKernelGGL((topk_select_kernel<true, false>), dim3(rows), dim3(nt), 0, stream, a);
     return hipGetLastError();
 }
 

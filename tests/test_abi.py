@@ -132,6 +132,18 @@ def test_topk_validation():
         assert call(L.dsa_topk, a) == code, change
     n = ctypes.c_size_t(7)
     assert L.dsa_topk_workspace(ctypes.byref(good_topk()), ctypes.byref(n)) == 0
+    assert n.value == 0                            # rows of up to 16,384 scores
+    a = good_topk()
+    a.Lmax = a.ld_scores = 131072
+    assert L.dsa_topk_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value >= 2 * 8 * 2048 * 8             # 8 chunk lists of (key, position) per row
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert call(L.dsa_topk, a) == 4
+    a.workspace_bytes, a.workspace = n.value, FAKE + 16
+    assert call(L.dsa_topk, a) == 5
+    a = good_topk()
+    a.B, a.Lmax, a.ld_scores = 1 << 30, 1 << 21, 1 << 21   # 2^37 level-0 blocks
+    assert call(L.dsa_topk, a) == 2
 
 
 def good_mla(B=1, S=1, K=2048):

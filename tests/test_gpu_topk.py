@@ -12,8 +12,10 @@ from gpu_util import check_topk_properties, dev, host, say
 pytestmark = pytest.mark.gpu
 
 
-def run_topk(scores_rows, n_valid, K, Lmax=None, sentinel=1e30):
-    """scores_rows [R, L] float32 -> GPU idx [R, K] (rows as B=R, S=1)."""
+def run_topk(scores_rows, n_valid, K, Lmax=None, sentinel=1e30, ws_fill=None):
+    """scores_rows [R, L] float32 -> GPU idx [R, K] (rows as B=R, S=1).
+    ws_fill: byte value the workspace holds before the call (its contents on
+    entry must not matter)."""
     import torch
     R, L = scores_rows.shape
     Lmax = Lmax or L
@@ -24,7 +26,12 @@ def run_topk(scores_rows, n_valid, K, Lmax=None, sentinel=1e30):
             buf[r, 0, max(n, 0):] = np.float32(sentinel)
     pos = (np.asarray(n_valid, np.int64) - 1).astype(np.int32).reshape(R, 1)
     count = torch.empty((R, 1), dtype=torch.int32, device="cuda")
-    idx = dsa.topk(dev(buf), dev(pos), K, count=count)
+    d_sc, d_pos = dev(buf), dev(pos)
+    ws = None
+    if ws_fill is not None:
+        ws = dsa.topk_workspace(d_sc, d_pos, K)
+        ws.fill_(ws_fill)
+    idx = dsa.topk(d_sc, d_pos, K, count=count, workspace=ws)
     torch.cuda.synchronize()
     return host(idx)[:, 0], host(count)[:, 0]
 
@@ -42,16 +49,46 @@ def test_topk_bit_exact_lds_rows(kind, K):
     assert np.array_equal(cnt, np.minimum(lens, K))
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "zeros"])
-def test_topk_bit_exact_long_rows(kind):
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "constant", "wide"])
+@pytest.mark.parametrize("K", [1, 100, 2048])
+def test_topk_bit_exact_long_rows(kind, K):
+    """Rows past one selection block (16,384 scores): chunk lists, then one
+    merge; lengths cover a one-score tail chunk, chunks past the causal end,
+    a row that fits in its first chunk and rows shorter than K."""
     L = 131072
-    lens = [131072, 16385, 40000, 70001]
-    sc = synth.topk_scores(2000, len(lens), L, kind)
-    say(f"topk long rows kind={kind}")
+    lens = [131072, 16385, 40000, 70001, 12000, 1500, 0, 98305]
+    sc = synth.topk_scores(2000 + K, len(lens), L, kind)
+    say(f"topk long rows kind={kind} K={K}")
+    g, cnt = run_topk(sc, lens, K, ws_fill=0xFF)
+    o = oracle.topk(sc, lens, K)
+    assert np.array_equal(g, o)
+    assert np.array_equal(cnt, np.minimum(lens, K))
+    check_topk_properties(sc, g, lens, K, kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_topk_multi_level_rows(kind):
+    """2^21-score rows: 128 chunk lists, merged to 16, to 2, then the row."""
+    L = 1 << 21
+    lens = [L, 1_000_001]
+    sc = synth.topk_scores(2500, len(lens), L, kind)
+    say(f"topk 2M rows kind={kind}")
+    g, cnt = run_topk(sc, lens, 2048, ws_fill=0x7F)
+    o = oracle.topk(sc, lens, 2048)
+    assert np.array_equal(g, o)
+    assert np.array_equal(cnt, np.minimum(lens, 2048))
+
+
+def test_topk_long_rows_many():
+    """Many 32K rows of ragged lengths (two chunk lists per row)."""
+    L = 32768
+    g0 = np.random.default_rng(7)
+    lens = g0.integers(0, L + 1, size=300).tolist()
+    sc = synth.topk_scores(2600, len(lens), L, "ties")
+    say("topk 300 rows of 32K")
     g, cnt = run_topk(sc, lens, 2048)
     o = oracle.topk(sc, lens, 2048)
     assert np.array_equal(g, o)
-    check_topk_properties(sc, g, lens, 2048, kind)
 
 
 def test_topk_prefill_rows():
