@@ -438,14 +438,26 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
 
 // ---------------------------------------------------------------------------
 // Fused decode path (one query row per batch row): every block quantises its
-// row's 64 query heads itself (into LDS) while its key loads are in flight,
-// and the block that covers the row's own position also rotates, quantises
-// and appends the new key, using it straight from LDS. One launch replaces
-// prepare(k) + prepare(q) + score.
-// Query quantisation layout: thread t owns head t/4, quarter t%4 of the 128
-// features; quarters 0/1 hold rotary pairs (j, j+32) for j in [16q, 16q+16),
-// quarters 2/3 hold features 64..95 / 96..127. The head's amax is reduced
-// over its four threads.
+// row's 64 query heads itself (into LDS) while its first key loads are in
+// flight, and the block that covers the row's own position also rotates,
+// quantises and appends the new key, using it straight from LDS. One launch
+// replaces prepare(k) + prepare(q) + score.
+// A block of NW waves scores chunks of NW * 16 U consecutive keys of its
+// row, wave w the keys [16 U w, 16 U w + 16 U) of a chunk; block x takes the
+// row's chunks x, x + gridDim.x, ... Calls with few keys in all get one chunk
+// per block (many small blocks: latency); calls with many get a few blocks
+// per CU that loop over chunks with two chunks in flight (three register
+// buffers in rotation), so the query quantisation is paid once per block.
+// Query quantisation layout: thread t owns head t / TPH and the part e =
+// t % TPH of its features (TPH = NW threads per head): parts e < TPH/2 hold
+// rotary pairs (j, j + 32), parts e >= TPH/2 runs of features 64..127. The
+// head's amax is reduced over its TPH threads.
+// Scoring: per 16 keys (u) and 16 heads (hg), 4 MFMAs over the 128 features;
+// lane (m, g) gets heads 4g..4g+3 of key m and accumulates
+// w'[h] * (s + |s|) = w[h] q_scale[h] ReLU(s), with w' = w q_scale / 2 (the
+// halving and doubling are exact). The four lanes g of a key then add their
+// sums with two cross-lane steps that also scatter the U key groups over the
+// lanes, so that one store per wave writes up to 64 consecutive scores.
 // ---------------------------------------------------------------------------
 template <bool BF16_IN>
 __device__ __forceinline__ float load_act(const void* base, int64_t i) {
@@ -458,13 +470,23 @@ __device__ __forceinline__ float round_act(float v) {
     return BF16_IN ? bf16_bits_to_float(float_to_bf16_bits(v)) : v;
 }
 
-template <int U, bool BF16_IN>
-__global__ __launch_bounds__(256) void decode_score_kernel(
+template <int U>
+struct DecChunk {
+    uint4 k[U][2];      // key codes: lane (m, g), key 16 u + m, bytes [32 g, 32 g + 32)
+    float ks;           // scale of the key this lane stores (-inf: page not present)
+};
+
+template <int U, int NW, bool LOOP, bool BF16_IN>
+__global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     int H, int Lmax, int P, const void* __restrict__ q_raw, const void* __restrict__ k_raw,
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, const float* __restrict__ w, uint8_t* __restrict__ kcache,
     float* __restrict__ kscale, uint8_t* __restrict__ q8_out, float* __restrict__ qs_out,
     float* __restrict__ scores, int64_t ld, CacheMap cmap) {
+    constexpr int kThreads = NW * 64;
+    constexpr int kTPH = kThreads / 64;                 // threads per query head
+    constexpr int kFPT = 128 / kTPH;                    // features per thread
+    constexpr int kChunkKeys = NW * 16 * U;
     __shared__ __align__(16) uint8_t qcodes[64 * 128];
     __shared__ float qscale[64];
     __shared__ __align__(16) uint8_t kcodes[128];
@@ -474,83 +496,113 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     const int p = pos[row];
     if (p < 0 || p >= Lmax || p >= P) return;
     const int n_valid = p + 1;
-    const int kblock0 = blockIdx.x * (64 * U);
-    if (kblock0 >= n_valid) return;
+    const int nchunks = (n_valid + kChunkKeys - 1) / kChunkKeys;
+    const int stride = static_cast<int>(gridDim.x);
+    int chunk = blockIdx.x;
+    if (chunk >= nchunks) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t b = row;
-    const int wkey0 = kblock0 + wave * 16 * U;
     const int64_t prow = cmap.row(b, p);                              // the new key's row
-    const bool has_new = k_raw != nullptr && prow >= 0 && kblock0 + 64 * U > p;
+    const int chunk_p = p / kChunkKeys;                               // chunk holding p
+    const bool has_new = k_raw != nullptr && prow >= 0 && chunk_p % stride == chunk;
+    // the key (within the wave's 16 U) whose score this lane stores
+    const int own = U == 4 ? lane : (U == 2 ? 16 * (g >> 1) + m : m);
+    const bool stores = U == 4 ? true : (U == 2 ? (g & 1) == 0 : g == 0);
+    const bool dense = cmap.table == nullptr;
+    const uint8_t* kc_row = kcache + (dense ? b * cmap.batch_rows * 128 : 0);
+    const float* ks_row = kscale + (dense ? b * cmap.batch_rows : 0);
 
-    // 1. key loads first (the new key, if any, is taken from LDS later);
-    // ks = -inf marks a key whose page is not present
-    uint4 kraw[U][2];
-    float ks[U];
+    // 1. key loads of chunk c (the new key, if any, is taken from LDS later)
+    auto load_chunk = [&](int c, DecChunk<U>& d) {
+        const int wkey0 = c * kChunkKeys + wave * 16 * U;
+        if (dense && wkey0 + 16 * U <= n_valid) {
+            const uint4* src =
+                reinterpret_cast<const uint4*>(kc_row + static_cast<int64_t>(wkey0 + m) * 128 + g * 32);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        int key = wkey0 + u * 16 + m;
-        key = key < n_valid ? key : n_valid - 1;
-        const int64_t krow = cmap.row(b, key);
-        const uint4* src =
-            reinterpret_cast<const uint4*>(kcache + (krow >= 0 ? krow : 0) * 128 + g * 32);
-        kraw[u][0] = src[0];
-        kraw[u][1] = src[1];
-        ks[u] = krow >= 0 ? kscale[krow] : -INFINITY;
+            for (int u = 0; u < U; ++u) {
+                d.k[u][0] = src[u * 128];
+                d.k[u][1] = src[u * 128 + 1];
+            }
+            d.ks = ks_row[wkey0 + own];
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int key = wkey0 + u * 16 + m;
+                key = key < n_valid ? key : n_valid - 1;
+                const int64_t krow = cmap.row(b, key);
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(kcache + (krow >= 0 ? krow : 0) * 128 + g * 32);
+                d.k[u][0] = src[0];
+                d.k[u][1] = src[1];
+            }
+            int okey = wkey0 + own;
+            okey = okey < n_valid ? okey : n_valid - 1;
+            const int64_t orow = cmap.row(b, okey);
+            d.ks = orow >= 0 ? kscale[orow] : -INFINITY;
+        }
+    };
+    DecChunk<U> A, Bc;
+    load_chunk(chunk, A);
+    if constexpr (LOOP) {                    // two chunks in flight during the quantisation
+        if (chunk + stride < nchunks) load_chunk(chunk + stride, Bc);
     }
 
     // 2. quantise the row's query heads into LDS
     {
 #pragma clang fp contract(off)
-        const int hh = tid >> 2, qt = tid & 3;
-        float v[32];
+        constexpr int kHalf = kTPH / 2;
+        const int hh = tid / kTPH, e = tid % kTPH;
+        float v[kFPT];
         float amax = 0.0f;
         if (hh < H) {
             const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128;
-            if (qt < 2) {
-                const int j0 = 16 * qt;
+            if (e < kHalf) {
+                const int j0 = (kFPT / 2) * e;
                 const float* c = cos_t + static_cast<int64_t>(p) * 32 + j0;
                 const float* sn = sin_t + static_cast<int64_t>(p) * 32 + j0;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < kFPT / 2; ++j) {
                     const float a = load_act<BF16_IN>(q_raw, base + j0 + j);
                     const float bb = load_act<BF16_IN>(q_raw, base + j0 + j + 32);
                     const float ac = a * c[j], bs = bb * sn[j];
                     const float as = a * sn[j], bc = bb * c[j];
                     v[j] = round_act<BF16_IN>(ac - bs);
-                    v[16 + j] = round_act<BF16_IN>(as + bc);
+                    v[kFPT / 2 + j] = round_act<BF16_IN>(as + bc);
                 }
             } else {
-                const int f0 = 64 + 32 * (qt - 2);
+                const int f0 = 64 + kFPT * (e - kHalf);
 #pragma unroll
-                for (int j = 0; j < 32; ++j) v[j] = load_act<BF16_IN>(q_raw, base + f0 + j);
+                for (int j = 0; j < kFPT; ++j) v[j] = load_act<BF16_IN>(q_raw, base + f0 + j);
             }
 #pragma unroll
-            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+            for (int j = 0; j < kFPT; ++j) amax = fmaxf(amax, fabsf(v[j]));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
+#pragma unroll
+        for (int o = 1; o < kTPH; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
         float scale = amax / 448.0f;
         if (!(scale > 0.0f)) scale = 1.0f;
-        // 32 codes packed into two 16-byte LDS stores
-        uint32_t pk[8];
+        uint32_t pk[kFPT / 4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kFPT / 4; ++i) {
             uint32_t word = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                word |= static_cast<uint32_t>(e4m3_encode(v[4 * i + e] / scale)) << (8 * e);
+            for (int q = 0; q < 4; ++q)
+                word |= static_cast<uint32_t>(e4m3_encode(v[4 * i + q] / scale)) << (8 * q);
             pk[i] = hh < H ? word : 0u;
         }
-        // quarters 0/1: features [16q, 16q+16) and [16q+32, 16q+48); 2/3: [32q, 32q+32)
-        const int off0 = qt < 2 ? 16 * qt : 32 * qt;
-        const int off1 = qt < 2 ? 16 * qt + 32 : 32 * qt + 16;
-        uint4* dst0 = reinterpret_cast<uint4*>(qcodes + hh * 128 + off0);
-        uint4* dst1 = reinterpret_cast<uint4*>(qcodes + hh * 128 + off1);
-        *dst0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        *dst1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        if (qt == 0) qscale[hh] = hh < H ? scale : 0.0f;
+        // parts e < TPH/2: bytes [j0, j0 + FPT/2) and [32 + j0, ...); others [f0, f0 + FPT)
+        uint8_t* dst = qcodes + hh * 128;
+        const int off0 = e < kHalf ? (kFPT / 2) * e : 64 + kFPT * (e - kHalf);
+        const int off1 = e < kHalf ? 32 + (kFPT / 2) * e : off0 + kFPT / 2;
+#pragma unroll
+        for (int i = 0; i < kFPT / 16; ++i) {          // FPT/2 bytes per half, 8 per store
+            reinterpret_cast<uint2*>(dst + off0)[i] = make_uint2(pk[2 * i], pk[2 * i + 1]);
+            reinterpret_cast<uint2*>(dst + off1)[i] =
+                make_uint2(pk[kFPT / 8 + 2 * i], pk[kFPT / 8 + 2 * i + 1]);
+        }
+        if (e == 0) qscale[hh] = hh < H ? scale : 0.0f;
     }
     // 3. the new key (block covering position p): wave 0, lane l holds l, l+64
     if (has_new && wave == 0) {
@@ -587,15 +639,16 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
     }
     __syncthreads();
     if (blockIdx.x == 0 && q8_out != nullptr) {
-        for (int i = tid; i < H * 8; i += 256)
+        for (int i = tid; i < H * 8; i += kThreads)
             reinterpret_cast<uint4*>(q8_out + static_cast<int64_t>(row) * H * 128)[i] =
                 reinterpret_cast<const uint4*>(qcodes)[i];
         if (tid < H) qs_out[static_cast<int64_t>(row) * H + tid] = qscale[tid];
     }
 
-    // 4. operands from LDS, MFMA stream (as score_kernel)
+    // 4. query operands from LDS (lane (m, g): head 16 hg + m, features
+    // 32 g + 8 kk + j), halved head weights
     bf16x8 qa[4][4];
-    float wq[4][4];
+    float wq2[4][4];
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
         const uint4* src = reinterpret_cast<const uint4*>(qcodes + (hg * 16 + m) * 128 + g * 32);
@@ -607,57 +660,131 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = hg * 16 + 4 * g + i;
-            wq[hg][i] = h < H ? w[static_cast<int64_t>(row) * H + h] * qscale[h] : 0.0f;
+            wq2[hg][i] = h < H ? 0.5f * (w[static_cast<int64_t>(row) * H + h] * qscale[h]) : 0.0f;
         }
     }
     float* out = scores + static_cast<int64_t>(row) * ld;
+
+    // 5. score chunk c (the chunk holding p first takes the new key's codes
+    // from LDS)
+    auto score_chunk = [&](int c, DecChunk<U>& d) {
+        const int wkey0 = c * kChunkKeys + wave * 16 * U;
+        if (has_new && c == chunk_p) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int key0 = wkey0 + u * 16;
-        if (key0 >= n_valid) break;
-        const int key = key0 + m;
-        float ksc = ks[u];
-        if (has_new && key == p) {
-            kraw[u][0] = reinterpret_cast<const uint4*>(kcodes + g * 32)[0];
-            kraw[u][1] = reinterpret_cast<const uint4*>(kcodes + g * 32)[1];
-            ksc = kscale_new;
+            for (int u = 0; u < U; ++u) {
+                if (wkey0 + 16 * u + m == p) {
+                    d.k[u][0] = reinterpret_cast<const uint4*>(kcodes + g * 32)[0];
+                    d.k[u][1] = reinterpret_cast<const uint4*>(kcodes + g * 32)[1];
+                }
+            }
         }
-        bf16x8 kbf[4];
-        kbf[0] = e4m3x8_to_bf16x8(kraw[u][0].x, kraw[u][0].y);
-        kbf[1] = e4m3x8_to_bf16x8(kraw[u][0].z, kraw[u][0].w);
-        kbf[2] = e4m3x8_to_bf16x8(kraw[u][1].x, kraw[u][1].y);
-        kbf[3] = e4m3x8_to_bf16x8(kraw[u][1].z, kraw[u][1].w);
-        float part = 0.0f;
+        float part[U];
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-            v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < U; ++u) {
+            const uint4 k0 = d.k[u][0], k1 = d.k[u][1];
+            bf16x8 kbf[4];
+            kbf[0] = e4m3x8_to_bf16x8(k0.x, k0.y);
+            kbf[1] = e4m3x8_to_bf16x8(k0.z, k0.w);
+            kbf[2] = e4m3x8_to_bf16x8(k1.x, k1.y);
+            kbf[3] = e4m3x8_to_bf16x8(k1.z, k1.w);
+            float sum = 0.0f;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
+            for (int hg = 0; hg < 4; ++hg) {
+                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part += wq[hg][i] * fmaxf(acc[i], 0.0f);
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16_16x16x32(qa[hg][kk], kbf[kk], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum = fmaf(wq2[hg][i], acc[i] + fabsf(acc[i]), sum);
+            }
+            part[u] = sum;
         }
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        if (g == 0 && key < n_valid) out[key] = ksc == -INFINITY ? -INFINITY : part * ksc;
+        // head sum over g, scattering the key groups: afterwards lane (m, g)
+        // holds the total of key `own`
+        float tot;
+        if constexpr (U == 4) {
+            const bool hi = g >= 2;                  // keeps groups 2, 3 (else 0, 1)
+            const float r0 = (hi ? part[2] : part[0]) + __shfl_xor(hi ? part[0] : part[2], 32);
+            const float r1 = (hi ? part[3] : part[1]) + __shfl_xor(hi ? part[1] : part[3], 32);
+            const bool odd = (g & 1) != 0;           // keeps the second of the two
+            tot = (odd ? r1 : r0) + __shfl_xor(odd ? r0 : r1, 16);
+        } else if constexpr (U == 2) {
+            const bool hi = g >= 2;                  // keeps group 1 (else 0)
+            const float r = (hi ? part[1] : part[0]) + __shfl_xor(hi ? part[0] : part[1], 32);
+            tot = r + __shfl_xor(r, 16);
+        } else {
+            const float r = part[0] + __shfl_xor(part[0], 32);
+            tot = r + __shfl_xor(r, 16);
+        }
+        const int key = wkey0 + own;
+        const float ksc = (has_new && key == p) ? kscale_new : d.ks;
+        if (stores && key < n_valid) out[key] = ksc == -INFINITY ? -INFINITY : tot * ksc;
+    };
+
+    if constexpr (!LOOP) {
+        score_chunk(chunk, A);
+    } else {
+        // three buffers in rotation, two chunks in flight: A holds chunk x,
+        // Bc chunk x + stride, C is free
+        DecChunk<U> C;
+        for (int x = chunk;; x += 3 * stride) {
+            if (x + 2 * stride < nchunks) load_chunk(x + 2 * stride, C);
+            score_chunk(x, A);
+            if (x + stride >= nchunks) break;
+            if (x + 3 * stride < nchunks) load_chunk(x + 3 * stride, A);
+            score_chunk(x + stride, Bc);
+            if (x + 2 * stride >= nchunks) break;
+            if (x + 4 * stride < nchunks) load_chunk(x + 4 * stride, Bc);
+            score_chunk(x + 2 * stride, C);
+            if (x + 3 * stride >= nchunks) break;
+        }
     }
 }
+
+// Looping decode grid: blocks of DSA_DEC_LOOP_NW waves scoring chunks of
+// DSA_DEC_LOOP_NW * 64 keys, about DSA_DEC_LOOP_BLOCKS blocks in all; used
+// when a call has more than that many chunks.
+#ifndef DSA_DEC_LOOP_BLOCKS
+#define DSA_DEC_LOOP_BLOCKS 256
+#endif
+#ifndef DSA_DEC_LOOP_NW
+#define DSA_DEC_LOOP_NW 8
+#endif
 
 hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, const void* q_raw,
                                const void* k_raw, const int32_t* pos, const float* cos_t,
                                const float* sin_t, const float* w, uint8_t* kcache,
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
                                int64_t ld, CacheMap cmap, hipStream_t stream) {
+    constexpr int kLoopChunk = DSA_DEC_LOOP_NW * 64;
+    const int chunksl = (Lmax + kLoopChunk - 1) / kLoopChunk;
+    const bool loop = static_cast<int64_t>(B) * chunksl > DSA_DEC_LOOP_BLOCKS;
     int U = 4;
-    while (U > 1 && static_cast<int64_t>(B) * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
-    const dim3 grid(static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U)), static_cast<unsigned>(B));
-#define DSA_DEC(UU, BF)                                                                          \
-    hipLaunchKernelGGL((decode_score_kernel<UU, BF>), grid, dim3(256), 0, stream, H, Lmax, P,    \
-                       q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out, qs_out,     \
-                       scores, ld, cmap)
-    if (bf16_in) {
-        if (U == 4) DSA_DEC(4, true); else if (U == 2) DSA_DEC(2, true); else DSA_DEC(1, true);
+    unsigned gx, threads;
+    if (loop) {
+        const int bpr = (DSA_DEC_LOOP_BLOCKS + B - 1) / B;
+        gx = static_cast<unsigned>(bpr < chunksl ? bpr : chunksl);
+        threads = DSA_DEC_LOOP_NW * 64;
     } else {
-        if (U == 4) DSA_DEC(4, false); else if (U == 2) DSA_DEC(2, false); else DSA_DEC(1, false);
+        // one chunk of 64 U keys per block, U shrunk (down to 1) to give more blocks
+        while (U > 1 && static_cast<int64_t>(B) * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
+        gx = static_cast<unsigned>((Lmax + 64 * U - 1) / (64 * U));
+        threads = 256;
+    }
+    const dim3 grid(gx, static_cast<unsigned>(B));
+#define DSA_DEC(UU, NWW, LP, BF)                                                                 \
+    hipLaunchKernelGGL((decode_score_kernel<UU, NWW, LP, BF>), grid, dim3(threads), 0, stream, H, \
+                       Lmax, P, q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out,    \
+                       qs_out, scores, ld, cmap)
+    if (bf16_in) {
+        if (loop) DSA_DEC(4, DSA_DEC_LOOP_NW, true, true);
+        else if (U == 4) DSA_DEC(4, 4, false, true);
+        else if (U == 2) DSA_DEC(2, 4, false, true);
+        else DSA_DEC(1, 4, false, true);
+    } else {
+        if (loop) DSA_DEC(4, DSA_DEC_LOOP_NW, true, false);
+        else if (U == 4) DSA_DEC(4, 4, false, false);
+        else if (U == 2) DSA_DEC(2, 4, false, false);
+        else DSA_DEC(1, 4, false, false);
     }
 #undef DSA_DEC
     return hipGetLastError();

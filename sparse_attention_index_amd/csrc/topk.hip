@@ -103,6 +103,20 @@ __device__ __forceinline__ void find_digit_wave0(RegShared& sh, int want) {
     }
 }
 
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+}
+
+// The float with order key k (the inverse of float_order_key; key
+// 0x80000000 gives +0.0). The key map is strictly monotone and maps -0 and +0
+// alike, so for non-NaN x: key(x) > k iff x > value(k), key(x) == k iff
+// x == value(k).
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ void clear_hist(RegShared& sh) {
     for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) sh.hist[b] = 0u;
 }
@@ -150,7 +164,6 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = static_cast<int>(blockDim.x) >> 6;
     const int nitems = static_cast<int>(blockDim.x) * kRegItems;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int base = wave * (kWave * kRegItems) + lane;
     const int kps = a.kp_shift;
     const int K = a.K;
@@ -257,12 +270,11 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     }
     const int keff = M < K ? M : K;
 
-    uint32_t T;                             // threshold order key
-    int eq_take;                            // keys equal to T that are taken
+    uint32_t T = 0u;                        // threshold order key
+    int eq_take = 0;                        // keys equal to T that are taken
     bool counted = false;                   // sh.wa / sh.wb already hold the per-wave counts
-    if (keff == M) {                        // every valid item is selected (keys >= 0)
-        T = 0u;
-        eq_take = M;
+    const bool take_all = keff == M;        // every valid item is selected
+    if (take_all) {
     } else if (!(vmax > vmin)) {            // all valid scores equal
         T = float_order_key(vmax);
         eq_take = keff;
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
                         if (lane == 0) at = atomicAdd(&sh.ccount, __popcll(m));
                         at = __shfl(at, 0);
                         if (is_c) {
-                            const int slot = at + __popcll(m & lt_mask);
+                            const int slot = at + lanes_below(m);
                             sh.cand[slot] = float_order_key(v[j]);
                             sh.cand_wave[slot] = wave;
                         }
@@ -375,15 +387,18 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         }
     }
 
-    // 4. ordered compaction
+    // 4. ordered compaction: taken are the valid items above T and, of those
+    // equal to T, the first eq_take in item order (compared as floats against
+    // the value of T)
+    const float Tf = order_key_value(T);
+    auto above = [&](int j) -> bool { return valid(j) && (take_all || v[j] > Tf); };
+    auto equal = [&](int j) -> bool { return !take_all && valid(j) && v[j] == Tf; };
     if (!counted) {
         int gtw = 0, eqw = 0;
 #pragma unroll
         for (int j = 0; j < kRegItems; ++j) {
-            const bool ok = valid(j);
-            const uint32_t uk = float_order_key(v[j]);
-            gtw += __popcll(__ballot(ok && uk > T));
-            eqw += __popcll(__ballot(ok && uk == T));
+            gtw += __popcll(__ballot(above(j)));
+            eqw += __popcll(__ballot(equal(j)));
         }
         if (lane == 0) {
             sh.wa[wave] = gtw;
@@ -405,14 +420,12 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
 #pragma unroll
     for (int j = 0; j < kRegItems; ++j) {
         const int i = base + kWave * j;
-        const bool ok = valid(j);
-        const uint32_t uk = float_order_key(v[j]);
-        const bool eq = ok && uk == T;
+        const bool eq = equal(j);
         const uint64_t eqm = __ballot(eq);
-        const bool take = (ok && uk > T) || (eq && e + __popcll(eqm & lt_mask) < eq_take);
+        const bool take = above(j) || (eq && e + lanes_below(eqm) < eq_take);
         e += __popcll(eqm);
         const uint64_t tm = __ballot(take);
-        const int slot = o + __popcll(tm & lt_mask);
+        const int slot = o + lanes_below(tm);
         if (take && slot < keff) {
             int32_t p;
             if constexpr (CAND_IN) p = a.in_pos[cbase + i];

@@ -84,6 +84,10 @@ CASES = [
     ("f32", 1, 3, 64, 700, [[699, 100, 1]], False, 104),
     # more than eight queries per batch row: the 64-query x 128-key tile path
     ("tiles", 2, 70, 64, 400, [list(range(330, 400)), list(range(0, 140, 2))], True, 105),
+    # more than 512 key chunks of 256 in the call: blocks loop over chunks; the
+    # new keys of rows 0 / 1 fall in a block's second chunk
+    ("loop", 6, 1, 64, 30000, [[29999], [12345], [0], [20000], [1792], [255]], True, 106),
+    ("loop-f32", 3, 1, 64, 50000, [[49999], [30001], [70]], False, 107),
 ]
 
 

@@ -45,11 +45,12 @@ def scatter_pool(dense, table, page, num_pages):
     return pool
 
 
-@pytest.mark.parametrize("S,page", [(1, 64), (1, 16), (3, 128), (20, 32)])
-def test_indexer_paged_matches_dense(S, page):
+@pytest.mark.parametrize("S,page,Lmax", [(1, 64, 1000), (1, 16, 1000), (3, 128, 1000),
+                                         (20, 32, 1000), (1, 64, 70000)])
+def test_indexer_paged_matches_dense(S, page, Lmax):
     import torch
-    B, H, Lmax = 2, 64, 1000
-    say(f"indexer paged S={S} page={page}")
+    B, H = 2, 64
+    say(f"indexer paged S={S} page={page} Lmax={Lmax}")
     g = synth.rng(400 + S + page)
     q_raw = synth.bf16_bits_to_f32(synth.to_bf16_bits(g.standard_normal((B, S, H, 128), dtype=np.float32)))
     k_all = synth.bf16_bits_to_f32(synth.to_bf16_bits(g.standard_normal((B, Lmax, 128), dtype=np.float32)))
