@@ -26,6 +26,15 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats to packed bf16 (lo in bits 0..15), rounded to nearest even by
+// the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = static_cast<__bf16>(lo);
+    r[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // ---- OCP E4M3 encoding (round to nearest even, saturating at 448) --------
 // Branch-free, on the bits of the float32 input. Normal outputs: adding
 // 0x7FFFF plus the lowest kept bit to the magnitude bits rounds the 23-bit

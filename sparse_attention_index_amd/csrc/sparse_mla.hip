@@ -47,7 +47,7 @@ namespace dsa {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-constexpr int kDl = 512, kDr = 64, kDq = 576;
+constexpr int kDl = 512, kDq = 576;
 constexpr int kTile = 32;
 constexpr int kKtStride = kDq + 8;      // bf16 per K-tile row (1168 B, staggers banks)
 constexpr int kMlaThreads = 256;        // 4 waves x 16 heads
@@ -291,10 +291,8 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
         uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
 #pragma unroll
         for (int t2 = 0; t2 < kT2; ++t2) {
-            const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][0] * inv)) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][1] * inv)) << 16);
-            const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][2] * inv)) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][3] * inv)) << 16);
+            const uint32_t lo = pack_bf16x2(acc[t2][0] * inv, acc[t2][1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[t2][2] * inv, acc[t2][3] * inv);
             *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
         }
         if (lse != nullptr && g == 0)
@@ -307,10 +305,8 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
         uint16_t* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
 #pragma unroll
         for (int t2 = 0; t2 < kT2; ++t2) {
-            const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][0])) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][1])) << 16);
-            const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(acc[t2][2])) |
-                                (static_cast<uint32_t>(float_to_bf16_bits(acc[t2][3])) << 16);
+            const uint32_t lo = pack_bf16x2(acc[t2][0], acc[t2][1]);
+            const uint32_t hi = pack_bf16x2(acc[t2][2], acc[t2][3]);
             *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
         }
         if (g == 0 && h < Hq)
@@ -403,10 +399,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
     const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
     uint16_t* oh = out + (row * Hq + h) * kDl + 4 * g;
     auto pack = [&](float4 a) {
-        const uint32_t lo = static_cast<uint32_t>(float_to_bf16_bits(a.x * inv)) |
-                            (static_cast<uint32_t>(float_to_bf16_bits(a.y * inv)) << 16);
-        const uint32_t hi = static_cast<uint32_t>(float_to_bf16_bits(a.z * inv)) |
-                            (static_cast<uint32_t>(float_to_bf16_bits(a.w * inv)) << 16);
+        const uint32_t lo = pack_bf16x2(a.x * inv, a.y * inv);
+        const uint32_t hi = pack_bf16x2(a.z * inv, a.w * inv);
         return make_uint2(lo, hi);
     };
     *reinterpret_cast<uint2*>(oh + 16 * t2a) = pack(a0);

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
 
     // 1. load the items
     float v[kRegItems];
+    int32_t pv[CAND_IN ? kRegItems : 1];     // candidate source: positions of the items
     uint32_t vmask = 0u;                     // candidate source: bit j = item j is valid
     int M = 0;                               // valid items of the block
     int start = 0;                           // score source: chunk start in the row
@@ -222,8 +223,10 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
             const int i = base + kWave * j;
             const int s = i >> kps;
             v[j] = 0.0f;
+            pv[j] = 0;
             if (s < nsl) {
                 v[j] = a.in_key[cbase + i];
+                pv[j] = a.in_pos[cbase + i];
                 vmask |= (i & kpm) < cnt[s] ? (1u << j) : 0u;
             }
         }
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         const int slot = o + lanes_below(tm);
         if (take && slot < keff) {
             int32_t p;
-            if constexpr (CAND_IN) p = a.in_pos[cbase + i];
+            if constexpr (CAND_IN) p = pv[j];
             else p = start + i;
             if constexpr (CAND_OUT) {
                 a.out_key[ob + slot] = v[j];
