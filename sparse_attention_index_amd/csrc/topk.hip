@@ -8,8 +8,9 @@
 // in ascending position order and padded with -1.
 //
 // The selection block: up to 16,384 items held in registers (16 per thread;
-// wave w owns the contiguous run [1024 w, 1024 w + 1024), lane l item j at
-// 1024 w + 64 j + l), of which the valid ones are ranked; it keeps
+// wave w owns the contiguous run [1024 w, 1024 w + 1024), in four groups of
+// 256: lane l holds items 1024 w + 256 g + 4 l + q, q < 4, of group g, so
+// every load is 16 bytes), of which the valid ones are ranked; it keeps
 // k = min(K, valid count) of them.
 //  1. Load (adding +0.0 folds -0.0 into +0.0) and the min/max of the valid
 //     items.
@@ -27,8 +28,9 @@
 //     the lowest item indices, as many as k leaves.
 //  4. Ordered compaction: per-wave counts of keys above / equal to T (taken
 //     during step 3 when one wave ranked b*, else by a ballot pass) give each
-//     wave its output start, and each wave writes its taken items in item
-//     order.
+//     wave its output start; per group, a DPP prefix sum of the lanes' taken
+//     counts places each lane's items, so each wave writes its taken items in
+//     item order.
 //
 // Rows of up to 16,384 scores: one selection block per row over the row
 // itself. Longer rows: a tournament. Level 0 splits the row into chunks of
@@ -164,7 +166,9 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = static_cast<int>(blockDim.x) >> 6;
     const int nitems = static_cast<int>(blockDim.x) * kRegItems;
-    const int base = wave * (kWave * kRegItems) + lane;
+    const int base4 = wave * (kWave * kRegItems) + lane * 4;
+    // block-local index of this thread's item j (group j / 4, element j % 4)
+    auto item = [&](int j) -> int { return base4 + (j >> 2) * (kWave * 4) + (j & 3); };
     const int kps = a.kp_shift;
     const int K = a.K;
 
@@ -179,12 +183,24 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         start = part * nitems;
         const float* src = a.scores + static_cast<int64_t>(row) * a.ld + start;
         const int lim = min(a.Lmax - start, nitems);
+        const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0u;
+        // items [i, i + 4) of the chunk, those at or past `bound` read as 0
+        auto load_group = [&](int g4, int bound) {
+            const int i = base4 + g4 * (kWave * 4);
+            if (vec && i + 3 < bound) {
+                const float4 t = *reinterpret_cast<const float4*>(src + i);
+                v[4 * g4] = t.x;
+                v[4 * g4 + 1] = t.y;
+                v[4 * g4 + 2] = t.z;
+                v[4 * g4 + 3] = t.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[4 * g4 + q] = i + q < bound ? src[i + q] : 0.0f;
+            }
+        };
         if (a.speculative) {
 #pragma unroll
-            for (int j = 0; j < kRegItems; ++j) {
-                const int i = base + kWave * j;
-                v[j] = i < lim ? src[i] : 0.0f;
-            }
+            for (int g4 = 0; g4 < kRegItems / 4; ++g4) load_group(g4, lim);
         }
         const int p = a.pos[row];
         const int n = (p >= 0 && p < a.Lmax) ? p + 1 : 0;
@@ -207,10 +223,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         }
         if (!a.speculative) {
 #pragma unroll
-            for (int j = 0; j < kRegItems; ++j) {
-                const int i = base + kWave * j;
-                v[j] = i < M ? src[i] : 0.0f;
-            }
+            for (int g4 = 0; g4 < kRegItems / 4; ++g4) load_group(g4, M);
         }
     } else {
         const int kpm = (1 << kps) - 1;
@@ -218,24 +231,53 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         const int nsl = min(nitems >> kps, a.in_lists - slot0);   // lists in the group
         cbase = (static_cast<int64_t>(row) * a.in_lists + slot0) << kps;
         const int32_t* cnt = a.in_cnt + static_cast<int64_t>(row) * a.in_lists + slot0;
+        // all loads first (keys, positions, list counts), then the valid
+        // bits. Lists of at least 4 entries keep a group of 4 in one list and
+        // 16-byte aligned (the workspace is 256-byte aligned).
+        int cj[kRegItems];
+        if (kps >= 2) {
 #pragma unroll
-        for (int j = 0; j < kRegItems; ++j) {
-            const int i = base + kWave * j;
-            const int s = i >> kps;
-            v[j] = 0.0f;
-            pv[j] = 0;
-            if (s < nsl) {
-                v[j] = a.in_key[cbase + i];
-                pv[j] = a.in_pos[cbase + i];
-                vmask |= (i & kpm) < cnt[s] ? (1u << j) : 0u;
+            for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
+                const int i = base4 + g4 * (kWave * 4);
+                const int s = i >> kps;
+                float4 kv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                int4 pq = make_int4(0, 0, 0, 0);
+                int c = 0;
+                if (s < nsl) {
+                    kv = *reinterpret_cast<const float4*>(a.in_key + cbase + i);
+                    pq = *reinterpret_cast<const int4*>(a.in_pos + cbase + i);
+                    c = cnt[s];
+                }
+                v[4 * g4] = kv.x;
+                v[4 * g4 + 1] = kv.y;
+                v[4 * g4 + 2] = kv.z;
+                v[4 * g4 + 3] = kv.w;
+                pv[4 * g4] = pq.x;
+                pv[4 * g4 + 1] = pq.y;
+                pv[4 * g4 + 2] = pq.z;
+                pv[4 * g4 + 3] = pq.w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cj[4 * g4 + q] = c;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kRegItems; ++j) {
+                const int i = item(j);
+                const int s = i >> kps;
+                const bool in = s < nsl;
+                v[j] = in ? a.in_key[cbase + i] : 0.0f;
+                pv[j] = in ? a.in_pos[cbase + i] : 0;
+                cj[j] = in ? cnt[s] : 0;
             }
         }
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) vmask |= (item(j) & kpm) < cj[j] ? (1u << j) : 0u;
     }
     // item j of this thread is valid: a prefix of the chunk (score source,
     // one compare against M) or the per-list counts (candidate source)
     auto valid = [&](int j) -> bool {
         if constexpr (CAND_IN) return (vmask >> j) & 1u;
-        else return base + kWave * j < M;
+        else return item(j) < M;
     };
     float vmin = INFINITY, vmax = -INFINITY;
 #pragma unroll
@@ -421,26 +463,52 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     if constexpr (CAND_OUT) ob = (static_cast<int64_t>(row) * a.nparts + part) << kps;
     else out = a.idx + static_cast<int64_t>(row) * K;
 #pragma unroll
-    for (int j = 0; j < kRegItems; ++j) {
-        const int i = base + kWave * j;
-        const bool eq = equal(j);
-        const uint64_t eqm = __ballot(eq);
-        const bool take = above(j) || (eq && e + lanes_below(eqm) < eq_take);
-        e += __popcll(eqm);
-        const uint64_t tm = __ballot(take);
-        const int slot = o + lanes_below(tm);
-        if (take && slot < keff) {
-            int32_t p;
-            if constexpr (CAND_IN) p = pv[j];
-            else p = start + i;
-            if constexpr (CAND_OUT) {
-                a.out_key[ob + slot] = v[j];
-                a.out_pos[ob + slot] = p;
-            } else {
-                out[slot] = p;
+    for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
+        bool tk[4], eqv[4];
+        int ne = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            tk[q] = above(4 * g4 + q);
+            eqv[q] = equal(4 * g4 + q);
+            ne += eqv[q] ? 1 : 0;
+        }
+        if (__ballot(ne > 0) != 0ull) {     // wave-uniform: ties at T are rare
+            // rank of each equal item among the equal items in item order
+            const int ein = wave_incl_scan_add(ne);
+            int er = e + ein - ne;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (eqv[q]) {
+                    tk[q] = er < eq_take;
+                    ++er;
+                }
+            }
+            e += __builtin_amdgcn_readlane(ein, 63);
+        }
+        int nt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nt += tk[q] ? 1 : 0;
+        const int tin = wave_incl_scan_add(nt);
+        int slot = o + tin - nt;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (tk[q]) {
+                if (slot < keff) {
+                    const int j = 4 * g4 + q;
+                    int32_t p;
+                    if constexpr (CAND_IN) p = pv[j];
+                    else p = start + item(j);
+                    if constexpr (CAND_OUT) {
+                        a.out_key[ob + slot] = v[j];
+                        a.out_pos[ob + slot] = p;
+                    } else {
+                        out[slot] = p;
+                    }
+                }
+                ++slot;
             }
         }
-        o += __popcll(tm);
+        o += __builtin_amdgcn_readlane(tin, 63);
     }
     if constexpr (CAND_OUT) {
         if (tid == 0) a.out_cnt[static_cast<int64_t>(row) * a.nparts + part] = keff;
