@@ -36,23 +36,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---- OCP E4M3 encoding (round to nearest even, saturating at 448) --------
-// Branch-free, on the bits of the float32 input. Normal outputs: adding
-// 0x7FFFF plus the lowest kept bit to the magnitude bits rounds the 23-bit
-// mantissa to 3 bits half-to-even (a carry bumps the exponent); shifting out
-// 20 bits and re-biasing the exponent from 127 to 7 gives the code, clamped
-// to 0x7E (448). Subnormal outputs (|v| < 2^-6) are multiples of 2^-9:
-// rint(|v| * 512), exact scaling, round half to even.
+// The code is the hardware conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950,
+// round to nearest even) of the input clamped to [-448, 448]. For every
+// float32 of magnitude at most 464 the hardware result equals the bit-level
+// definition: normal outputs round the 23-bit mantissa to 3 bits half-to-even
+// (a carry bumps the exponent) and re-bias the exponent from 127 to 7,
+// saturating at 0x7E (448); outputs below 2^-6 are the subnormal multiples
+// of 2^-9, rint(|v| * 512); the sign is kept (checked exhaustively on the
+// device). The clamp supplies the saturation above 448.
+__device__ __forceinline__ float e4m3_clamp(float v) {
+    return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
 __device__ __forceinline__ uint8_t e4m3_encode(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t ua = u & 0x7FFFFFFFu;
-    const float a = __uint_as_float(ua);
-    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-    int32_t cn = static_cast<int32_t>(r >> 20) - (120 << 3);
-    cn = cn < 0x7E ? cn : 0x7E;
-    const uint32_t cs = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-    const uint32_t code = a < 0.015625f ? cs : static_cast<uint32_t>(cn);
-    return static_cast<uint8_t>(sign | code);
+    const float c = e4m3_clamp(v);
+    return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFF);
+}
+
+// Four codes packed little-endian into one word (two conversions).
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return static_cast<uint32_t>(w);
 }
 
 // ---- wave reductions (wave64) ---------------------------------------------

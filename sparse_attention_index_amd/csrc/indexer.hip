@@ -586,10 +586,8 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
         uint32_t pk[kFPT / 4];
 #pragma unroll
         for (int i = 0; i < kFPT / 4; ++i) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                word |= static_cast<uint32_t>(e4m3_encode(v[4 * i + q] / scale)) << (8 * q);
+            const uint32_t word = e4m3_encode4(v[4 * i] / scale, v[4 * i + 1] / scale,
+                                               v[4 * i + 2] / scale, v[4 * i + 3] / scale);
             pk[i] = hh < H ? word : 0u;
         }
         // parts e < TPH/2: bytes [j0, j0 + FPT/2) and [32 + j0, ...); others [f0, f0 + FPT)

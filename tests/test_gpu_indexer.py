@@ -154,6 +154,60 @@ def test_indexer_zero_and_extreme_rows():
     check_scores(host(sc)[:, 0], o[:, 0], pos[:, 0] + 1, "extreme")
 
 
+def e4m3_boundary_rows():
+    """float32 rows [n, 128] whose features 1..127 run through every finite
+    E4M3 value, every midpoint between neighbouring values (ties to even),
+    the float32 values one ulp either side of each midpoint, zeros and
+    float32 subnormals, both signs; feature 0 is 448, so the block scale is
+    448 / 448 = 1 and each code is the E4M3 rounding of the value itself."""
+    vals = oracle.e4m3_decode(np.arange(128, dtype=np.uint8)).astype(np.float32)
+    vals = np.unique(vals[np.isfinite(vals)])                      # 0 .. 448
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    extra = np.array([1e-40, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9, 447.99997], np.float32)
+    pos_vals = np.concatenate([vals, mids, near, extra]).astype(np.float32)
+    pos_vals = pos_vals[pos_vals <= 448]
+    allv = np.concatenate([pos_vals, -pos_vals, np.array([-0.0], np.float32)])
+    n = (allv.size + 126) // 127
+    rows = np.zeros((n, 128), np.float32)
+    rows[:, 0] = 448.0
+    flat = rows[:, 1:].reshape(-1)
+    flat[:allv.size] = allv
+    rows[:, 1:] = flat.reshape(n, 127)
+    return rows
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_fp8_codes_at_rounding_boundaries(S):
+    """The E4M3 encoder of the key append (every S) and of the query
+    preparation (fused decode kernel at S = 1, row preparation at S = 2)
+    against the oracle's codec, at position 0 where RoPE is the identity."""
+    import torch
+    rows = e4m3_boundary_rows()
+    n = rows.shape[0]
+    cos, sin = oracle.rope_table(4)
+    # keys: n batch rows appended at position 0
+    kc = torch.zeros((n, 4, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((n, 4), dtype=torch.float32, device="cuda")
+    dsa.indexer_append(dev(rows[:, None]), dev(np.zeros((n, 1), np.int32)), dev(cos), dev(sin),
+                       kc, ks)
+    ok8, oks, _ = oracle.indexer_prepare(rows, np.zeros(n, np.int32), cos, sin, False)
+    assert np.all(oks == 1.0)
+    assert np.array_equal(host(kc)[:, 0], ok8) and np.array_equal(host(ks)[:, 0], oks)
+    # queries: the rows as heads of S query rows at position 0
+    H = 64
+    reps = (S * H + n - 1) // n
+    q_rows = np.tile(rows, (reps, 1))[:S * H].reshape(1, S, H, 128)
+    w = np.ones((1, S, H), np.float32)
+    q8 = torch.empty((1, S, H, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((1, S, H), dtype=torch.float32, device="cuda")
+    dsa.indexer(dev(q_rows), dev(w), dev(np.zeros((1, S), np.int32)), dev(cos), dev(sin),
+                kc[:1], ks[:1], q_fp8=q8, q_scale=qs)
+    torch.cuda.synchronize()
+    oq8, oqs, _ = oracle.indexer_prepare(q_rows, np.zeros((1, S, H), np.int32), cos, sin, False)
+    assert np.array_equal(host(q8), oq8) and np.array_equal(host(qs), oqs)
+
+
 def test_positions_out_of_range_are_skipped():
     import torch
     B, S, H, Lmax = 2, 1, 8, 128

@@ -58,6 +58,11 @@ CASES = [
     ("heads20", 1, 2, 20, 900, 256, 900, 0.2),
     ("heads1", 1, 1, 1, 500, 64, 500, 0.1),
     ("prefill-rows", 1, 300, 128, 600, 256, 600, 0.4),
+    # long selections over more blocks than CUs (whole rows; a partial head
+    # group; two splits per row with merge)
+    ("long-rows", 1, 300, 128, 1200, 1024, 1200, 0.6),
+    ("long-heads80", 1, 272, 80, 700, 512, 700, 0.5),
+    ("long-split", 1, 130, 128, 2500, 2048, 2500, 0.9),
 ]
 
 
