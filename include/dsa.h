@@ -157,6 +157,8 @@ dsa_status dsa_rope_table(const dsa_rope_table_args* args, hipStream_t stream);
  *   q_fp8   [B][S][H][128] uint8 (out, optional)
  *   q_scale [B][S][H] float32 (out, optional; given iff q_fp8 is)
  *   scores  row r at scores + r*ld_scores, float32, ld_scores >= Lmax
+ * Alignment: q_raw, k_raw, k_cache, q_fp8, rope_cos and rope_sin 16 bytes;
+ * the other arrays 4.
  * Limits: 1 <= H <= 64, B, S >= 1, 1 <= Lmax, P >= 1. A row whose position
  * lies outside [0, min(Lmax, P)) is skipped (nothing appended or scored).
  * With S > 1 every row's key is appended before any row is scored, so a

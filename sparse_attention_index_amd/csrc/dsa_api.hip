@@ -91,7 +91,6 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
     if (a->act_dtype != DSA_DTYPE_F32 && a->act_dtype != DSA_DTYPE_BF16) return DSA_ERR_UNSUPPORTED;
     if ((a->flags & ~(DSA_INDEXER_APPEND_ONLY | DSA_INDEXER_HADAMARD | DSA_INDEXER_POW2_SCALE)) != 0)
         return DSA_ERR_UNSUPPORTED;
-    const size_t esz = a->act_dtype == DSA_DTYPE_BF16 ? 2 : 4;
     const bool append_only = (a->flags & DSA_INDEXER_APPEND_ONLY) != 0;
     if (!a->pos || !a->rope_cos || !a->rope_sin || !a->k_cache || !a->k_scale) return DSA_ERR_NULL;
     if (append_only) {
@@ -100,10 +99,10 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
         if (!a->q_raw || !a->w || !a->scores) return DSA_ERR_NULL;
         if ((a->q_fp8 == nullptr) != (a->q_scale == nullptr)) return DSA_ERR_NULL;
     }
-    const uintptr_t amask = esz - 1;
+    const uintptr_t amask = 15;                     // activation rows are read 16 bytes at a time
     if (!aligned16(a->k_cache) || (reinterpret_cast<uintptr_t>(a->k_raw) & amask) ||
-        !aligned4(a->k_scale) || !aligned4(a->pos) || !aligned4(a->rope_cos) ||
-        !aligned4(a->rope_sin))
+        !aligned4(a->k_scale) || !aligned4(a->pos) || !aligned16(a->rope_cos) ||
+        !aligned16(a->rope_sin))
         return DSA_ERR_ALIGN;
     if (!append_only &&
         ((reinterpret_cast<uintptr_t>(a->q_raw) & amask) || (a->q_fp8 && !aligned16(a->q_fp8)) ||

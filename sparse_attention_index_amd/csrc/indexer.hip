@@ -26,18 +26,21 @@ namespace dsa {
 
 // ---------------------------------------------------------------------------
 // prepare: RoPE (non-interleaved, first 64 features) + cast + block FP8.
-// Lane l holds features l and l+64 of its row; the rotation pairs feature j
-// (lane j) with j+32 (lane j+32), exchanged with one cross-lane swap. Each
-// wave handles kPrepRows consecutive rows and issues all their loads (pos,
-// then table entries and inputs) together, so the dependent global round
-// trips are paid once per kPrepRows rows.
+// Lane l of a wave holds features [8c, 8c + 8), c = l % 16, of row l / 16 of
+// a group of four rows (16-byte loads, 8-byte code stores). The rotation
+// pairs feature j (chunk c < 4) with j + 32 (chunk c + 4): partner lanes
+// differ by 4. The row's amax is reduced over its 16 lanes. Each wave handles
+// kPrepGroups groups and issues all their loads (pos, then table entries and
+// inputs) together, so the dependent global round trips are paid once per
+// 4 kPrepGroups rows.
 // Options: `had` replaces the rotated row by H_128 x / sqrt(128) (fast
-// Walsh-Hadamard transform in float32, butterfly strides 1..32 across lanes
-// and 64 inside the lane, then a multiplication by fl32(128^-0.5), rounded
-// to the activation dtype); `pow2` rounds the block scale up to a power of
-// two.
+// Walsh-Hadamard transform in float32, butterfly strides 1, 2, 4 inside the
+// lane and 8 .. 64 across lanes, in that order, then a multiplication by
+// fl32(128^-0.5), rounded to the activation dtype); `pow2` rounds the block
+// scale up to a power of two.
 // ---------------------------------------------------------------------------
-constexpr int kPrepRows = 8;
+constexpr int kPrepGroups = 2;
+constexpr int kPrepRowsPerWave = 4 * kPrepGroups;
 constexpr float kInvSqrt128 = 0.088388347648318440550f;   // fl32(128^-0.5)
 
 // smallest power of two >= v (v > 0, finite)
@@ -52,13 +55,28 @@ __device__ __forceinline__ float pow2_ceil(float v) {
     return __uint_as_float(u);
 }
 
-// one stride of the Walsh-Hadamard butterfly on features lane (a) and
-// lane + 64 (c): (x[i], x[i+s]) -> (x[i] + x[i+s], x[i] - x[i+s])
-__device__ __forceinline__ void wht_step(float& a, float& c, int lane, int s) {
-    const float pa = __shfl_xor(a, s), pc = __shfl_xor(c, s);
-    const bool upper = (lane & s) != 0;
-    a = upper ? pa - a : a + pa;
-    c = upper ? pc - c : c + pc;
+// one butterfly stride s (a lane-index bit: features differ by 8 s) of the
+// Walsh-Hadamard transform across lanes: (x[i], x[i+s]) -> (x[i] + x[i+s],
+// x[i] - x[i+s])
+__device__ __forceinline__ void wht_lanes(float (&y)[8], int c, int s) {
+    const bool upper = (c & s) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float pa = __shfl_xor(y[e], s);
+        y[e] = upper ? pa - y[e] : y[e] + pa;
+    }
+}
+
+// the same inside the lane for strides 1, 2, 4 of the feature index
+__device__ __forceinline__ void wht_lane(float (&y)[8], int s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if ((e & s) == 0) {
+            const float lo = y[e], hi = y[e + s];
+            y[e] = lo + hi;
+            y[e + s] = lo - hi;
+        }
+    }
 }
 
 template <bool BF16_IN, bool TO_CACHE>
@@ -67,87 +85,112 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, uint8_t* __restrict__ codes_out,
     float* __restrict__ scales_out, int had, int pow2, CacheMap cmap) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRows;
+    const int lane = threadIdx.x & 63, c = lane & 15, rsub = lane >> 4;
+    const int64_t row0 =
+        (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kPrepRowsPerWave;
     if (row0 >= nrows) return;
-    const int j = lane & 31;
+    const bool rotary = c < 8;
+    const int j0 = 8 * (c & 3);                    // rotary pair index of element 0
 
-    int p[kPrepRows];
-    float x0[kPrepRows], x1[kPrepRows];
+    int p[kPrepGroups];
+    float xv[kPrepGroups][8];
 #pragma unroll
-    for (int k = 0; k < kPrepRows; ++k) {
-        const int64_t row = row0 + k;
+    for (int gi = 0; gi < kPrepGroups; ++gi) {
+        const int64_t row = row0 + 4 * gi + rsub;
         const bool ok = row < nrows;
-        p[k] = ok ? pos[row / rows_per_pos] : -1;
+        p[gi] = ok ? pos[row / rows_per_pos] : -1;
+        const int64_t rr = ok ? row : 0;
         if (BF16_IN) {
-            const uint16_t* xr = static_cast<const uint16_t*>(x) + (ok ? row : 0) * 128;
-            x0[k] = bf16_bits_to_float(xr[lane]);
-            x1[k] = bf16_bits_to_float(xr[lane + 64]);
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) +
+                                                            rr * 128 + 8 * c);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xv[gi][2 * e] = __uint_as_float(w4[e] << 16);
+                xv[gi][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+            }
         } else {
-            const float* xr = static_cast<const float*>(x) + (ok ? row : 0) * 128;
-            x0[k] = xr[lane];
-            x1[k] = xr[lane + 64];
+            const float4* src =
+                reinterpret_cast<const float4*>(static_cast<const float*>(x) + rr * 128 + 8 * c);
+            const float4 a = src[0], bq = src[1];
+            xv[gi][0] = a.x; xv[gi][1] = a.y; xv[gi][2] = a.z; xv[gi][3] = a.w;
+            xv[gi][4] = bq.x; xv[gi][5] = bq.y; xv[gi][6] = bq.z; xv[gi][7] = bq.w;
         }
     }
-    float cs[kPrepRows], sn[kPrepRows];
+    float cs[kPrepGroups][8], sn[kPrepGroups][8];
 #pragma unroll
-    for (int k = 0; k < kPrepRows; ++k) {
-        const bool ok = p[k] >= 0 && p[k] < Lmax && p[k] < P;
-        const int64_t pe = ok ? p[k] : 0;
-        cs[k] = cos_t[pe * 32 + j];
-        sn[k] = sin_t[pe * 32 + j];
+    for (int gi = 0; gi < kPrepGroups; ++gi) {
+        const bool ok = p[gi] >= 0 && p[gi] < Lmax && p[gi] < P;
+        const int64_t pe = ok ? p[gi] : 0;
+        const float4* ct = reinterpret_cast<const float4*>(cos_t + pe * 32 + j0);
+        const float4* st = reinterpret_cast<const float4*>(sin_t + pe * 32 + j0);
+        float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0, s0 = c0, s1 = c0;
+        if (rotary) {
+            c0 = ct[0]; c1 = ct[1];
+            s0 = st[0]; s1 = st[1];
+        }
+        cs[gi][0] = c0.x; cs[gi][1] = c0.y; cs[gi][2] = c0.z; cs[gi][3] = c0.w;
+        cs[gi][4] = c1.x; cs[gi][5] = c1.y; cs[gi][6] = c1.z; cs[gi][7] = c1.w;
+        sn[gi][0] = s0.x; sn[gi][1] = s0.y; sn[gi][2] = s0.z; sn[gi][3] = s0.w;
+        sn[gi][4] = s1.x; sn[gi][5] = s1.y; sn[gi][6] = s1.z; sn[gi][7] = s1.w;
     }
 #pragma unroll
-    for (int k = 0; k < kPrepRows; ++k) {
-        const int64_t row = row0 + k;
-        if (row >= nrows) break;                   // wave-uniform
-        if (!(p[k] >= 0 && p[k] < Lmax && p[k] < P)) continue;
-        const float other = __shfl_xor(x0[k], 32);
-        float y0;
+    for (int gi = 0; gi < kPrepGroups; ++gi) {
+        const int64_t row = row0 + 4 * gi + rsub;
+        if (row0 + 4 * gi >= nrows) break;         // wave-uniform
+        const bool ok = row < nrows && p[gi] >= 0 && p[gi] < Lmax && p[gi] < P;
+        float y[8];
         {
 #pragma clang fp contract(off)
             // pair (a, b) = (x[j], x[j+32]):  a' = a c - b s,  b' = a s + b c
-            if (lane < 32) {
-                const float ac = x0[k] * cs[k], bs = other * sn[k];
-                y0 = ac - bs;
-            } else {
-                const float as = other * sn[k], bc = x0[k] * cs[k];
-                y0 = as + bc;
-            }
-        }
-        if (BF16_IN) y0 = bf16_bits_to_float(float_to_bf16_bits(y0));   // cast back to bf16
-        float y1 = x1[k];
-        if (had) {
 #pragma unroll
-            for (int st = 1; st < 64; st <<= 1) wht_step(y0, y1, lane, st);
-            const float t = y0 + y1;
-            y1 = y0 - y1;
-            y0 = t * kInvSqrt128;
-            y1 = y1 * kInvSqrt128;
-            if (BF16_IN) {
-                y0 = bf16_bits_to_float(float_to_bf16_bits(y0));
-                y1 = bf16_bits_to_float(float_to_bf16_bits(y1));
+            for (int e = 0; e < 8; ++e) {
+                const float other = __shfl_xor(xv[gi][e], 4);
+                float r;
+                if (c < 4) {
+                    const float ac = xv[gi][e] * cs[gi][e], bs = other * sn[gi][e];
+                    r = ac - bs;
+                } else {
+                    const float as = other * sn[gi][e], bc = xv[gi][e] * cs[gi][e];
+                    r = as + bc;
+                }
+                if (BF16_IN) r = bf16_bits_to_float(float_to_bf16_bits(r));   // cast back
+                y[e] = rotary ? r : xv[gi][e];
             }
         }
-
-        const float amax = wave_max_dpp(fmaxf(fabsf(y0), fabsf(y1)));
+        if (had) {
+            wht_lane(y, 1);
+            wht_lane(y, 2);
+            wht_lane(y, 4);
+#pragma unroll
+            for (int st = 1; st < 16; st <<= 1) wht_lanes(y, c, st);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                y[e] = y[e] * kInvSqrt128;
+                if (BF16_IN) y[e] = bf16_bits_to_float(float_to_bf16_bits(y[e]));
+            }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
         float scale = amax / 448.0f;
         if (pow2) scale = scale > 0.0f ? pow2_ceil(scale) : 1.0f;
         else if (!(scale > 0.0f)) scale = 1.0f;
-        const uint8_t c0 = e4m3_encode(y0 / scale);
-        const uint8_t c1 = e4m3_encode(y1 / scale);
-
+        const uint32_t w0 = e4m3_encode4(y[0] / scale, y[1] / scale, y[2] / scale, y[3] / scale);
+        const uint32_t w1 = e4m3_encode4(y[4] / scale, y[5] / scale, y[6] / scale, y[7] / scale);
+        if (!ok) continue;
         int64_t dst;
         if (TO_CACHE) {
             const int64_t b = (row / rows_per_pos) / S;
-            dst = cmap.row(b, p[k]);
+            dst = cmap.row(b, p[gi]);
             if (dst < 0) continue;                  // page not present: nothing to write
         } else {
             dst = row;
         }
-        codes_out[dst * 128 + lane] = c0;
-        codes_out[dst * 128 + lane + 64] = c1;
-        if (lane == 0) scales_out[dst] = scale;
+        *reinterpret_cast<uint2*>(codes_out + dst * 128 + 8 * c) = make_uint2(w0, w1);
+        if (c == 0) scales_out[dst] = scale;
     }
 }
 
@@ -156,7 +199,7 @@ hipError_t launch_prepare(bool bf16_in, bool to_cache, int64_t nrows, int rows_p
                           const float* sin_t, uint8_t* codes, float* scales, bool hadamard,
                           bool pow2, CacheMap cmap, hipStream_t stream) {
     if (nrows <= 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((nrows + 4 * kPrepRows - 1) / (4 * kPrepRows))),
+    const dim3 grid(static_cast<unsigned>((nrows + 4 * kPrepRowsPerWave - 1) / (4 * kPrepRowsPerWave))),
         block(256);
 #define DSA_PREP(B, C)                                                                         \
     hipLaunchKernelGGL((prepare_rows_kernel<B, C>), grid, block, 0, stream, nrows, rows_per_pos, \
@@ -333,13 +376,14 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
     __syncthreads();
     if (k0 >= s_maxnv) return;                         // tile wholly past every causal end
 
-    // per-head query weights
+    // per-head query weights, halved: the epilogue adds w' (s + |s|), which
+    // is w q_scale ReLU(s) exactly
     for (int i = tid; i < 64 * kQT; i += 256) {
         const int h = i / kQT, qi = i - h * kQT;
         float v = 0.0f;
         if (h < H && t0 + qi < S) {
             const int64_t r = row0 + qi;
-            v = w[r * H + h] * qscale[r * H + h];
+            v = 0.5f * (w[r * H + h] * qscale[r * H + h]);
         }
         wqs[h][qi] = v;
     }
@@ -416,8 +460,10 @@ __global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int kt2 = 0; kt2 < kKW; ++kt2)
-                    I[kt2][4 * r + c] += wr[c] * fmaxf(sacc[kt2][4 * r + c], 0.0f);
+                for (int kt2 = 0; kt2 < kKW; ++kt2) {
+                    const float sv = sacc[kt2][4 * r + c];
+                    I[kt2][4 * r + c] = fmaf(wr[c], sv + fabsf(sv), I[kt2][4 * r + c]);
+                }
         }
     }
 

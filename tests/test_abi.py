@@ -95,7 +95,8 @@ def test_indexer_validation():
     cases = [
         (dict(H=65), 2), (dict(H=0), 2), (dict(B=0), 2), (dict(Lmax=0), 2), (dict(P=0), 2),
         (dict(ld_scores=100), 2), (dict(act_dtype=7), 3), (dict(flags=8), 3),
-        (dict(flags=1, k_raw=None), 1), (dict(flags=1, k_raw=FAKE + 1), 5),
+        (dict(flags=1, k_raw=None), 1), (dict(flags=1, k_raw=FAKE + 1), 5), (dict(k_raw=FAKE + 8), 5),
+        (dict(q_raw=FAKE + 4), 5), (dict(rope_sin=FAKE + 4), 5),
         (dict(q_raw=None), 1), (dict(scores=None), 1), (dict(q_scale=None), 1),
         (dict(k_cache=FAKE + 8), 5), (dict(B=300, S=300), 2),
     ]
