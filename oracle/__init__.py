@@ -54,6 +54,8 @@ def _load():
                                   _ptr, _f64, _ptr, _ptr]),
         "orc_mla_mha": (None, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _ptr,
                                _ptr, _ptr, _ptr, _ptr, _f64, _ptr]),
+        "orc_sparse_mha": (None, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _ptr,
+                                  _ptr, _ptr, _ptr, _f64, _ptr]),
         "orc_num_threads": (_i32, []),
     }
     for name, (res, args) in sigs.items():
@@ -265,6 +267,72 @@ def mla_mha(q_nope, q_pe, wkv_b, latent, kpe, idx, scale):
     _load().orc_mla_mha(B, S, Hq, Dn, Dv, Dl, Dr, Lmax, K, _p(qn), _p(qp), _p(W), _p(lat),
                         _p(pe), _p(ix), float(scale), _p(out))
     return out
+
+
+def sparse_mha(q, kv, kpe, idx, scale, pos=None, Dn=128):
+    """Multi-head prefill attention over up-projected keys and values (page
+    "RoPE coefficients", MLA prefill excerpt): q [B,S,Hq,Dn+Dr] (q_nope then
+    q_pe), kv [B,Lmax,Hq,Dn+Dv] (k_nope then v), kpe [B,Lmax,Dr], idx [B,S,K];
+    the selection is a set and, with pos [B,S], causally masked.
+    Returns float64 [B,S,Hq,Dv]."""
+    qq = _c(q, np.float64)
+    kk = _c(kv, np.float64)
+    pe = _c(kpe, np.float64)
+    ix = _c(idx, np.int32)
+    B, S, Hq, Dq = qq.shape
+    Lmax, Dkv = kk.shape[1], kk.shape[3]
+    Dr = pe.shape[2]
+    Dv = Dkv - Dn
+    K = ix.shape[-1]
+    assert Dq == Dn + Dr and kk.shape[:3] == (B, Lmax, Hq) and pe.shape[:2] == (B, Lmax)
+    assert ix.shape == (B, S, K)
+    pp = None if pos is None else _c(np.broadcast_to(pos, (B, S)), np.int32)
+    out = np.empty((B, S, Hq, Dv), np.float64)
+    _load().orc_sparse_mha(B, S, Hq, Dn, Dv, Dr, Lmax, K, _p(qq), _p(kk), _p(pe), _p(ix),
+                           None if pp is None else _p(pp), float(scale), _p(out))
+    return out
+
+
+# ----------------------------------------------------------- projections --
+# wkv_b [Hq, Dn+Dv, Dl]: rows 0..Dn-1 of head h are W_UK (keys' non-rotary
+# part), rows Dn.. are W_UV (values). Plain float64 matrix products.
+
+def kv_up(latent, wkv_b):
+    """Up-projection of the MLA prefill excerpt (page "RoPE coefficients"):
+    kv = wkv_b(latent) viewed as [.., Hq, Dn+Dv]. latent [B,L,Dl] ->
+    float64 [B,L,Hq,Dn+Dv]."""
+    lat = _c(latent, np.float64)
+    W = _c(wkv_b, np.float64)
+    Hq, Dkv, Dl = W.shape
+    B, L, _ = lat.shape
+    y = lat.reshape(B * L, Dl) @ W.reshape(Hq * Dkv, Dl).T
+    return y.reshape(B, L, Hq, Dkv)
+
+
+def absorb_q(q_nope, wkv_b, Dn=128):
+    """Query absorption of the MQA decode excerpt (page "Similarities"):
+    q_lat[..., h, c] = sum_d q_nope[..., h, d] W_UK[h][d][c].
+    q_nope [..., Hq, Dn] -> float64 [..., Hq, Dl]."""
+    qn = _c(q_nope, np.float64)
+    W = _c(wkv_b, np.float64)[:, :Dn]                     # [Hq, Dn, Dl]
+    lead = qn.shape[:-2]
+    Hq = qn.shape[-2]
+    x = qn.reshape(-1, Hq, Dn).transpose(1, 0, 2)         # [Hq, R, Dn]
+    y = np.matmul(x, W)                                   # [Hq, R, Dl]
+    return y.transpose(1, 0, 2).reshape(lead + (Hq, W.shape[2]))
+
+
+def absorb_o(x_lat, wkv_b, Dn=128):
+    """Output absorption of the MQA decode excerpt (page "Similarities"):
+    o[..., h, d] = sum_c x[..., h, c] W_UV[h][d][c].
+    x_lat [..., Hq, Dl] -> float64 [..., Hq, Dv]."""
+    xx = _c(x_lat, np.float64)
+    W = _c(wkv_b, np.float64)[:, Dn:]                     # [Hq, Dv, Dl]
+    lead = xx.shape[:-2]
+    Hq, Dl = xx.shape[-2:]
+    x = xx.reshape(-1, Hq, Dl).transpose(1, 0, 2)         # [Hq, R, Dl]
+    y = np.matmul(x, W.transpose(0, 2, 1))                # [Hq, R, Dv]
+    return y.transpose(1, 0, 2).reshape(lead + (Hq, W.shape[1]))
 
 
 # ------------------------------------------------------------ whole path --

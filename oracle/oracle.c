@@ -571,3 +571,72 @@ void orc_mla_mha(int B, int S, int Hq, int Dn, int Dv, int Dl, int Dr, int Lmax,
         free(v);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * Multi-head (non-absorbed) prefill attention over per-head keys and values
+ * that are already up-projected [P2 MLA prefill excerpt: k = [k_nope ;
+ * k_pe broadcast over heads], scores = q . k * softmax_scale, plus the index
+ * mask (0 at the selected positions, -inf elsewhere, built by scattering the
+ * top-k list) and the causal mask, softmax over positions, scores . v].
+ * The selection is a set, as the scattered mask makes it: a position listed
+ * twice counts once. Position p of row r = (b, s) takes part iff it appears in
+ * idx[r], 0 <= p < Lmax, and (when pos is given) p <= pos[r]. A row with no
+ * such position gives out = 0.
+ * q [B][S][Hq][Dn+Dr] (q_nope then q_pe), kv [B][Lmax][Hq][Dn+Dv] (k_nope
+ * then v), kpe [B][Lmax][Dr], idx [B][S][K], pos [B][S] or NULL,
+ * out [B][S][Hq][Dv].
+ * Pinned by: with kv from the up-projection it equals orc_mla_mha (which
+ * equals the absorbed form, itself pinned to PyTorch's attention); masking
+ * by position against a dense masked softmax written with PyTorch.
+ * ---------------------------------------------------------------------- */
+void orc_sparse_mha(int B, int S, int Hq, int Dn, int Dv, int Dr, int Lmax, int K,
+                    const double* q, const double* kv, const double* kpe,
+                    const int32_t* idx, const int32_t* pos, double scale, double* out) {
+    int64_t r, nrows = (int64_t)B * S;
+    const int Dq = Dn + Dr, Dkv = Dn + Dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < nrows; ++r) {
+        int64_t b = r / S;
+        const int32_t* sel = idx + r * K;
+        unsigned char* in_mask = (unsigned char*)calloc((size_t)Lmax, 1);
+        double* z = (double*)malloc(sizeof(double) * (size_t)Lmax);
+        int j, p, h, d;
+        for (j = 0; j < K; ++j) {
+            p = sel[j];
+            if (p < 0 || p >= Lmax) continue;
+            if (pos != NULL && p > pos[r]) continue;
+            in_mask[p] = 1;
+        }
+        for (h = 0; h < Hq; ++h) {
+            const double* qh = q + (r * Hq + h) * Dq;
+            double* o = out + (r * Hq + h) * Dv;
+            double m = -INFINITY, l = 0.0;
+            for (p = 0; p < Lmax; ++p) {
+                const double* kh;
+                const double* pe;
+                double dot = 0.0;
+                if (!in_mask[p]) continue;
+                kh = kv + ((b * Lmax + p) * Hq + h) * Dkv;
+                pe = kpe + (b * Lmax + p) * Dr;
+                for (d = 0; d < Dn; ++d) dot += qh[d] * kh[d];
+                for (d = 0; d < Dr; ++d) dot += qh[Dn + d] * pe[d];
+                z[p] = scale * dot;
+                if (z[p] > m) m = z[p];
+            }
+            for (d = 0; d < Dv; ++d) o[d] = 0.0;
+            if (m == -INFINITY) continue;
+            for (p = 0; p < Lmax; ++p) {
+                const double* vh;
+                double w;
+                if (!in_mask[p]) continue;
+                vh = kv + ((b * Lmax + p) * Hq + h) * Dkv + Dn;
+                w = exp(z[p] - m);
+                l += w;
+                for (d = 0; d < Dv; ++d) o[d] += w * vh[d];
+            }
+            for (d = 0; d < Dv; ++d) o[d] /= l;
+        }
+        free(z);
+        free(in_mask);
+    }
+}

@@ -102,6 +102,15 @@ void orc_mla_mha(int B, int S, int Hq, int Dn, int Dv, int Dl, int Dr, int Lmax,
                  const double* wkv_b, const double* latent, const double* kpe,
                  const int32_t* idx, double scale, double* out);
 
+/* Multi-head prefill attention over up-projected per-head keys and values,
+ * the selection taken as a set (a repeated position counts once) and, when
+ * pos is given, causally masked (p <= pos[r]):
+ *   z = scale * (q[r][h][0:Dn] . kv[b][p][h][0:Dn] + q[r][h][Dn:] . kpe[b][p]),
+ * out[r][h] = sum softmax * kv[b][p][h][Dn:Dn+Dv]; empty rows give 0. */
+void orc_sparse_mha(int B, int S, int Hq, int Dn, int Dv, int Dr, int Lmax, int K,
+                    const double* q, const double* kv, const double* kpe,
+                    const int32_t* idx, const int32_t* pos, double scale, double* out);
+
 int orc_num_threads(void);
 
 #ifdef __cplusplus

@@ -43,10 +43,68 @@ def test_absorbed_equals_non_absorbed():
     idx = synth.random_selection(9, B * S, K, [200, 150], fill=0.3).reshape(B, S, K)
     scale = 192 ** -0.5
     mha = oracle.mla_mha(q_nope, q_pe, W, lat, pe, idx, scale)
-    q_abs = np.einsum("bshd,hdc->bshc", q_nope, W[:, :Dn])
+    q_abs = oracle.absorb_q(q_nope, W)
     x, _ = oracle.sparse_mla(np.concatenate([q_abs, q_pe], -1), lat, pe, idx, scale)
-    absorbed = np.einsum("bshc,hdc->bshd", x, W[:, Dn:])
+    absorbed = oracle.absorb_o(x, W)
     assert np.allclose(absorbed, mha, rtol=1e-10, atol=1e-12)
+    # the same through einsum, so that a wrong slice or transpose inside the
+    # absorption helpers fails here even where the two forms would agree
+    assert np.allclose(q_abs, np.einsum("bshd,hdc->bshc", q_nope, W[:, :Dn]), rtol=1e-12)
+    assert np.allclose(absorbed, np.einsum("bshc,hdc->bshd", x, W[:, Dn:]), rtol=1e-12)
+    # the multi-head form on the up-projected keys and values is the same
+    # attention (selection distinct and inside the causal range)
+    kv = oracle.kv_up(lat, W)
+    pos = np.array([[199, 149]], np.int32)
+    mha2 = oracle.sparse_mha(np.concatenate([q_nope, q_pe], -1), kv, pe, idx, scale, pos=pos)
+    assert np.allclose(mha2, mha, rtol=1e-10, atol=1e-12)
+
+
+def test_kv_up_is_the_linear_layer_split_per_head():
+    # The pages apply wkv_b as a linear layer and view its output as
+    # [.., heads, k_nope + v]; PyTorch's linear computes the same product.
+    B, L, Hq, Dl = 2, 7, 3, 512
+    lat, W = rand(40, B, L, Dl), rand(41, Hq, 256, Dl)
+    ref = torch.nn.functional.linear(torch.from_numpy(lat),
+                                     torch.from_numpy(W.reshape(Hq * 256, Dl)))
+    kv = oracle.kv_up(lat, W)
+    assert np.allclose(kv, ref.view(B, L, Hq, 256).numpy(), rtol=1e-12, atol=1e-12)
+    # head 1, position 4: k_nope is W_UK[1] c, v is W_UV[1] c
+    assert np.allclose(kv[1, 4, 1, :128], W[1, :128] @ lat[1, 4], rtol=1e-12)
+    assert np.allclose(kv[1, 4, 1, 128:], W[1, 128:] @ lat[1, 4], rtol=1e-12)
+
+
+def test_mha_equals_dense_masked_softmax():
+    # The MLA prefill excerpt's own formulation: scores over every position,
+    # an index mask scattered from the top-k list (repeats collapse), plus the
+    # causal mask, softmax, product with v. Written with PyTorch in float64.
+    B, S, Hq, L, K = 2, 5, 3, 40, 12
+    q, kv, pe = rand(42, B, S, Hq, 192), rand(43, B, L, Hq, 256), rand(44, B, L, 64)
+    g = np.random.Generator(np.random.PCG64(45))
+    idx = g.integers(-1, L, size=(B, S, K)).astype(np.int32)
+    idx[0, 1, :4] = 7                                 # a repeated position
+    idx[0, 0, 0], idx[1, 2, 0] = 3, 5                 # positions equal to pos (kept)
+    idx[0, 0, 1], idx[1, 2, 1] = 4, 6                 # one past pos (masked)
+    pos = np.array([[3, 10, 39, 25, 0], [39, 17, 5, 30, 12]], np.int32)
+    scale = 0.09
+    out = oracle.sparse_mha(q, kv, pe, idx, scale, pos=pos)
+    qt, kvt, pet = map(torch.from_numpy, (q, kv, pe))
+    k = torch.cat([kvt[..., :128], pet[:, :, None].expand(B, L, Hq, 64)], -1)
+    scores = torch.einsum("bshd,bthd->bsht", qt, k) * scale
+    idx_t = torch.from_numpy(idx.astype(np.int64))
+    index_mask = torch.full((B, S, L + 1), float("-inf"), dtype=torch.float64)
+    index_mask.scatter_(-1, torch.where(idx_t < 0, L, idx_t), 0.0)   # -1 -> spare column
+    index_mask = index_mask[..., :L]
+    causal = torch.where(torch.arange(L)[None, None] <= torch.from_numpy(pos)[..., None], 0.0,
+                         float("-inf")).to(torch.float64)
+    scores = scores + (index_mask + causal)[:, :, None]
+    ref = torch.einsum("bsht,bthd->bshd", scores.softmax(-1), kvt[..., 128:]).numpy()
+    live = np.isfinite(scores.numpy()).any(-1)                     # [B,S,Hq]
+    assert np.allclose(out[live], ref[live], rtol=1e-12, atol=1e-12)
+    assert np.all(out[~live] == 0)
+    assert (~live).any() and live.any()
+    # without positions the causal mask is off
+    out_nc = oracle.sparse_mha(q, kv, pe, idx, scale)
+    assert not np.allclose(out_nc, out)
 
 
 def test_equal_logits_give_mean_and_single_row_gives_row():
