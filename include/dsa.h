@@ -323,6 +323,92 @@ typedef struct dsa_mla_append_args {
 dsa_status dsa_mla_append(const dsa_mla_append_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * MLA projections: the key/value up-projection of the multi-head prefill
+ * form and the two absorption products of the absorbed form.
+ * Pages: "RoPE coefficients" (MLA prefill excerpt: wkv_b applied to the
+ * latent rows, its output viewed per head as k_nope (128) then v (128));
+ * "Similarities" (MQA decode excerpt: q_nope times W_UK[h] is the latent
+ * query, the latent attention output times W_UV[h]^T the head's output).
+ * wkv_b [Hq][256][512] bf16 row-major: rows 0..127 of head h are W_UK[h],
+ * rows 128..255 are W_UV[h].
+ *   dsa_mla_kv_up     y[b][s][256h + d] = sum_c wkv_b[h][d][c] * x[b][s][c]
+ *                     (x rows of 512 features, y rows of Hq*256)
+ *   dsa_mla_absorb_q  y[b][s][h][c] = sum_d x[b][s][h][d] * W_UK[h][d][c]
+ *                     (x head rows of 128, y head rows of 512: only those
+ *                     512 elements are written, so y may be the 576-wide
+ *                     query of dsa_sparse_mla)
+ *   dsa_mla_absorb_o  y[b][s][h][d] = sum_c x[b][s][h][c] * W_UV[h][d][c]
+ *                     (x head rows of 512, y head rows of 128)
+ * Products accumulate in float32 (bf16 MFMA); the result is rounded to bf16
+ * once (nearest even).
+ * Addressing, element strides: row s of batch b of x starts at
+ * x + b*x_batch_stride + s*x_row_stride, head h of it at + h*x_head_stride;
+ * y likewise. dsa_mla_kv_up ignores the head strides. Output heads, rows and
+ * batches must not overlap (checked from the strides); y must not overlap x
+ * or wkv_b.
+ * Limits: B >= 1, 1 <= rows <= 2^24, 1 <= Hq <= 128, B (kv_up) or B*Hq
+ * (absorption) <= 65535; every pointer 16-byte aligned, strides
+ * non-negative multiples of 8 elements. No workspace.
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_mla_proj_args {
+    int32_t B, rows, Hq;
+    const uint16_t* wkv_b;
+    const uint16_t* x;
+    int64_t x_row_stride, x_batch_stride, x_head_stride;
+    uint16_t* y;
+    int64_t y_row_stride, y_batch_stride, y_head_stride;
+} dsa_mla_proj_args;
+
+dsa_status dsa_mla_kv_up(const dsa_mla_proj_args* args, hipStream_t stream);
+dsa_status dsa_mla_absorb_q(const dsa_mla_proj_args* args, hipStream_t stream);
+dsa_status dsa_mla_absorb_o(const dsa_mla_proj_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention in the multi-head (non-absorbed) prefill form.
+ * Page "RoPE coefficients" (MLA prefill excerpt): per-head keys
+ * [k_nope ; k_pe] and values from the up-projection; scores scaled, the
+ * index mask scattered from the top-k list and the causal mask added,
+ * softmax over positions, product with the values.
+ * For row r = (b, s) and head h, over the positions p that appear in idx[r]
+ * (a repeated entry counts once), with 0 <= p < Lmax and, when pos is given,
+ * p <= pos[b][s]:
+ *   z_p = scale * (q[r][h][0:128] . kv[b][p][h][0:128] + q[r][h][128:192] . rope[b][p])
+ *   out[r][h][:] = sum_p softmax(z)_p * kv[b][p][h][128:256]       (bf16)
+ * Products and sums in float32; the probabilities are rounded to bf16 for
+ * the value product. A row with no such position gives 0.
+ * Layouts: q [B][S][Hq][192] bf16 (q_nope, then q_pe already rotated);
+ *   kv [B][Lmax][Hq][256] bf16 contiguous (dsa_mla_kv_up with rows = Lmax);
+ *   rope row p of batch b at rope + b*rope_batch_stride + p*rope_row_stride
+ *   (64 bf16, dense caches only); idx [B][S][K] int32; pos [B][S] int32 or
+ *   NULL (no causal mask); out [B][S][Hq][128] bf16.
+ * Cost: every 64-position tile that any of 128 consecutive rows selects is
+ * computed for all of them, so the work follows the causal extent (as the
+ * pages' dense masked form does), not K as in dsa_sparse_mla.
+ * Limits: 1 <= Hq <= 128, 1 <= K <= 2048, 1 <= Lmax <= 65536, B, S >= 1,
+ * B*S <= 2^26; pointers 16-byte aligned (idx, pos 4), rope strides multiples
+ * of 8 elements. scale > 0 and finite.
+ * Workspace: dsa_sparse_mha_workspace() bytes, 256-byte aligned (per-row
+ * bit masks and per-128-row key-tile lists); contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+typedef struct dsa_mha_args {
+    int32_t B, S, Hq, Lmax, K;
+    const uint16_t* q;
+    const uint16_t* kv;
+    const uint16_t* rope;
+    int64_t rope_row_stride;
+    int64_t rope_batch_stride;
+    const int32_t* idx;
+    const int32_t* pos;          /* optional */
+    float scale;
+    uint16_t* out;
+    void* workspace;
+    size_t workspace_bytes;
+} dsa_mha_args;
+
+dsa_status dsa_sparse_mha_workspace(const dsa_mha_args* args, size_t* bytes);
+dsa_status dsa_sparse_mha(const dsa_mha_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Helpers.
  * ---------------------------------------------------------------------- */
 const char* dsa_status_str(dsa_status status);   /* static string, never NULL */

@@ -12,6 +12,12 @@ Calls (same names as the C ABI, without the ``dsa_`` prefix):
                                             -> scores float32 [B, S, Lmax]
     topk(scores, pos, K)                    -> idx int32 [B, S, K]
     sparse_mla(q, latent, rope, idx, scale) -> out bf16 [B, S, Hq, 512] (, lse)
+    mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None)
+    mla_kv_up(latent, wkv_b)                -> kv bf16 [B, L, Hq, 256]
+    mla_absorb_q(q_nope, wkv_b)             -> bf16 [B, S, Hq, 512]
+    mla_absorb_o(x, wkv_b)                  -> bf16 [B, S, Hq, 128]
+    sparse_mha(q, kv, rope, idx, scale, pos=None)
+                                            -> out bf16 [B, S, Hq, 128]
 """
 from __future__ import annotations
 
@@ -79,9 +85,24 @@ class MlaAppendArgs(ctypes.Structure):
                 ("block_table", _vp), ("page_size", _i32), ("max_pages", _i32), ("num_pages", _i32)]
 
 
+class MlaProjArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("rows", _i32), ("Hq", _i32), ("wkv_b", _vp), ("x", _vp),
+                ("x_row_stride", _i64), ("x_batch_stride", _i64), ("x_head_stride", _i64),
+                ("y", _vp), ("y_row_stride", _i64), ("y_batch_stride", _i64),
+                ("y_head_stride", _i64)]
+
+
+class MhaArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("S", _i32), ("Hq", _i32), ("Lmax", _i32), ("K", _i32),
+                ("q", _vp), ("kv", _vp), ("rope", _vp), ("rope_row_stride", _i64),
+                ("rope_batch_stride", _i64), ("idx", _vp), ("pos", _vp), ("scale", _f32),
+                ("out", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
 EXPORTS = ("dsa_rope_table", "dsa_indexer_workspace", "dsa_indexer", "dsa_topk_workspace",
            "dsa_topk", "dsa_sparse_mla_workspace", "dsa_sparse_mla", "dsa_mla_append",
-           "dsa_status_str", "dsa_abi_version")
+           "dsa_mla_kv_up", "dsa_mla_absorb_q", "dsa_mla_absorb_o", "dsa_sparse_mha_workspace",
+           "dsa_sparse_mha", "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -106,11 +127,14 @@ def lib():
     L.dsa_abi_version.restype = ctypes.c_int
     L.dsa_abi_version.argtypes = []
     for name, st in (("rope_table", RopeTableArgs), ("indexer", IndexerArgs),
-                     ("topk", TopkArgs), ("sparse_mla", MlaArgs)):
+                     ("topk", TopkArgs), ("sparse_mla", MlaArgs),
+                     ("mla_append", MlaAppendArgs), ("mla_kv_up", MlaProjArgs),
+                     ("mla_absorb_q", MlaProjArgs), ("mla_absorb_o", MlaProjArgs),
+                     ("sparse_mha", MhaArgs)):
         fn = getattr(L, "dsa_" + name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(st), _vp]
-        if name != "rope_table":
+        if name in ("indexer", "topk", "sparse_mla", "sparse_mha"):
             ws = getattr(L, f"dsa_{name}_workspace")
             ws.restype = ctypes.c_int
             ws.argtypes = [ctypes.POINTER(st), ctypes.POINTER(_sz)]
@@ -416,6 +440,119 @@ def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None, paging=
     if paging is not None:
         paging.set_fields(a)
     _check(lib().dsa_mla_append(ctypes.byref(a), _stream()))
+
+
+# ------------------------------------------------------------ projections --
+
+def _proj_view(t, name, width, heads=None):
+    """(row stride, batch stride, head stride) of a bf16 device tensor
+    [B, rows, width] or [B, rows, Hq, width] with unit inner stride."""
+    import torch
+    dims = 3 if heads is None else 4
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 \
+            or t.dim() != dims or t.shape[-1] != width or t.stride(-1) != 1 \
+            or (heads is not None and t.shape[2] != heads):
+        shape = "[B, rows, %d]" % width if heads is None else "[B, rows, Hq, %d]" % width
+        raise ValueError(f"{name} must be a bf16 device tensor {shape} with unit inner stride")
+    return t.stride(1), t.stride(0), (0 if heads is None else t.stride(2))
+
+
+def _wkv_b(wkv_b):
+    import torch
+    _need(wkv_b, "wkv_b", torch.bfloat16)
+    if wkv_b.dim() != 3 or tuple(wkv_b.shape[1:]) != (256, LATENT_DIM):
+        raise ValueError("wkv_b must be [Hq, 256, 512] (W_UK rows 0..127, W_UV rows 128..255)")
+    return wkv_b.shape[0]
+
+
+def mla_kv_up(latent, wkv_b, out=None):
+    """Up-projection of the multi-head prefill form: latent [B, L, 512] ->
+    kv [B, L, Hq, 256] (k_nope then v per head)."""
+    import torch
+    Hq = _wkv_b(wkv_b)
+    B, L = latent.shape[:2]
+    xs = _proj_view(latent, "latent", LATENT_DIM)
+    if out is None:
+        out = torch.empty((B, L, Hq, 256), dtype=torch.bfloat16, device=latent.device)
+    ys = _proj_view(out, "out", 256, Hq)
+    if tuple(out.shape[:2]) != (B, L) or out.stride(2) != 256:
+        raise ValueError("out must be [B, L, Hq, 256] with contiguous heads")
+    a = MlaProjArgs(B, L, Hq, _ptr(wkv_b), _ptr(latent), xs[0], xs[1], 0, _ptr(out), ys[0],
+                    ys[1], 0)
+    _check(lib().dsa_mla_kv_up(ctypes.byref(a), _stream()))
+    return out
+
+
+def _absorb(fn, x, wkv_b, out, din, dout):
+    import torch
+    Hq = _wkv_b(wkv_b)
+    xs = _proj_view(x, "x", din, Hq)
+    B, S = x.shape[:2]
+    if out is None:
+        out = torch.empty((B, S, Hq, dout), dtype=torch.bfloat16, device=x.device)
+    ys = _proj_view(out, "out", dout, Hq)
+    if tuple(out.shape[:2]) != (B, S):
+        raise ValueError("out must match x's leading dimensions")
+    a = MlaProjArgs(B, S, Hq, _ptr(wkv_b), _ptr(x), xs[0], xs[1], xs[2], _ptr(out), ys[0],
+                    ys[1], ys[2])
+    _check(fn(ctypes.byref(a), _stream()))
+    return out
+
+
+def mla_absorb_q(q_nope, wkv_b, out=None):
+    """q_nope [B, S, Hq, 128] -> q_nope . W_UK [B, S, Hq, 512]; out may be a
+    view such as q[..., :512] of a [B, S, Hq, 576] query."""
+    return _absorb(lib().dsa_mla_absorb_q, q_nope, wkv_b, out, 128, LATENT_DIM)
+
+
+def mla_absorb_o(x, wkv_b, out=None):
+    """x [B, S, Hq, 512] (latent attention output) -> x . W_UV^T [B, S, Hq, 128]."""
+    return _absorb(lib().dsa_mla_absorb_o, x, wkv_b, out, LATENT_DIM, 128)
+
+
+def mha_args(q, kv, rope, idx, scale, out, pos=None, workspace=None) -> MhaArgs:
+    import torch
+    B, S, Hq, _ = q.shape
+    K = idx.shape[-1]
+    _need(q, "q", torch.bfloat16, (B, S, Hq, 192))
+    _need(kv, "kv", torch.bfloat16)
+    if kv.dim() != 4 or kv.shape[0] != B or kv.shape[2] != Hq or kv.shape[3] != 256:
+        raise ValueError("kv must be [B, Lmax, Hq, 256]")
+    Lmax = kv.shape[1]
+    if rope.dtype != torch.bfloat16 or not rope.is_cuda or rope.dim() != 3 or \
+            rope.shape[0] != B or rope.shape[1] != Lmax or rope.shape[2] != ROPE_DIM or \
+            rope.stride(2) != 1:
+        raise ValueError("rope must be a bf16 device tensor [B, Lmax, 64] with unit inner stride")
+    _need(idx, "idx", torch.int32, (B, S, K))
+    _need(out, "out", torch.bfloat16, (B, S, Hq, 128))
+    if pos is not None:
+        _need(pos, "pos", torch.int32, (B, S))
+    return MhaArgs(B, S, Hq, Lmax, K, _ptr(q), _ptr(kv), _ptr(rope), rope.stride(1),
+                   rope.stride(0), _ptr(idx), _ptr(pos), float(scale), _ptr(out),
+                   _ptr(workspace), 0 if workspace is None else workspace.numel())
+
+
+def sparse_mha_workspace_bytes(args: MhaArgs) -> int:
+    n = _sz(0)
+    _check(lib().dsa_sparse_mha_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_mha(q, kv, rope, idx, scale: float, pos=None, out=None, workspace=None):
+    """Multi-head (non-absorbed) sparse prefill attention: q [B, S, Hq, 192],
+    kv [B, Lmax, Hq, 256] (mla_kv_up), rope [B, Lmax, 64], idx [B, S, K],
+    optional pos [B, S] (causal mask) -> out bf16 [B, S, Hq, 128]."""
+    import torch
+    B, S, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, S, Hq, 128), dtype=torch.bfloat16, device=q.device)
+    a = mha_args(q, kv, rope, idx, scale, out, pos, workspace)
+    need = sparse_mha_workspace_bytes(a)
+    if workspace is None or workspace.numel() < need:
+        workspace = _workspace(need, q.device)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(lib().dsa_sparse_mha(ctypes.byref(a), _stream()))
+    return out
 
 
 def softmax_scale(qk_head_dim: int = 192, yarn: bool = False, rope_factor: float = 40.0,

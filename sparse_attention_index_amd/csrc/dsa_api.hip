@@ -42,6 +42,14 @@ hipError_t launch_mla_append(int B, int S, int Hq, int Lmax, int P, const uint16
                              const float* sin_t, uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              uint16_t* rope, int64_t rope_rs, int64_t rope_bs, uint16_t* q,
                              CacheMap cmap, hipStream_t stream);
+hipError_t launch_mla_proj(int mode, int B, int rows, int Hq, const uint16_t* wkv_b,
+                           const uint16_t* x, int64_t xrs, int64_t xbs, int64_t xhs, uint16_t* y,
+                           int64_t yrs, int64_t ybs, int64_t yhs, hipStream_t stream);
+size_t mha_workspace_bytes(int B, int S, int Lmax);
+hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
+                             const uint16_t* kv, const uint16_t* rope, int64_t rope_rs,
+                             int64_t rope_bs, const int32_t* idx, const int32_t* pos, float scale,
+                             uint16_t* out, void* workspace, hipStream_t stream);
 }  // namespace dsa
 
 namespace {
@@ -181,7 +189,65 @@ dsa_status check_mla_append(const dsa_mla_append_args* a) {
     return check_paging(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
 }
 
+// ----------------------------------------------------------- projections ---
+// mode 0: kv_up (x rows of 512, y rows of Hq*256), 1: absorb_q (x heads of
+// 128, y heads of 512), 2: absorb_o (x heads of 512, y heads of 128)
+dsa_status check_mla_proj(const dsa_mla_proj_args* a, int mode) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->rows < 1 || a->rows > (1 << 24) || a->Hq < 1 ||
+        a->Hq > DSA_MAX_ATTN_HEADS)
+        return DSA_ERR_SHAPE;
+    const int64_t zs = mode == 0 ? a->B : static_cast<int64_t>(a->B) * a->Hq;
+    if (zs > kMaxGridY) return DSA_ERR_SHAPE;
+    if (!a->wkv_b || !a->x || !a->y) return DSA_ERR_NULL;
+    const int64_t yw = mode == 0 ? int64_t(256) * a->Hq : (mode == 1 ? DSA_LATENT_DIM : 128);
+    const int64_t xh = mode == 0 ? 0 : a->x_head_stride, yh = mode == 0 ? 0 : a->y_head_stride;
+    if (a->x_row_stride < 0 || a->x_batch_stride < 0 || a->y_row_stride < 0 ||
+        a->y_batch_stride < 0 || xh < 0 || yh < 0)
+        return DSA_ERR_SHAPE;
+    // output heads, rows and batches must not overlap
+    if (mode != 0 && a->Hq > 1 && yh < yw) return DSA_ERR_SHAPE;
+    const int64_t yrow = (mode == 0 ? 0 : (a->Hq - 1) * yh) + yw;
+    if (a->rows > 1 && a->y_row_stride < yrow) return DSA_ERR_SHAPE;
+    if (a->B > 1 && a->y_batch_stride < (a->rows - 1) * a->y_row_stride + yrow) return DSA_ERR_SHAPE;
+    if (!aligned16(a->wkv_b) || !aligned16(a->x) || !aligned16(a->y)) return DSA_ERR_ALIGN;
+    if ((a->x_row_stride % 8) || (a->x_batch_stride % 8) || (xh % 8) || (a->y_row_stride % 8) ||
+        (a->y_batch_stride % 8) || (yh % 8))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+// ------------------------------------------------------------------- mha ---
+constexpr int kMhaMaxL = 65536;
+
+dsa_status check_mha(const dsa_mha_args* a) {
+    if (a == nullptr) return DSA_ERR_NULL;
+    if (a->B < 1 || a->S < 1 || a->Hq < 1 || a->Hq > DSA_MAX_ATTN_HEADS || a->Lmax < 1 ||
+        a->Lmax > kMhaMaxL || a->K < 1 || a->K > DSA_MAX_TOPK)
+        return DSA_ERR_SHAPE;
+    const int64_t nqt = static_cast<int64_t>(a->B) * ((a->S + 127) / 128);
+    if (nqt * a->Hq > (int64_t(1) << 31) - 1 || static_cast<int64_t>(a->B) * a->S > (1 << 26))
+        return DSA_ERR_SHAPE;
+    if (!(a->scale > 0.0f) || !std::isfinite(a->scale)) return DSA_ERR_SHAPE;
+    if (a->rope_row_stride < DSA_ROPE_DIM || a->rope_batch_stride < 0) return DSA_ERR_SHAPE;
+    if (!a->q || !a->kv || !a->rope || !a->idx || !a->out) return DSA_ERR_NULL;
+    if (!aligned16(a->q) || !aligned16(a->kv) || !aligned16(a->rope) || !aligned16(a->out) ||
+        !aligned4(a->idx) || (a->pos && !aligned4(a->pos)))
+        return DSA_ERR_ALIGN;
+    if ((a->rope_row_stride % 8) || (a->rope_batch_stride % 8)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+dsa_status run_mla_proj(const dsa_mla_proj_args* a, int mode, hipStream_t stream) {
+    const dsa_status st = check_mla_proj(a, mode);
+    if (st != DSA_OK) return st;
+    return hip_status(dsa::launch_mla_proj(mode, a->B, a->rows, a->Hq, a->wkv_b, a->x,
+                                           a->x_row_stride, a->x_batch_stride, a->x_head_stride,
+                                           a->y, a->y_row_stride, a->y_batch_stride,
+                                           a->y_head_stride, stream));
+}
 
 }  // namespace
 
@@ -333,6 +399,38 @@ dsa_status dsa_mla_append(const dsa_mla_append_args* a, hipStream_t stream) {
         a->rope_cos, a->rope_sin, a->latent, a->latent_row_stride, a->latent_batch_stride,
         a->rope, a->rope_row_stride, a->rope_batch_stride, a->q,
         make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, 0), stream));
+}
+
+dsa_status dsa_mla_kv_up(const dsa_mla_proj_args* a, hipStream_t stream) {
+    return run_mla_proj(a, 0, stream);
+}
+
+dsa_status dsa_mla_absorb_q(const dsa_mla_proj_args* a, hipStream_t stream) {
+    return run_mla_proj(a, 1, stream);
+}
+
+dsa_status dsa_mla_absorb_o(const dsa_mla_proj_args* a, hipStream_t stream) {
+    return run_mla_proj(a, 2, stream);
+}
+
+dsa_status dsa_sparse_mha_workspace(const dsa_mha_args* a, size_t* bytes) {
+    if (bytes == nullptr) return DSA_ERR_NULL;
+    const dsa_status st = check_mha(a);
+    if (st != DSA_OK) return st;
+    *bytes = dsa::mha_workspace_bytes(a->B, a->S, a->Lmax);
+    return DSA_OK;
+}
+
+dsa_status dsa_sparse_mha(const dsa_mha_args* a, hipStream_t stream) {
+    const dsa_status st = check_mha(a);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::mha_workspace_bytes(a->B, a->S, a->Lmax);
+    if (a->workspace == nullptr || a->workspace_bytes < need) return DSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+    return hip_status(dsa::launch_sparse_mha(a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->kv,
+                                             a->rope, a->rope_row_stride, a->rope_batch_stride,
+                                             a->idx, a->pos, a->scale, a->out, a->workspace,
+                                             stream));
 }
 
 }  // extern "C"

@@ -11,6 +11,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// 16-byte staging register (a native vector: copies stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -119,6 +121,17 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
     r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
     return r;
+}
+
+// Transposing LDS read ds_read_b64_tr_b16 (gfx950). Within each 16-lane
+// group, lane 4e+q passes the address of elements 4q..4q+3 of row e of a
+// 4 x 16 block of 16-bit elements; lane i receives column i of rows 0..3.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_v4s*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))));
 }
 
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, v4f c) {

@@ -1,0 +1,356 @@
+// sparse_mha.hip -- sparse attention in the multi-head (non-absorbed) prefill
+// form, gfx950.
+//
+// Method (page "RoPE coefficients", MLA prefill excerpt): every head has its
+// own key [k_nope (128) ; k_pe (64, shared by the heads)] and value (128)
+// from the up-projection of the latent rows; the scores q . k are scaled,
+// the index mask (0 where the top-k list scatters, -inf elsewhere) and the
+// causal mask are added, and the softmax over positions weights the values.
+// For row r = (b, s), head h:
+//   z_p   = scale * (q[r][h][0:128] . kv[b][p][h][0:128] + q[r][h][128:192] . rope[b][p])
+//   out[r][h] = sum_p softmax(z)_p kv[b][p][h][128:256]
+// over the positions p in the row's list (a repeat counts once, as in a
+// scattered mask) with 0 <= p < Lmax and p <= pos[r] when positions are
+// given.
+//
+// Design. The masked dense form is computed, tile by tile, only where the
+// mask has something:
+//  1. selection_mask_kernel turns each row's list into a bit mask over
+//     positions (two 32-bit words per 64-position tile) and, for every
+//     128-row query tile, lists the 64-position key tiles that any of its
+//     rows selects, with the union of the rows' bits.
+//  2. sparse_mha_kernel: one block of 4 waves per (query tile, head); wave w
+//     serves rows 32w..32w+31 as two 16-row groups. For each listed key tile
+//     the block gathers the head's 64 key/value rows into an LDS tile
+//     [64][k_nope | k_pe | v] (positions no row selects are zero and not
+//     read), then per wave
+//       S^T = K Q^T    bf16 MFMA 16x16x32, keys x rows, Q^T held in VGPRs,
+//                      each K operand read once for both row groups;
+//       online softmax per row (masked scores are -inf), in log2 units,
+//                      against a reference maximum that moves only when the
+//                      running maximum passes it by 8;
+//       O^T += V^T P^T P^T straight from the S^T registers (the key order
+//                      inside the MFMA's K dimension only has to agree
+//                      between the operands), V^T by the transposing LDS
+//                      read from the row-major tile.
+//     Two blocks share a CU and hide each other's gathers. Launch order: with Hq a multiple of 8, each XCD takes
+//     whole heads, so one head's keys and values stay in its L2; within a
+//     head the query tiles with the longest causal extent go first.
+#include "dsa_common.h"
+
+namespace dsa {
+
+constexpr int kMhaRows = 128;           // query rows per block
+constexpr int kMhaKeys = 64;            // positions per key tile
+constexpr int kMhaThreads = 256;
+constexpr int kMhaRS = 320 + 8;         // bf16 per LDS key row: k_nope 0..127, k_pe 128..191, v 192..319
+constexpr int kMaskThreads = 256;
+
+// ---- 1. bit masks and key-tile lists ---------------------------------------
+// Grid: one block per query tile (B * ntq). LDS: one mask row per wave and
+// the tile's union row (5 * nw words).
+__global__ __launch_bounds__(kMaskThreads) void selection_mask_kernel(
+    int S, int Lmax, int K, int nkt, int ntq, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ pos, uint32_t* __restrict__ mask, int4* __restrict__ tiles) {
+    extern __shared__ uint32_t msm[];
+    const int nw = 2 * nkt;
+    uint32_t* tun = msm + 4 * nw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qt = blockIdx.x;
+    const int64_t b = qt / ntq;
+    const int t0 = (qt % ntq) * kMhaRows;
+    for (int i = tid; i < nw; i += kMaskThreads) tun[i] = 0u;
+    uint32_t* rb = msm + wave * nw;
+    for (int it = 0; it < kMhaRows / 4; ++it) {
+        const int t = t0 + 4 * it + wave;
+        const bool valid = t < S;
+        const int64_t r = b * S + t;
+        for (int i = lane; i < nw; i += 64) rb[i] = 0u;
+        __syncthreads();
+        if (valid) {
+            const int pr = pos != nullptr ? pos[r] : 0x7FFFFFFF;
+            const int32_t* sel = idx + r * K;
+            for (int j0 = 0; j0 < K; j0 += 64) {
+                const int j = j0 + lane;
+                const int p = j < K ? sel[j] : -1;
+                const bool ok = p >= 0 && p < Lmax && p <= pr;
+                // lanes holding the same word OR their bits towards the first
+                // lane of each run of equal words, which alone writes (fewer
+                // LDS atomics on the same address); any order is correct
+                int w = ok ? (p >> 5) : -1 - lane;
+                uint32_t bit = ok ? (1u << (p & 31)) : 0u;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t ob = static_cast<uint32_t>(__shfl_down(static_cast<int>(bit), d));
+                    const int ow = __shfl_down(w, d);
+                    if (ow == w) bit |= ob;
+                }
+                const int prev = __shfl_up(w, 1);
+                if (ok && (lane == 0 || prev != w)) atomicOr(&rb[w], bit);
+            }
+        }
+        __syncthreads();
+        if (valid) {
+            uint32_t* mrow = mask + r * nw;
+            for (int i = lane; i < nw; i += 64) {
+                const uint32_t v = rb[i];
+                mrow[i] = v;
+                if (v) atomicOr(&tun[i], v);
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int4* tl = tiles + static_cast<int64_t>(qt) * (nkt + 1);
+        int base = 0;
+        for (int k0 = 0; k0 < nkt; k0 += 64) {
+            const int kt = k0 + lane;
+            const uint32_t lo = kt < nkt ? tun[2 * kt] : 0u;
+            const uint32_t hi = kt < nkt ? tun[2 * kt + 1] : 0u;
+            const bool nz = (lo | hi) != 0u;
+            const uint64_t bal = __ballot(nz);
+            const int rank = __popcll(bal & ((uint64_t(1) << lane) - 1));
+            if (nz) tl[1 + base + rank] = make_int4(kt, static_cast<int>(lo), static_cast<int>(hi), 0);
+            base += __popcll(bal);
+        }
+        if (lane == 0) tl[0] = make_int4(base, 0, 0, 0);
+    }
+}
+
+// ---- 2. attention over the listed key tiles ---------------------------------
+__global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
+    int S, int Hq, int Lmax, int nkt, int ntq, int nqt, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ rope, int64_t rope_rs,
+    int64_t rope_bs, const uint32_t* __restrict__ mask, const int4* __restrict__ tiles,
+    float scale_log2, uint16_t* __restrict__ out) {
+    __shared__ __align__(16) uint16_t Kt[kMhaKeys * kMhaRS];
+
+    // launch index -> (head, query tile); longest causal extent first
+    const int L = blockIdx.x;
+    int h, qtg;
+    if ((Hq & 7) == 0) {
+        const int j = L >> 3;
+        h = (j / nqt) * 8 + (L & 7);
+        qtg = nqt - 1 - (j % nqt);
+    } else {
+        h = L % Hq;
+        qtg = nqt - 1 - L / Hq;
+    }
+    const int64_t b = qtg / ntq;
+    const int t0 = (qtg % ntq) * kMhaRows;
+    const int nw = 2 * nkt;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+
+    // rows of this lane's two groups: t0 + 32 wave + 16 qg + m
+    int64_t rr[2];
+    bool rv[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int t = t0 + 32 * wave + 16 * qg + m;
+        rv[qg] = t < S;
+        rr[qg] = b * S + (rv[qg] ? t : 0);
+    }
+    // Q^T operands: lane (row m, chunk g) holds q[row][h][32 ks + 8 g .. +7]
+    bf16x8 qreg[2][6];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const uint16_t* qh = q + (rr[qg] * Hq + h) * 192 + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks) {
+            uint4 v = *reinterpret_cast<const uint4*>(qh + 32 * ks);
+            if (!rv[qg]) v = make_uint4(0u, 0u, 0u, 0u);
+            qreg[qg][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    v4f acc[2][8];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) acc[qg][t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f}, lr_run[2] = {0.0f, 0.0f};
+
+    const int4* tl = tiles + static_cast<int64_t>(qtg) * (nkt + 1);
+    const int ntile = tl[0].x;
+
+    // gather: key row tid/4, quarter sub = tid%4: kv chunks sub + 4i (i < 8)
+    // and rope chunks sub, sub + 4 (16 bytes each)
+    const int gkey = tid >> 2, gsub = tid & 3;
+    u32x4 G[10];
+    uint2 mw[2];
+    const uint16_t* kv_bh = kv + (b * Lmax * Hq + h) * 256;
+    const uint16_t* rope_b = rope + b * rope_bs;
+    auto fetch = [&](int it) {
+        const int4 e = tl[1 + it];
+        const int kt = e.x;
+        const uint32_t u = gkey < 32 ? static_cast<uint32_t>(e.y) >> gkey
+                                     : static_cast<uint32_t>(e.z) >> (gkey - 32);
+        // positions no row of the tile selects (and those past Lmax) read
+        // position 0 and are zeroed
+        const bool live = (u & 1u) != 0u;
+        const int s = live ? kt * kMhaKeys + gkey : 0;
+        const uint16_t* krow = kv_bh + static_cast<int64_t>(s) * Hq * 256 + 8 * gsub;
+        const uint16_t* prow = rope_b + static_cast<int64_t>(s) * rope_rs + 8 * gsub;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const u32x4*>(krow + 32 * i);
+        G[8] = *reinterpret_cast<const u32x4*>(prow);
+        G[9] = *reinterpret_cast<const u32x4*>(prow + 32);
+        if (!live) {
+#pragma unroll
+            for (int i = 0; i < 10; ++i) G[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg)
+            mw[qg] = rv[qg] ? *reinterpret_cast<const uint2*>(mask + rr[qg] * nw + 2 * kt)
+                            : make_uint2(0u, 0u);
+    };
+    auto store = [&]() {
+        uint16_t* dst = Kt + gkey * kMhaRS + 8 * gsub;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 32 * i) = G[i];        // k_nope
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 192 + 32 * i) = G[4 + i];  // v
+        *reinterpret_cast<u32x4*>(dst + 128) = G[8];                                      // k_pe
+        *reinterpret_cast<u32x4*>(dst + 160) = G[9];
+    };
+
+    // transposing-read address: lane 4e+q of group g reads v features 4q..
+    // of key 4g+e (and 16+4g+e) inside a 32-key half
+    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kMhaRS + 192 + 4 * (lane & 3);
+
+    for (int it = 0; it < ntile; ++it) {
+        __syncthreads();                               // previous tile consumed
+        fetch(it);
+        store();
+        const uint2 mcur[2] = {mw[0], mw[1]};
+        __syncthreads();
+
+        // S^T: s[qg][st] for keys 16 st + 4 g + i, row m of group qg
+        v4f s[2][4];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) s[qg][st] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(
+                    Kt + (16 * st + m) * kMhaRS + 32 * ks + 8 * g);
+                s[0][st] = mfma_bf16_16x16x32(kop, qreg[0][ks], s[0][st]);
+                s[1][st] = mfma_bf16_16x16x32(kop, qreg[1][ks], s[1][st]);
+            }
+        }
+
+        bf16x8 pv[2][2];
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg) {
+            float z[16];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const uint32_t word = st < 2 ? mcur[qg].x : mcur[qg].y;
+                const uint32_t nib = (word >> ((16 * st + 4 * g) & 31)) & 0xFu;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    z[4 * st + i] = (nib >> i) & 1u ? s[qg][st][i] * scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, z[4 * st + i]);
+                }
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            if (tmax > m_run[qg] + 8.0f) {
+                const float corr = (m_run[qg] == -INFINITY) ? 0.0f : exp2f(m_run[qg] - tmax);
+                l_run[qg] *= corr;
+                lr_run[qg] *= corr;
+                m_run[qg] = tmax;
+                if (__ballot(corr != 1.0f)) {
+#pragma unroll
+                    for (int t2 = 0; t2 < 8; ++t2) acc[qg][t2] *= corr;
+                }
+            }
+            const bool live = m_run[qg] != -INFINITY;
+            float psum = 0.0f, prsum = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    // k slot 8g + i of the value product: key 32 kk + 4 g + i
+                    // (i < 4) or 32 kk + 16 + 4 g + i - 4
+                    const float zz = z[4 * (2 * kk + (i >> 2)) + (i & 3)];
+                    const float pe = live ? __builtin_amdgcn_exp2f(zz - m_run[qg]) : 0.0f;
+                    const __bf16 pb = static_cast<__bf16>(pe);
+                    pv[qg][kk][i] = pb;
+                    psum += pe;
+                    prsum += static_cast<float>(pb);
+                }
+            }
+            l_run[qg] += psum;
+            lr_run[qg] += prsum;
+        }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int t2 = 0; t2 < 8; ++t2) {
+                const uint16_t* p = Kt + 32 * kk * kMhaRS + tr_off + 16 * t2;
+                const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
+                const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 16 * kMhaRS));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc[0][t2] = mfma_bf16_16x16x32(va, pv[0][kk], acc[0][t2]);
+                acc[1][t2] = mfma_bf16_16x16x32(va, pv[1][kk], acc[1][t2]);
+            }
+        }
+    }
+
+    // lane holds O^T[16 t2 + 4 g + i][row m of group qg]
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        float lr_tot = lr_run[qg] + __shfl_xor(lr_run[qg], 16);
+        lr_tot += __shfl_xor(lr_tot, 32);
+        if (!rv[qg]) continue;
+        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+        uint16_t* oh = out + (rr[qg] * Hq + h) * 128 + 4 * g;
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) {
+            const uint32_t lo = pack_bf16x2(acc[qg][t2][0] * inv, acc[qg][t2][1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[qg][t2][2] * inv, acc[qg][t2][3] * inv);
+            *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
+        }
+    }
+}
+
+// Workspace: bit masks [B*S][2*nkt] words, then (256-byte aligned) the tile
+// lists [B*ntq][nkt + 1] of int4.
+size_t mha_workspace_bytes(int B, int S, int Lmax) {
+    const int64_t nkt = (Lmax + kMhaKeys - 1) / kMhaKeys;
+    const int64_t ntq = (S + kMhaRows - 1) / kMhaRows;
+    const size_t maskb = static_cast<size_t>(B) * S * 2 * nkt * sizeof(uint32_t);
+    const size_t tl = static_cast<size_t>(B) * ntq * (nkt + 1) * sizeof(int4);
+    return (maskb + 255) / 256 * 256 + tl;
+}
+
+hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
+                             const uint16_t* kv, const uint16_t* rope, int64_t rope_rs,
+                             int64_t rope_bs, const int32_t* idx, const int32_t* pos, float scale,
+                             uint16_t* out, void* workspace, hipStream_t stream) {
+    const int nkt = (Lmax + kMhaKeys - 1) / kMhaKeys;
+    const int ntq = (S + kMhaRows - 1) / kMhaRows;
+    const int nqt = B * ntq;
+    const size_t maskb = static_cast<size_t>(B) * S * 2 * nkt * sizeof(uint32_t);
+    uint32_t* mask = static_cast<uint32_t*>(workspace);
+    int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + (maskb + 255) / 256 * 256);
+    const size_t lds = sizeof(uint32_t) * 5 * 2 * nkt;
+    hipLaunchKernelGGL(selection_mask_kernel, dim3(static_cast<unsigned>(nqt)), dim3(kMaskThreads),
+                       lds, stream, S, Lmax, K, nkt, ntq, idx, pos, mask, tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(sparse_mha_kernel, dim3(static_cast<unsigned>(nqt * Hq)), dim3(kMhaThreads),
+                       0, stream, S, Hq, Lmax, nkt, ntq, nqt, q, kv, rope, rope_rs, rope_bs, mask,
+                       tiles, scale_log2, out);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

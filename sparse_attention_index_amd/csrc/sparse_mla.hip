@@ -45,8 +45,6 @@
 
 namespace dsa {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-
 constexpr int kDl = 512, kDq = 576;
 constexpr int kTile = 32;
 constexpr int kKtStride = kDq + 8;      // bf16 per K-tile row (1168 B, staggers banks)
@@ -62,13 +60,6 @@ constexpr size_t kMlaLdsBytes = sizeof(uint16_t) * kTile * kKtStride + sizeof(in
 // keeps the LDS operand reads of a tile a fixed number of MFMAs ahead.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 #define DSA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
-__device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
-    typedef __attribute__((address_space(3))) v4s lds_v4s;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<lds_v4s*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
-            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))));
-}
 
 template <bool PIPE>
 __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 15, names
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -47,6 +47,8 @@ STRUCTS = {
     "dsa_topk_args": dsa.TopkArgs,
     "dsa_mla_args": dsa.MlaArgs,
     "dsa_mla_append_args": dsa.MlaAppendArgs,
+    "dsa_mla_proj_args": dsa.MlaProjArgs,
+    "dsa_mha_args": dsa.MhaArgs,
 }
 
 
@@ -223,3 +225,67 @@ def test_paging_validation(fields, code):
         for k, v in fields.items():
             setattr(a, k, v)
         assert call(fn, a) == code, (make.__name__, fields)
+
+
+def good_proj(mode):
+    # 2 batches x 300 rows x 128 heads, contiguous layouts
+    if mode == "kv_up":
+        return dsa.MlaProjArgs(2, 300, 128, FAKE, FAKE, 512, 512 * 300, 0, FAKE, 128 * 256,
+                               128 * 256 * 300, 0)
+    din, dout = (128, 512) if mode == "absorb_q" else (512, 128)
+    return dsa.MlaProjArgs(2, 300, 128, FAKE, FAKE, 128 * din, 128 * din * 300, din, FAKE,
+                           128 * dout, 128 * dout * 300, dout)
+
+
+@pytest.mark.parametrize("mode", ["kv_up", "absorb_q", "absorb_o"])
+def test_mla_proj_validation(mode):
+    L = dsa.lib()
+    fn = getattr(L, "dsa_mla_" + mode)
+    cases = [(dict(B=0), 2), (dict(rows=0), 2), (dict(Hq=129), 2), (dict(Hq=0), 2),
+             (dict(rows=(1 << 24) + 1), 2), (dict(wkv_b=None), 1), (dict(x=None), 1),
+             (dict(y=None), 1), (dict(x=FAKE + 8), 5), (dict(wkv_b=FAKE + 2), 5),
+             (dict(x_row_stride=-8), 2), (dict(y_batch_stride=8), 2)]
+    if mode == "kv_up":
+        cases += [(dict(y_row_stride=128 * 256 - 8), 2), (dict(x_row_stride=516), 5),
+                  (dict(B=70000), 2)]
+    else:
+        # the 576-wide query as output of the query absorption is fine
+        cases += [(dict(y_head_stride=8), 2), (dict(x_head_stride=4), 5),
+                  (dict(B=600), 2)]                          # B * Hq grid rows > 65535
+    for change, code in cases:
+        a = good_proj(mode)
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(fn, a) == code, change
+    assert fn(None, None) == 1
+
+
+def good_mha():
+    return dsa.MhaArgs(1, 4096, 128, 4096, 2048, FAKE, FAKE, FAKE, 64, 64 * 4096, FAKE, FAKE,
+                       0.1, FAKE, None, 0)
+
+
+def test_mha_validation():
+    L = dsa.lib()
+    for change, code in [(dict(Hq=129), 2), (dict(K=2049), 2), (dict(Lmax=65537), 2),
+                         (dict(S=0), 2), (dict(scale=0.0), 2), (dict(rope_row_stride=32), 2),
+                         (dict(q=None), 1), (dict(kv=None), 1), (dict(idx=None), 1),
+                         (dict(out=None), 1), (dict(kv=FAKE + 8), 5), (dict(pos=FAKE + 2), 5),
+                         (dict(rope_row_stride=68), 5)]:
+        a = good_mha()
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(L.dsa_sparse_mha, a) == code, change
+    n = ctypes.c_size_t(0)
+    a = good_mha()
+    assert L.dsa_sparse_mha_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+    # bit masks (4096 rows x 128 words) and tile lists (32 query tiles x 65 entries)
+    assert n.value >= 4096 * 128 * 4 + 32 * 65 * 16
+    assert call(L.dsa_sparse_mha, a) == 4
+    a.workspace, a.workspace_bytes = FAKE + 16, n.value
+    assert call(L.dsa_sparse_mha, a) == 5
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert call(L.dsa_sparse_mha, a) == 4
+    a.pos = None                                   # positions are optional
+    a.workspace_bytes = n.value - 1
+    assert call(L.dsa_sparse_mha, a) == 4
