@@ -496,14 +496,30 @@ def prefill_leg(reps=20):
         dsa.mla_args(q_mla, latent, kpe, idx, scale, out))), dtype=torch.uint8, device=dev)
     tws = dsa.topk_workspace(scores, pos, K)
 
+    # the multi-head (non-absorbed) form and the absorption products, on the
+    # same latent cache and selection; wkv_b ~ N(0, 1/512)
+    wkv_b = (randn(Hq, 256, 512) * (512 ** -0.5)).to(torch.bfloat16)
+    q_nope = randn(1, T, Hq, 128).to(torch.bfloat16)
+    q192 = torch.cat([q_nope, q_mla[..., 512:]], -1).contiguous()
+    kv = torch.empty((1, T, Hq, 256), dtype=torch.bfloat16, device=dev)
+    o128 = torch.empty((1, T, Hq, 128), dtype=torch.bfloat16, device=dev)
+    qa = torch.empty((1, T, Hq, 576), dtype=torch.bfloat16, device=dev)
+    hws = torch.empty(max(1, dsa.sparse_mha_workspace_bytes(
+        dsa.mha_args(q192, kv, kpe, idx, scale, o128, pos))), dtype=torch.uint8, device=dev)
+
     calls = {
         "indexer": lambda: dsa.indexer(q_raw, w, pos, cos, sin, kc, ks, scores, k_raw=k_raw,
                                        workspace=iws),
         "topk": lambda: dsa.topk(scores, pos, K, idx=idx, workspace=tws),
         "sparse_mla": lambda: dsa.sparse_mla(q_mla, latent, kpe, idx, scale, out=out,
                                              workspace=mws),
+        "absorb_q": lambda: dsa.mla_absorb_q(q_nope, wkv_b, out=qa[..., :512]),
+        "absorb_o": lambda: dsa.mla_absorb_o(out, wkv_b, out=o128),
+        "kv_up": lambda: dsa.mla_kv_up(latent, wkv_b, out=kv),
+        "sparse_mha": lambda: dsa.sparse_mha(q192, kv, kpe, idx, scale, pos=pos, out=o128,
+                                             workspace=hws),
     }
-    for c in ("indexer", "topk", "sparse_mla"):
+    for c in calls:
         calls[c]()
     torch.cuda.synchronize()
     us = {}
@@ -525,6 +541,15 @@ def prefill_leg(reps=20):
     topk_bytes = 4 * pairs + 4 * sel
     idx_tfs = idx_tflop / (us["indexer"] * 1e-6)
     mla_tfs = mla_tflop / (us["sparse_mla"] * 1e-6)
+    gemm_tflop = {"absorb_q": 2.0 * T * Hq * 128 * 512 / 1e12,
+                  "absorb_o": 2.0 * T * Hq * 512 * 128 / 1e12,
+                  "kv_up": 2.0 * T * 512 * Hq * 256 / 1e12}
+    mha_tflop = 2.0 * Hq * (192 + 128) * sel / 1e12
+    # executed work: every listed 64-position tile of each 128-row query tile
+    tl = hws[dsa.sparse_mha_tiles_offset(1, T, T):].view(torch.int32).view(-1, T // 64 + 1, 4)
+    ntiles = int(tl[:, 0, 0].sum().item())
+    mha_exec_tflop = 2.0 * Hq * (192 + 128) * 128 * 64 * ntiles / 1e12
+    mha_tfs = mha_tflop / (us["sparse_mha"] * 1e-6)
     return {
         "workload": "prefill T=4096 (B=1, L=4096, H_I=64, top-2048, 128 heads)",
         "call_us": {k: round(v, 1) for k, v in us.items()},
@@ -537,6 +562,18 @@ def prefill_leg(reps=20):
                        "frac_bf16_mfma": round(mla_tfs / BF16_MFMA_PEAK_TFLOPS, 4)},
         "topk": {"GBps": round(topk_bytes / (us["topk"] * 1e-6) / 1e9, 1), "bytes": topk_bytes,
                  "frac_hbm": round(topk_bytes / (us["topk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "projections": {c: {"tflops": round(f / (us[c] * 1e-6), 1), "flop": round(f * 1e12),
+                            "frac_bf16_mfma": round(f / (us[c] * 1e-6) / BF16_MFMA_PEAK_TFLOPS, 4)}
+                        for c, f in gemm_tflop.items()},
+        "sparse_mha": {"tflops": round(mha_tfs, 1), "flop": round(mha_tflop * 1e12),
+                       "frac_bf16_mfma": round(mha_tfs / BF16_MFMA_PEAK_TFLOPS, 4),
+                       "executed_flop": round(mha_exec_tflop * 1e12),
+                       "executed_tflops": round(mha_exec_tflop / (us["sparse_mha"] * 1e-6), 1),
+                       "note": "flop counts the selected (row, position) pairs; executed_flop "
+                               "every 64-position tile any of 128 rows selects"},
+        "forms_us": {"absorbed (absorb_q + sparse_mla + absorb_o)":
+                     round(us["absorb_q"] + us["sparse_mla"] + us["absorb_o"], 1),
+                     "multi-head (kv_up + sparse_mha)": round(us["kv_up"] + us["sparse_mha"], 1)},
     }
 
 

@@ -532,6 +532,15 @@ def mha_args(q, kv, rope, idx, scale, out, pos=None, workspace=None) -> MhaArgs:
                    _ptr(workspace), 0 if workspace is None else workspace.numel())
 
 
+def sparse_mha_tiles_offset(B: int, S: int, Lmax: int) -> int:
+    """Byte offset of the key-tile lists inside the workspace: after the bit
+    masks ([B*S][2*ceil(Lmax/64)] words), rounded up to 256. The lists are
+    [B*ceil(S/128)][ceil(Lmax/64) + 1] int4: entry 0 holds the count, then
+    (tile, union bits low, union bits high, 0)."""
+    nkt = (Lmax + 63) // 64
+    return (B * S * 2 * nkt * 4 + 255) // 256 * 256
+
+
 def sparse_mha_workspace_bytes(args: MhaArgs) -> int:
     n = _sz(0)
     _check(lib().dsa_sparse_mha_workspace(ctypes.byref(args), ctypes.byref(n)))

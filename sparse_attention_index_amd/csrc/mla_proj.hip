@@ -15,23 +15,30 @@
 //   kv_up     A = latent rows [rows][512], B = wkv_b as [Hq*256][512]   (B is N x K)
 //   absorb_q  per (b, h): A = q_nope [rows][128], B = W_UK[h] [128][512] (B is K x N)
 //   absorb_o  per (b, h): A = x [rows][512],      B = W_UV[h] [128][512] (B is N x K)
-// Block tile 128 x 128 x 64, 4 waves of 64 x 64 (4 x 4 MFMA 16x16x32
-// tiles); A and B tiles pass through double-buffered LDS, the next k-slice
-// is loaded into registers while the current one is multiplied. Each MFMA
-// computes a tile of C^T (B rows as the first operand), so a lane ends with
-// four consecutive output columns of one row: 8-byte stores. A B operand
-// stored K x N is read column-wise from its row-major LDS tile by the
-// transposing LDS read.
+// Block tile 128 x 128, 4 waves of 64 x 64 (4 x 4 MFMA 16x16x32 tiles),
+// k-slices of 32. The slices stream through a ring of LDS stages filled
+// straight from global memory (global_load_lds, 16 bytes per lane, no
+// registers), two slices ahead of the one being multiplied; raw barriers
+// and explicit vector-memory waits keep the loads in flight across them.
+// Tiles are stored with XOR-swizzled 16-byte chunks so the operand reads
+// of one MFMA hit distinct banks. Each MFMA computes a tile of C^T (B rows
+// as the first operand), so a lane ends with four consecutive output
+// columns of one row: 8-byte stores. A B operand stored K x N is read
+// column-wise by the transposing LDS read.
 #include "dsa_common.h"
 
 namespace dsa {
 
-constexpr int kGM = 128, kGN = 128, kGK = 64;
+#ifndef DSA_GEMM_STAGES
+#define DSA_GEMM_STAGES 3
+#endif
+constexpr int kGM = 128, kGN = 128, kGK = 32;
+constexpr int kGStages = DSA_GEMM_STAGES;            // k-slices in the LDS ring
 constexpr int kGThreads = 256;
-constexpr int kGAStride = kGK + 8;      // bf16 per LDS row of an A (or N x K B) tile
-constexpr int kGBnStride = kGN + 8;     // bf16 per LDS row of a K x N B tile
-constexpr size_t kGemmLds =
-    sizeof(uint16_t) * 2 * (kGM * kGAStride + kGN * kGAStride);   // both buffers, both tiles
+constexpr int kGTileBytes = 128 * kGK * 2;           // one 128 x 32 (or 32 x 128) bf16 tile
+constexpr int kGStageBytes = 2 * kGTileBytes;        // A tile + B tile
+constexpr size_t kGemmLds = static_cast<size_t>(kGStages) * kGStageBytes;
+constexpr int kGLoads = 4;                           // 16-byte loads per thread per slice
 
 struct GemmArgs {
     int M, N, K;
@@ -45,12 +52,25 @@ struct GemmArgs {
     int64_t ldc, c_s1, c_s2;
 };
 
+// s_waitcnt with only the vector-memory counter limited to n (n < 64)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// bytes 16 l .. 16 l + 15 after the wave-uniform LDS address `dst`.
+__device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* dst) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(
+        src, reinterpret_cast<lds_void*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
+                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))),
+        16, 0, 0);
+}
+
 template <bool B_KN>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* As = reinterpret_cast<uint16_t*>(smem);                 // [2][128][72]
-    uint16_t* Bs = As + 2 * kGM * kGAStride;                          // [2][128][72] / [2][64][136]
-    constexpr int kBBuf = B_KN ? kGK * kGBnStride : kGN * kGAStride;
 
     const int z = blockIdx.y;
     const int z1 = z / a.zdiv, z2 = z - z1 * a.zdiv;
@@ -64,48 +84,39 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
     const int m = lane & 15, g = lane >> 4;
 
-    // Staging: A (and an N x K B) rows tid/8 + 32 i, 8 elements at (tid%8)*8;
-    // a K x N B: k-rows tid/16 + 16 i, 8 columns at (tid%16)*8. Rows of A
-    // past M are zero.
-    const int ar = tid >> 3, ac = (tid & 7) * 8;
-    const int br = tid >> 4, bc = (tid & 15) * 8;
-    const uint16_t* arow[4];
-    bool aval[4];
+    // LDS tiles, filled straight from global memory (lane l of a wave
+    // instruction writes bytes 16 l .. 16 l + 15 of that instruction's 1 KiB).
+    //  - 128 x 32 tiles (A; B stored N x K): 64-byte rows of four 16-byte
+    //    chunks, chunk c of row r at position c ^ ((r >> 2) & 3), so the 16
+    //    rows of an MFMA operand read fall on distinct banks. Instruction j
+    //    of wave w fills rows 16 (4 j + w) .. +15.
+    //  - 32 x 128 tiles (B stored K x N): 256-byte rows of sixteen chunks,
+    //    chunk c of row r at position c ^ (2 (r & 3)); instruction j of wave
+    //    w fills rows 4 (4 j + w) .. +3.
+    // Source addresses of this thread's four loads (k offset added per slice);
+    // A rows past M load row M - 1 (their products are never stored).
+    const uint16_t* srcA[2];
+    const uint16_t* srcB[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = m0 + ar + 32 * i;
-        aval[i] = row < a.M;
-        arow[i] = A + static_cast<int64_t>(aval[i] ? row : 0) * a.lda + ac;
+    for (int j = 0; j < 2; ++j) {
+        const int r = 16 * (4 * j + wave) + (lane >> 2), p = lane & 3;
+        const int c = p ^ ((r >> 2) & 3);
+        srcA[j] = A + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.lda + 8 * c;
+        if (!B_KN) {
+            srcB[j] = B + static_cast<int64_t>(n0 + r) * a.ldb + 8 * c;
+        } else {
+            const int kr = 4 * (4 * j + wave) + (lane >> 4), pb = lane & 15;
+            srcB[j] = B + static_cast<int64_t>(kr) * a.ldb + n0 + 8 * (pb ^ (2 * (kr & 3)));
+        }
     }
-    u32x4 ga[4], gb[4];
-    auto load = [&](int k0) {
+    auto issue = [&](int kt) {
+        unsigned char* st = smem + (kt % kGStages) * kGStageBytes;
+        const int64_t kA = static_cast<int64_t>(kt) * kGK;
+        const int64_t kB = B_KN ? kA * a.ldb : kA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ga[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);   // row 0 past M
-            if (!aval[i]) ga[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (!B_KN)
-                gb[i] = *reinterpret_cast<const u32x4*>(
-                    B + static_cast<int64_t>(n0 + ar + 32 * i) * a.ldb + k0 + ac);
-            else
-                gb[i] = *reinterpret_cast<const u32x4*>(
-                    B + static_cast<int64_t>(k0 + br + 16 * i) * a.ldb + n0 + bc);
-        }
-    };
-    auto store = [&](int buf) {
-        uint16_t* as = As + buf * kGM * kGAStride;
-        uint16_t* bs = Bs + buf * kBBuf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(as + (ar + 32 * i) * kGAStride + ac) = ga[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (!B_KN)
-                *reinterpret_cast<u32x4*>(bs + (ar + 32 * i) * kGAStride + ac) = gb[i];
-            else
-                *reinterpret_cast<u32x4*>(bs + (br + 16 * i) * kGBnStride + bc) = gb[i];
+        for (int j = 0; j < 2; ++j) {
+            load_to_lds(srcA[j] + kA, st + (4 * j + wave) * 1024);
+            load_to_lds(srcB[j] + kB, st + kGTileBytes + (4 * j + wave) * 1024);
         }
     };
 
@@ -115,45 +126,47 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // transposing-read address inside a 4 x 16 block (K x N tiles)
-    const int tr_off = ((lane >> 2) & 3) * kGBnStride + 4 * (lane & 3);
+    // operand read offsets (bytes within a stage)
+    const int swzA = (m >> 2) & 3;
+    const int offA = (64 * wm + m) * 64 + 16 * (g ^ swzA);            // + 16 i rows: + 1024 i
+    const int offBnt = kGTileBytes + (64 * wn + m) * 64 + 16 * (g ^ swzA);
+    // K x N: lane 4e + q of group g reads row 8g + e (and 8g + 4 + e),
+    // columns 64 wn + 16 j + 4q: chunk 8 wn + 2 j + q / 2, half q % 2
+    const int e = (lane >> 2) & 3, q = lane & 3;
+    const int offBkn = kGTileBytes + (8 * g + e) * 256 + 8 * (q & 1);
+    const int cBkn = 8 * wn + (q >> 1);
+
     const int nk = a.K / kGK;
-    load(0);
-    store(0);
-    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kGStages - 1; ++s)
+        if (s < nk) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        // the last step reloads its own slice (no branch around the loads)
-        load(min(kt + 1, nk - 1) * kGK);
-        const uint16_t* as = As + buf * kGM * kGAStride;
-        const uint16_t* bs = Bs + buf * kBBuf;
+        // slice kt has landed once at most (stages - 2) later slices are in flight
+        if (kt + kGStages - 2 < nk) wait_vmcnt<kGLoads * (kGStages - 2)>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + kGStages - 1 < nk) issue(kt + kGStages - 1);
+        const unsigned char* st = smem + (kt % kGStages) * kGStageBytes;
+        bf16x8 av[4], bv[4];
 #pragma unroll
-        for (int ks = 0; ks < kGK / 32; ++ks) {
-            bf16x8 av[4], bv[4];
+        for (int i = 0; i < 4; ++i)
+            av[i] = *reinterpret_cast<const bf16x8*>(st + offA + 1024 * i);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *reinterpret_cast<const bf16x8*>(as + (64 * wm + 16 * i + m) * kGAStride +
-                                                         32 * ks + 8 * g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!B_KN) {
-                    bv[j] = *reinterpret_cast<const bf16x8*>(
-                        bs + (64 * wn + 16 * j + m) * kGAStride + 32 * ks + 8 * g);
-                } else {
-                    // lane (column n, group g) gets k = 8g..8g+3, then 8g+4..8g+7
-                    const uint16_t* p = bs + (32 * ks + 8 * g) * kGBnStride + 64 * wn + 16 * j + tr_off;
-                    const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
-                    const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 4 * kGBnStride));
-                    bv[j] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                }
+        for (int j = 0; j < 4; ++j) {
+            if (!B_KN) {
+                bv[j] = *reinterpret_cast<const bf16x8*>(st + offBnt + 1024 * j);
+            } else {
+                const int pos = (cBkn + 2 * j) ^ (2 * e);
+                const uint16_t* p = reinterpret_cast<const uint16_t*>(st + offBkn + 16 * pos);
+                const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
+                const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 4 * 128));
+                bv[j] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(bv[j], av[i], acc[i][j]);
         }
-        store(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(bv[j], av[i], acc[i][j]);
     }
 
     // lane holds C[64 wm + 16 i + m][64 wn + 16 j + 4 g + 0..3]

@@ -26,7 +26,9 @@
 //     read), then per wave
 //       S^T = K Q^T    bf16 MFMA 16x16x32, keys x rows, Q^T held in VGPRs,
 //                      each K operand read once for both row groups;
-//       online softmax per row (masked scores are -inf), in log2 units,
+//       online softmax per row (masked scores are -inf; a wave whose rows
+//                      select the whole tile skips the mask tests), in log2
+//                      units with the scale folded into the exponent's fma,
 //                      against a reference maximum that moves only when the
 //                      running maximum passes it by 8;
 //       O^T += V^T P^T P^T straight from the S^T registers (the key order
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
         for (int t2 = 0; t2 < 8; ++t2) acc[qg][t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f}, lr_run[2] = {0.0f, 0.0f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
 
     const int4* tl = tiles + static_cast<int64_t>(qtg) * (nkt + 1);
     const int ntile = tl[0].x;
@@ -245,48 +247,62 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
         bf16x8 pv[2][2];
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg) {
+            // raw scores (the scale goes into the exponent's fma); positions
+            // the row does not select are -inf
             float z[16];
-            float tmax = -INFINITY;
+            const uint32_t gm = 0x000F000Fu << (4 * g);
+            const bool full = ((mcur[qg].x & gm) == gm) && ((mcur[qg].y & gm) == gm);
+            if (__ballot(!full) == 0) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const uint32_t word = st < 2 ? mcur[qg].x : mcur[qg].y;
-                const uint32_t nib = (word >> ((16 * st + 4 * g) & 31)) & 0xFu;
+                for (int st = 0; st < 4; ++st)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    z[4 * st + i] = (nib >> i) & 1u ? s[qg][st][i] * scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, z[4 * st + i]);
+                    for (int i = 0; i < 4; ++i) z[4 * st + i] = s[qg][st][i];
+            } else {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const uint32_t word = st < 2 ? mcur[qg].x : mcur[qg].y;
+                    const uint32_t nib = (word >> ((16 * st + 4 * g) & 31)) & 0xFu;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        z[4 * st + i] = (nib >> i) & 1u ? s[qg][st][i] : -INFINITY;
                 }
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            float zmax = z[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) zmax = fmaxf(zmax, z[i]);
+            zmax = fmaxf(zmax, __shfl_xor(zmax, 16));
+            zmax = fmaxf(zmax, __shfl_xor(zmax, 32));
+            const float tmax = zmax * scale_log2;
             if (tmax > m_run[qg] + 8.0f) {
                 const float corr = (m_run[qg] == -INFINITY) ? 0.0f : exp2f(m_run[qg] - tmax);
                 l_run[qg] *= corr;
-                lr_run[qg] *= corr;
                 m_run[qg] = tmax;
                 if (__ballot(corr != 1.0f)) {
 #pragma unroll
                     for (int t2 = 0; t2 < 8; ++t2) acc[qg][t2] *= corr;
                 }
             }
-            const bool live = m_run[qg] != -INFINITY;
-            float psum = 0.0f, prsum = 0.0f;
+            // exp2(scale z - m); before any selected position m is -inf and
+            // every z is -inf: an offset of 0 keeps p = 0
+            const float moff = m_run[qg] == -INFINITY ? 0.0f : -m_run[qg];
+            float psum = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < 8; i += 2) {
                     // k slot 8g + i of the value product: key 32 kk + 4 g + i
                     // (i < 4) or 32 kk + 16 + 4 g + i - 4
-                    const float zz = z[4 * (2 * kk + (i >> 2)) + (i & 3)];
-                    const float pe = live ? __builtin_amdgcn_exp2f(zz - m_run[qg]) : 0.0f;
-                    const __bf16 pb = static_cast<__bf16>(pe);
-                    pv[qg][kk][i] = pb;
-                    psum += pe;
-                    prsum += static_cast<float>(pb);
+                    const float z0 = z[4 * (2 * kk + (i >> 2)) + (i & 3)];
+                    const float z1 = z[4 * (2 * kk + (i >> 2)) + (i & 3) + 1];
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(z0, scale_log2, moff));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(z1, scale_log2, moff));
+                    const bf16x2 pb = __builtin_bit_cast(bf16x2, pack_bf16x2(p0, p1));
+                    pv[qg][kk][i] = pb[0];
+                    pv[qg][kk][i + 1] = pb[1];
+                    psum += p0 + p1;
                 }
             }
             l_run[qg] += psum;
-            lr_run[qg] += prsum;
         }
 
         // O^T += V^T P^T
@@ -307,7 +323,7 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     // lane holds O^T[16 t2 + 4 g + i][row m of group qg]
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
-        float lr_tot = lr_run[qg] + __shfl_xor(lr_run[qg], 16);
+        float lr_tot = l_run[qg] + __shfl_xor(l_run[qg], 16);
         lr_tot += __shfl_xor(lr_tot, 32);
         if (!rv[qg]) continue;
         const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;

@@ -31,6 +31,11 @@ def test_library_exports_every_declared_function():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (dsa_\w+)$", out, re.M))
     assert set(names) <= exported
+    # every kernel and helper of the library is defined in it (a kernel
+    # template the host pass failed to instantiate would be left undefined)
+    undef = subprocess.run(["nm", "-D", "--undefined-only", dsa.LIB_PATH], capture_output=True,
+                           text=True, check=True).stdout
+    assert not re.findall(r"_ZN3dsa\w*", undef), undef
 
 
 def test_abi_version_and_status_strings():
