@@ -546,7 +546,9 @@ def prefill_leg(reps=20):
                   "kv_up": 2.0 * T * 512 * Hq * 256 / 1e12}
     mha_tflop = 2.0 * Hq * (192 + 128) * sel / 1e12
     # executed work: every listed 64-position tile of each 128-row query tile
-    tl = hws[dsa.sparse_mha_tiles_offset(1, T, T):].view(torch.int32).view(-1, T // 64 + 1, 4)
+    toff = dsa.sparse_mha_tiles_offset(1, T, T)
+    nqt = T // 128
+    tl = hws[toff:toff + nqt * (T // 64 + 1) * 16].view(torch.int32).view(nqt, T // 64 + 1, 4)
     ntiles = int(tl[:, 0, 0].sum().item())
     mha_exec_tflop = 2.0 * Hq * (192 + 128) * 128 * 64 * ntiles / 1e12
     mha_tfs = mha_tflop / (us["sparse_mha"] * 1e-6)

@@ -388,7 +388,8 @@ dsa_status dsa_mla_absorb_o(const dsa_mla_proj_args* args, hipStream_t stream);
  * B*S <= 2^26; pointers 16-byte aligned (idx, pos 4), rope strides multiples
  * of 8 elements. scale > 0 and finite.
  * Workspace: dsa_sparse_mha_workspace() bytes, 256-byte aligned (per-row
- * bit masks and per-128-row key-tile lists); contents on entry do not matter.
+ * bit masks, per-128-row key-tile lists and 256 zero bytes the call writes
+ * itself); contents on entry do not matter.
  * ---------------------------------------------------------------------- */
 typedef struct dsa_mha_args {
     int32_t B, S, Hq, Lmax, K;

@@ -536,7 +536,8 @@ def sparse_mha_tiles_offset(B: int, S: int, Lmax: int) -> int:
     """Byte offset of the key-tile lists inside the workspace: after the bit
     masks ([B*S][2*ceil(Lmax/64)] words), rounded up to 256. The lists are
     [B*ceil(S/128)][ceil(Lmax/64) + 1] int4: entry 0 holds the count, then
-    (tile, union bits low, union bits high, 0)."""
+    (tile, union bits low, union bits high, 0); 256 zero bytes follow them
+    (at the next multiple of 256)."""
     nkt = (Lmax + 63) // 64
     return (B * S * 2 * nkt * 4 + 255) // 256 * 256
 

@@ -20,10 +20,11 @@
 //     128-row query tile, lists the 64-position key tiles that any of its
 //     rows selects, with the union of the rows' bits.
 //  2. sparse_mha_kernel: one block of 4 waves per (query tile, head); wave w
-//     serves rows 32w..32w+31 as two 16-row groups. For each listed key tile
-//     the block gathers the head's 64 key/value rows into an LDS tile
-//     [64][k_nope | k_pe | v] (positions no row selects are zero and not
-//     read), then per wave
+//     serves rows 32w..32w+31 as two 16-row groups. The head's 64 key/value
+//     rows of each listed key tile go straight from global memory into one
+//     of two LDS tile buffers (direct loads, no registers; positions no row
+//     selects load zeros): the next tile's loads are issued before the
+//     current tile is computed. Per wave and tile:
 //       S^T = K Q^T    bf16 MFMA 16x16x32, keys x rows, Q^T held in VGPRs,
 //                      each K operand read once for both row groups;
 //       online softmax per row (masked scores are -inf; a wave whose rows
@@ -34,10 +35,12 @@
 //       O^T += V^T P^T P^T straight from the S^T registers (the key order
 //                      inside the MFMA's K dimension only has to agree
 //                      between the operands), V^T by the transposing LDS
-//                      read from the row-major tile.
-//     Two blocks share a CU and hide each other's gathers. Launch order: with Hq a multiple of 8, each XCD takes
-//     whole heads, so one head's keys and values stay in its L2; within a
-//     head the query tiles with the longest causal extent go first.
+//                      read from the row-major value rows.
+//     Tile rows are stored with XOR-swizzled 16-byte chunks so the operand
+//     reads hit distinct banks. Launch order: with Hq a multiple of 8, each
+//     XCD takes whole heads, so one head's keys and values stay in its L2;
+//     within a head the query tiles with the longest causal extent go
+//     first.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -45,7 +48,11 @@ namespace dsa {
 constexpr int kMhaRows = 128;           // query rows per block
 constexpr int kMhaKeys = 64;            // positions per key tile
 constexpr int kMhaThreads = 256;
-constexpr int kMhaRS = 320 + 8;         // bf16 per LDS key row: k_nope 0..127, k_pe 128..191, v 192..319
+// LDS tile buffer: k_nope [64][256 B], k_pe [64][128 B], v [64][256 B]
+constexpr int kMhaKP = 64 * 256, kMhaV = kMhaKP + 64 * 128;
+constexpr int kMhaTileBytes = kMhaV + 64 * 256;
+constexpr int kMhaLoads = kMhaTileBytes / 1024 / 4;   // direct loads per thread per tile (10)
+constexpr size_t kMhaLds = 2 * static_cast<size_t>(kMhaTileBytes);
 constexpr int kMaskThreads = 256;
 
 // ---- 1. bit masks and key-tile lists ---------------------------------------
@@ -53,7 +60,8 @@ constexpr int kMaskThreads = 256;
 // the tile's union row (5 * nw words).
 __global__ __launch_bounds__(kMaskThreads) void selection_mask_kernel(
     int S, int Lmax, int K, int nkt, int ntq, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ pos, uint32_t* __restrict__ mask, int4* __restrict__ tiles) {
+    const int32_t* __restrict__ pos, uint32_t* __restrict__ mask, int4* __restrict__ tiles,
+    uint16_t* __restrict__ zeros) {
     extern __shared__ uint32_t msm[];
     const int nw = 2 * nkt;
     uint32_t* tun = msm + 4 * nw;
@@ -62,6 +70,8 @@ __global__ __launch_bounds__(kMaskThreads) void selection_mask_kernel(
     const int64_t b = qt / ntq;
     const int t0 = (qt % ntq) * kMhaRows;
     for (int i = tid; i < nw; i += kMaskThreads) tun[i] = 0u;
+    // 256 zero bytes: the source of unselected positions in the attention gather
+    if (qt == 0 && tid < 16) reinterpret_cast<uint4*>(zeros)[tid] = make_uint4(0u, 0u, 0u, 0u);
     uint32_t* rb = msm + wave * nw;
     for (int it = 0; it < kMhaRows / 4; ++it) {
         const int t = t0 + 4 * it + wave;
@@ -120,12 +130,27 @@ __global__ __launch_bounds__(kMaskThreads) void selection_mask_kernel(
 }
 
 // ---- 2. attention over the listed key tiles ---------------------------------
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// bytes 16 l .. 16 l + 15 after the wave-uniform LDS address `dst`.
+__device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* dst) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(
+        src, reinterpret_cast<lds_void*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
+                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))),
+        16, 0, 0);
+}
+
+// wait until every vector-memory load of this wave has completed
+__device__ __forceinline__ void wait_vmcnt0() {
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
+
 __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     int S, int Hq, int Lmax, int nkt, int ntq, int nqt, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ rope, int64_t rope_rs,
     int64_t rope_bs, const uint32_t* __restrict__ mask, const int4* __restrict__ tiles,
-    float scale_log2, uint16_t* __restrict__ out) {
-    __shared__ __align__(16) uint16_t Kt[kMhaKeys * kMhaRS];
+    const uint16_t* __restrict__ zeros, float scale_log2, uint16_t* __restrict__ out) {
+    extern __shared__ __align__(16) unsigned char kvs[];     // two tile buffers
 
     // launch index -> (head, query tile); longest causal extent first
     const int L = blockIdx.x;
@@ -175,57 +200,75 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     const int4* tl = tiles + static_cast<int64_t>(qtg) * (nkt + 1);
     const int ntile = tl[0].x;
 
-    // gather: key row tid/4, quarter sub = tid%4: kv chunks sub + 4i (i < 8)
-    // and rope chunks sub, sub + 4 (16 bytes each)
-    const int gkey = tid >> 2, gsub = tid & 3;
-    u32x4 G[10];
+    // Gather: direct global-to-LDS loads (lane l of a wave instruction
+    // writes bytes 16 l .. +15 of that instruction's 1 KiB). Regions of a
+    // tile buffer, with 16-byte chunk c of row r stored at position c ^ f(r):
+    //   k_nope rows of 16 chunks, f = r & 15            (instructions 0..15, 4 rows each)
+    //   k_pe   rows of  8 chunks, f = (r >> 1) & 7      (16..23, 8 rows each)
+    //   v      rows of 16 chunks, f = 2 (r & 3) | 8 ((r >> 2) & 1)   (24..39)
+    // so that the 16 rows of a K operand read, and the rows of a transposing
+    // V read, fall on distinct banks. Wave w issues instructions w + 4 i;
+    // the chunk a lane loads does not depend on i. Positions no row of the
+    // query tile selects load 16 zero bytes.
+    const int rq = lane >> 4, r8 = lane >> 3;
+    const int cKN = (lane & 15) ^ ((4 * wave + rq) & 15);
+    const int cKP = (lane & 7) ^ ((4 * wave + rq) & 7);
+    const int cV = (lane & 15) ^ (2 * rq | 8 * (wave & 1));
     uint2 mw[2];
     const uint16_t* kv_bh = kv + (b * Lmax * Hq + h) * 256;
     const uint16_t* rope_b = rope + b * rope_bs;
-    auto fetch = [&](int it) {
+    const int64_t kv_rs = static_cast<int64_t>(Hq) * 256;
+    auto issue = [&](int it) {
         const int4 e = tl[1 + it];
         const int kt = e.x;
-        const uint32_t u = gkey < 32 ? static_cast<uint32_t>(e.y) >> gkey
-                                     : static_cast<uint32_t>(e.z) >> (gkey - 32);
-        // positions no row of the tile selects (and those past Lmax) read
-        // position 0 and are zeroed
-        const bool live = (u & 1u) != 0u;
-        const int s = live ? kt * kMhaKeys + gkey : 0;
-        const uint16_t* krow = kv_bh + static_cast<int64_t>(s) * Hq * 256 + 8 * gsub;
-        const uint16_t* prow = rope_b + static_cast<int64_t>(s) * rope_rs + 8 * gsub;
+        unsigned char* buf = kvs + (it & 1) * kMhaTileBytes;
+        const int64_t s0 = static_cast<int64_t>(kt) * kMhaKeys;
+        // the source, or the zero bytes for a position no row selects (a
+        // select on the address, so every lane issues the same loads)
+        auto pick = [&](int r, const uint16_t* src) {
+            const uint32_t bit = (r < 32 ? static_cast<uint32_t>(e.y) >> r
+                                         : static_cast<uint32_t>(e.z) >> (r - 32)) & 1u;
+            const uint64_t a = reinterpret_cast<uint64_t>(src), zz = reinterpret_cast<uint64_t>(zeros);
+            return reinterpret_cast<const uint16_t*>(zz ^ ((a ^ zz) & (0ull - bit)));
+        };
 #pragma unroll
-        for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const u32x4*>(krow + 32 * i);
-        G[8] = *reinterpret_cast<const u32x4*>(prow);
-        G[9] = *reinterpret_cast<const u32x4*>(prow + 32);
-        if (!live) {
+        for (int i = 0; i < 4; ++i) {                     // k_nope: rows 4 n + lane / 16
+            const int r = 4 * wave + 16 * i + rq;
+            const uint16_t* src = kv_bh + (s0 + r) * kv_rs + 8 * cKN;
+            load_to_lds(pick(r, src), buf + 1024 * (wave + 4 * i));
+        }
 #pragma unroll
-            for (int i = 0; i < 10; ++i) G[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 2; ++i) {                     // k_pe: rows 8 n' + lane / 8
+            const int r = 8 * wave + 32 * i + r8;
+            const uint16_t* src = rope_b + (s0 + r) * rope_rs + 8 * cKP;
+            load_to_lds(pick(r, src), buf + kMhaKP + 1024 * (wave + 4 * i));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {                     // v: rows 4 n'' + lane / 16
+            const int r = 4 * wave + 16 * i + rq;
+            const uint16_t* src = kv_bh + (s0 + r) * kv_rs + 128 + 8 * cV;
+            load_to_lds(pick(r, src), buf + kMhaV + 1024 * (wave + 4 * i));
         }
 #pragma unroll
         for (int qg = 0; qg < 2; ++qg)
             mw[qg] = rv[qg] ? *reinterpret_cast<const uint2*>(mask + rr[qg] * nw + 2 * kt)
                             : make_uint2(0u, 0u);
     };
-    auto store = [&]() {
-        uint16_t* dst = Kt + gkey * kMhaRS + 8 * gsub;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 32 * i) = G[i];        // k_nope
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 192 + 32 * i) = G[4 + i];  // v
-        *reinterpret_cast<u32x4*>(dst + 128) = G[8];                                      // k_pe
-        *reinterpret_cast<u32x4*>(dst + 160) = G[9];
-    };
 
-    // transposing-read address: lane 4e+q of group g reads v features 4q..
-    // of key 4g+e (and 16+4g+e) inside a 32-key half
-    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kMhaRS + 192 + 4 * (lane & 3);
+    // operand reads: K rows 16 st + m; V^T transposing reads, lane 4e+q of
+    // group g: rows 4g + e (+16) of a 32-key half, value chunk 2 t2 + q/2,
+    // half q % 2
+    const int e4 = (lane >> 2) & 3, q4 = lane & 3;
+    const int fv = 2 * e4 | 8 * (g & 1);
+    const int vrow = kMhaV + (4 * g + e4) * 256 + 8 * (q4 & 1);
 
+    if (ntile > 0) issue(0);
     for (int it = 0; it < ntile; ++it) {
-        __syncthreads();                               // previous tile consumed
-        fetch(it);
-        store();
+        wait_vmcnt0();                                 // this tile's loads (own)
+        __builtin_amdgcn_s_barrier();                  // everyone's; previous tile consumed
         const uint2 mcur[2] = {mw[0], mw[1]};
-        __syncthreads();
+        if (it + 1 < ntile) issue(it + 1);
+        const unsigned char* Kt = kvs + (it & 1) * kMhaTileBytes;
 
         // S^T: s[qg][st] for keys 16 st + 4 g + i, row m of group qg
         v4f s[2][4];
@@ -237,8 +280,11 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
         for (int ks = 0; ks < 6; ++ks) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(
-                    Kt + (16 * st + m) * kMhaRS + 32 * ks + 8 * g);
+                const int row = 16 * st + m;
+                const unsigned char* kp =
+                    ks < 4 ? Kt + row * 256 + 16 * ((4 * ks + g) ^ m)
+                           : Kt + kMhaKP + row * 128 + 16 * ((4 * (ks - 4) + g) ^ ((m >> 1) & 7));
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kp);
                 s[0][st] = mfma_bf16_16x16x32(kop, qreg[0][ks], s[0][st]);
                 s[1][st] = mfma_bf16_16x16x32(kop, qreg[1][ks], s[1][st]);
             }
@@ -310,9 +356,11 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int t2 = 0; t2 < 8; ++t2) {
-                const uint16_t* p = Kt + 32 * kk * kMhaRS + tr_off + 16 * t2;
-                const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
-                const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 16 * kMhaRS));
+                const int c = 2 * t2 + (q4 >> 1);
+                const unsigned char* p = Kt + 32 * kk * 256 + vrow + 16 * (c ^ fv);
+                const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(reinterpret_cast<const uint16_t*>(p)));
+                const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(
+                    reinterpret_cast<const uint16_t*>(p + 16 * 256)));
                 const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 acc[0][t2] = mfma_bf16_16x16x32(va, pv[0][kk], acc[0][t2]);
                 acc[1][t2] = mfma_bf16_16x16x32(va, pv[1][kk], acc[1][t2]);
@@ -344,28 +392,35 @@ size_t mha_workspace_bytes(int B, int S, int Lmax) {
     const int64_t ntq = (S + kMhaRows - 1) / kMhaRows;
     const size_t maskb = static_cast<size_t>(B) * S * 2 * nkt * sizeof(uint32_t);
     const size_t tl = static_cast<size_t>(B) * ntq * (nkt + 1) * sizeof(int4);
-    return (maskb + 255) / 256 * 256 + tl;
+    return (maskb + 255) / 256 * 256 + (tl + 255) / 256 * 256 + 256;
 }
 
 hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
                              const uint16_t* kv, const uint16_t* rope, int64_t rope_rs,
                              int64_t rope_bs, const int32_t* idx, const int32_t* pos, float scale,
                              uint16_t* out, void* workspace, hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&sparse_mha_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMhaLds));
+    if (attr != hipSuccess) return attr;
     const int nkt = (Lmax + kMhaKeys - 1) / kMhaKeys;
     const int ntq = (S + kMhaRows - 1) / kMhaRows;
     const int nqt = B * ntq;
     const size_t maskb = static_cast<size_t>(B) * S * 2 * nkt * sizeof(uint32_t);
-    uint32_t* mask = static_cast<uint32_t*>(workspace);
-    int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + (maskb + 255) / 256 * 256);
+    const size_t tlb = static_cast<size_t>(nqt) * (nkt + 1) * sizeof(int4);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* mask = reinterpret_cast<uint32_t*>(ws);
+    int4* tiles = reinterpret_cast<int4*>(ws + (maskb + 255) / 256 * 256);
+    uint16_t* zeros = reinterpret_cast<uint16_t*>(ws + (maskb + 255) / 256 * 256 + (tlb + 255) / 256 * 256);
     const size_t lds = sizeof(uint32_t) * 5 * 2 * nkt;
     hipLaunchKernelGGL(selection_mask_kernel, dim3(static_cast<unsigned>(nqt)), dim3(kMaskThreads),
-                       lds, stream, S, Lmax, K, nkt, ntq, idx, pos, mask, tiles);
+                       lds, stream, S, Lmax, K, nkt, ntq, idx, pos, mask, tiles, zeros);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL(sparse_mha_kernel, dim3(static_cast<unsigned>(nqt * Hq)), dim3(kMhaThreads),
-                       0, stream, S, Hq, Lmax, nkt, ntq, nqt, q, kv, rope, rope_rs, rope_bs, mask,
-                       tiles, scale_log2, out);
+                       kMhaLds, stream, S, Hq, Lmax, nkt, ntq, nqt, q, kv, rope, rope_rs, rope_bs,
+                       mask, tiles, zeros, scale_log2, out);
     return hipGetLastError();
 }
 
