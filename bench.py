@@ -58,6 +58,8 @@ def parse():
                     help="skip the prefill leg (T = 4096 causal queries, per-call TFLOP/s)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="add the supplementary batch sweep (B = 1..64 rows at L = 16384)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy five times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -295,6 +297,17 @@ def measure(wl, st, steps, warmup):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
 
+    # distribution of single steps: a second pass with an event between steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        step_graphs[i % R].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(steps)])
+    quantiles = {k: round(float(np.percentile(per_step_us, q)), 2)
+                 for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     # per-call device time: each call graph runs the call once per replica
     reps_call = max(1, (steps + R - 1) // R)
     avg_us = {}
@@ -315,7 +328,7 @@ def measure(wl, st, steps, warmup):
     ab = algorithmic_bytes(wl, n_valid, keff)
     dom = max(avg_us, key=avg_us.get)
     ms_per_step = total_ms / steps
-    return dict(ab=ab, dom=dom, avg_us=avg_us, ms_per_step=ms_per_step,
+    return dict(ab=ab, dom=dom, avg_us=avg_us, ms_per_step=ms_per_step, quantiles=quantiles,
                 achieved=ab[dom] / (avg_us[dom] * 1e-6) / 1e9,
                 value=wl.B * wl.S * steps / (total_ms / 1000.0),
                 step_hbm_frac=round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
@@ -337,6 +350,7 @@ def other_workloads_leg(args):
         out[name] = {
             "value": round(m["value"], 1), "unit": "queries/s",
             "ms_per_step": round(m["ms_per_step"], 5),
+            "step_us_quantiles": m["quantiles"],
             "config": {"B": wl.B, "L": wl.Lmax, "topk": wl.K, "replicas": st["R"],
                        "replica_bytes": st["per_replica"]},
             "step_algorithmic_bytes": m["ab"]["step"],
@@ -345,6 +359,29 @@ def other_workloads_leg(args):
             "dominant": {"kernel": dom, "achieved_gbs": round(m["achieved"], 1),
                          "frac": round(m["achieved"] / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": m["ab"][dom]},
+        }
+        del st, m
+        torch.cuda.empty_cache()
+    return out
+
+
+def sweep_leg(args):
+    """Supplementary: decode16k's shapes at B = 1, 4, 16, 32, 64 rows (all at
+    L = 16384), to show where the single-row latency stops dominating."""
+    import torch
+
+    import synth
+
+    out = {}
+    for B in (1, 4, 16, 32, 64):
+        wl = synth.sweep_workload(B)
+        st = setup(wl, args.replica_bytes)
+        m = measure(wl, st, args.steps, args.warmup)
+        out[f"B={B}"] = {
+            "value": round(m["value"], 1), "unit": "queries/s",
+            "us_per_step": round(m["ms_per_step"] * 1000.0, 2),
+            "step_hbm_frac": m["step_hbm_frac"],
+            "call_avg_us": {k: round(v, 2) for k, v in m["avg_us"].items()},
         }
         del st, m
         torch.cuda.empty_cache()
@@ -615,9 +652,40 @@ def cpu_baseline(wl, x, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or done >= 1000:
             break
-    return dict(value=done / el, unit="queries/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{done} single-query decode steps of {wl.name} (batch row 0, "
-                       f"L={n}, H=64, top-{wl.K}, 128 heads) in {el:.1f} s")
+    cores = oracle.num_threads()
+    rec = dict(value=done / el, unit="queries/s", cores=cores, kind="oracle",
+               sample=f"{done} single-query decode steps of {wl.name} (batch row 0, "
+                      f"L={n}, H=64, top-{wl.K}, 128 heads) in {el:.1f} s")
+    # the same steps on one core, for a few seconds
+    oracle.set_num_threads(1)
+    try:
+        done1 = 0
+        t0 = time.perf_counter()
+        while True:
+            q8, qs, _ = oracle.indexer_prepare(x["q_raw"][b:b + 1], pos[..., None], cos, sin, True)
+            kd = oracle.dequantize(k8, ks)
+            sc = oracle.indexer_scores(oracle.dequantize(q8, qs), x["w"][b:b + 1], kd, pos + 1)
+            idx = oracle.topk(sc[0], pos[0] + 1, wl.K)[None]
+            oracle.sparse_mla(qm, lat, kpe, idx, wl.softmax_scale)
+            done1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= seconds / 3 or done1 >= 100:
+                break
+    finally:
+        oracle.set_num_threads(cores)
+    rec["one_core"] = {"value": done1 / el1, "sample": f"{done1} steps in {el1:.1f} s"}
+    rec["host"] = {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+    return rec
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ main --
@@ -672,6 +740,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "L": wl.Lmax, "indexer_heads": wl.H,
                    "attn_heads": wl.Hq, "topk": wl.K, "replicas": st["R"],
                    "replica_bytes": st["per_replica"], "launch": "one HIP graph per step"},
+        "step_us_quantiles": m["quantiles"],
         "step_algorithmic_bytes": ab["step"],
         "step_hbm_frac": m["step_hbm_frac"],
         "call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
@@ -687,6 +756,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_others:
         rec["other_workloads"] = other_workloads_leg(args)
+    if args.sweep:
+        rec["sweep"] = sweep_leg(args)
     if not args.no_prefill:
         rec["prefill"] = prefill_leg()
     if not args.no_cpu_baseline:

@@ -57,6 +57,7 @@ def _load():
         "orc_sparse_mha": (None, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _ptr,
                                   _ptr, _ptr, _ptr, _f64, _ptr]),
         "orc_num_threads": (_i32, []),
+        "orc_set_num_threads": (None, [_i32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -76,6 +77,11 @@ def _p(a):
 
 def num_threads() -> int:
     return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the following oracle calls use (OpenMP)."""
+    _load().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- dtypes --

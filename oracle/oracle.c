@@ -49,6 +49,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (n >= 1); no effect without OpenMP. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------
  * E4M3 codec [OFP8]; the format the indexer's "FP8" means [P1 TileLang
  * kernels paragraph, P4 act_quant call]. Sign bit, 4 exponent bits (bias 7),

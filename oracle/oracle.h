@@ -112,6 +112,7 @@ void orc_sparse_mha(int B, int S, int Hq, int Dn, int Dv, int Dr, int Lmax, int 
                     const int32_t* idx, const int32_t* pos, double scale, double* out);
 
 int orc_num_threads(void);
+void orc_set_num_threads(int n);   /* threads for later calls; n >= 1 */
 
 #ifdef __cplusplus
 }

@@ -68,8 +68,11 @@ __device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* 
         16, 0, 0);
 }
 
-template <bool B_KN>
+// MODE 0: kv up-projection, 1: query absorption (B stored K x N),
+// 2: output absorption; one instantiation each, so profiles tell them apart
+template <int MODE>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr bool B_KN = MODE == 1;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int z = blockIdx.y;
@@ -184,14 +187,14 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     }
 }
 
-template <bool B_KN>
+template <int MODE>
 static hipError_t run_gemm(const GemmArgs& a, int nbatch, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_kernel<B_KN>),
+        reinterpret_cast<const void*>(&gemm_bf16_kernel<MODE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
     if (attr != hipSuccess) return attr;
     const int ntiles = a.N / kGN;
-    hipLaunchKernelGGL(gemm_bf16_kernel<B_KN>, dim3(static_cast<unsigned>(a.mtiles * ntiles),
+    hipLaunchKernelGGL(gemm_bf16_kernel<MODE>, dim3(static_cast<unsigned>(a.mtiles * ntiles),
                                                     static_cast<unsigned>(nbatch)),
                        dim3(kGThreads), kGemmLds, stream, a);
     return hipGetLastError();
@@ -216,7 +219,7 @@ hipError_t launch_mla_proj(int mode, int B, int rows, int Hq, const uint16_t* wk
         a.a_s1 = xbs;
         a.B = wkv_b;
         a.c_s1 = ybs;
-        return run_gemm<false>(a, B, stream);
+        return run_gemm<0>(a, B, stream);
     }
     a.zdiv = Hq;
     a.a_s1 = xbs;
@@ -228,12 +231,12 @@ hipError_t launch_mla_proj(int mode, int B, int rows, int Hq, const uint16_t* wk
         a.N = 512;
         a.K = 128;
         a.B = wkv_b;                      // W_UK[h]: [128 (k)][512 (n)]
-        return run_gemm<true>(a, B * Hq, stream);
+        return run_gemm<1>(a, B * Hq, stream);
     }
     a.N = 128;
     a.K = 512;
     a.B = wkv_b + 128 * 512;              // W_UV[h]: [128 (n)][512 (k)]
-    return run_gemm<false>(a, B * Hq, stream);
+    return run_gemm<2>(a, B * Hq, stream);
 }
 
 }  // namespace dsa

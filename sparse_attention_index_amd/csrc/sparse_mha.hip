@@ -15,10 +15,11 @@
 //
 // Design. The masked dense form is computed, tile by tile, only where the
 // mask has something:
-//  1. selection_mask_kernel turns each row's list into a bit mask over
-//     positions (two 32-bit words per 64-position tile) and, for every
-//     128-row query tile, lists the 64-position key tiles that any of its
-//     rows selects, with the union of the rows' bits.
+//  1. selection_rows_kernel turns each row's list into a bit mask over
+//     positions (two 32-bit words per 64-position tile, one wave per row);
+//     tile_lists_kernel lists, for every 128-row query tile, the
+//     64-position key tiles that any of its rows selects, with the union of
+//     the rows' bits.
 //  2. sparse_mha_kernel: one block of 4 waves per (query tile, head); wave w
 //     serves rows 32w..32w+31 as two 16-row groups. The head's 64 key/value
 //     rows of each listed key tile go straight from global memory into one
@@ -56,60 +57,73 @@ constexpr size_t kMhaLds = 2 * static_cast<size_t>(kMhaTileBytes);
 constexpr int kMaskThreads = 256;
 
 // ---- 1. bit masks and key-tile lists ---------------------------------------
-// Grid: one block per query tile (B * ntq). LDS: one mask row per wave and
-// the tile's union row (5 * nw words).
-__global__ __launch_bounds__(kMaskThreads) void selection_mask_kernel(
-    int S, int Lmax, int K, int nkt, int ntq, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ pos, uint32_t* __restrict__ mask, int4* __restrict__ tiles,
-    uint16_t* __restrict__ zeros) {
+// 1a. One wave per query row: the row's list becomes a bit mask over
+// positions, built in LDS (one row per wave) and written out whole.
+constexpr int kMaskRowsPerBlock = kMaskThreads / 64;
+
+__global__ __launch_bounds__(kMaskThreads) void selection_rows_kernel(
+    int S, int Lmax, int K, int nw, int64_t nrows, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ pos, uint32_t* __restrict__ mask, uint16_t* __restrict__ zeros) {
     extern __shared__ uint32_t msm[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kMaskRowsPerBlock + wave;
+    const bool valid = r < nrows;
+    // 256 zero bytes: the source of unselected positions in the attention gather
+    if (blockIdx.x == 0 && tid < 16) reinterpret_cast<uint4*>(zeros)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t* rb = msm + wave * nw;
+    for (int i = lane; i < nw; i += 64) rb[i] = 0u;
+    __syncthreads();
+    if (valid) {
+        const int pr = pos != nullptr ? pos[r] : 0x7FFFFFFF;
+        const int32_t* sel = idx + r * K;
+        for (int j0 = 0; j0 < K; j0 += 64) {
+            const int j = j0 + lane;
+            const int p = j < K ? sel[j] : -1;
+            const bool ok = p >= 0 && p < Lmax && p <= pr;
+            // lanes holding the same word OR their bits towards the first
+            // lane of each run of equal words, which alone writes (fewer LDS
+            // atomics on one address); any order of the list is correct
+            int w = ok ? (p >> 5) : -1 - lane;
+            uint32_t bit = ok ? (1u << (p & 31)) : 0u;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t ob = static_cast<uint32_t>(__shfl_down(static_cast<int>(bit), d));
+                const int ow = __shfl_down(w, d);
+                if (ow == w) bit |= ob;
+            }
+            const int prev = __shfl_up(w, 1);
+            if (ok && (lane == 0 || prev != w)) atomicOr(&rb[w], bit);
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        uint32_t* mrow = mask + r * nw;
+        for (int i = lane; i < nw; i += 64) mrow[i] = rb[i];
+    }
+}
+
+// 1b. One block per 128-row query tile: the union of its rows' masks, then
+// the list of 64-position tiles with any bit set (entry 0: the count; then
+// (tile, union bits low, union bits high, 0) in ascending order).
+__global__ __launch_bounds__(kMaskThreads) void tile_lists_kernel(
+    int S, int nkt, int ntq, const uint32_t* __restrict__ mask, int4* __restrict__ tiles) {
+    extern __shared__ uint32_t tun[];
     const int nw = 2 * nkt;
-    uint32_t* tun = msm + 4 * nw;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qt = blockIdx.x;
     const int64_t b = qt / ntq;
     const int t0 = (qt % ntq) * kMhaRows;
+    const int t1 = min(S, t0 + kMhaRows);
+    const uint32_t* m0 = mask + (b * S + t0) * nw;
     for (int i = tid; i < nw; i += kMaskThreads) tun[i] = 0u;
-    // 256 zero bytes: the source of unselected positions in the attention gather
-    if (qt == 0 && tid < 16) reinterpret_cast<uint4*>(zeros)[tid] = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t* rb = msm + wave * nw;
-    for (int it = 0; it < kMhaRows / 4; ++it) {
-        const int t = t0 + 4 * it + wave;
-        const bool valid = t < S;
-        const int64_t r = b * S + t;
-        for (int i = lane; i < nw; i += 64) rb[i] = 0u;
-        __syncthreads();
-        if (valid) {
-            const int pr = pos != nullptr ? pos[r] : 0x7FFFFFFF;
-            const int32_t* sel = idx + r * K;
-            for (int j0 = 0; j0 < K; j0 += 64) {
-                const int j = j0 + lane;
-                const int p = j < K ? sel[j] : -1;
-                const bool ok = p >= 0 && p < Lmax && p <= pr;
-                // lanes holding the same word OR their bits towards the first
-                // lane of each run of equal words, which alone writes (fewer
-                // LDS atomics on the same address); any order is correct
-                int w = ok ? (p >> 5) : -1 - lane;
-                uint32_t bit = ok ? (1u << (p & 31)) : 0u;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint32_t ob = static_cast<uint32_t>(__shfl_down(static_cast<int>(bit), d));
-                    const int ow = __shfl_down(w, d);
-                    if (ow == w) bit |= ob;
-                }
-                const int prev = __shfl_up(w, 1);
-                if (ok && (lane == 0 || prev != w)) atomicOr(&rb[w], bit);
-            }
-        }
-        __syncthreads();
-        if (valid) {
-            uint32_t* mrow = mask + r * nw;
-            for (int i = lane; i < nw; i += 64) {
-                const uint32_t v = rb[i];
-                mrow[i] = v;
-                if (v) atomicOr(&tun[i], v);
-            }
-        }
+    __syncthreads();
+    // G row groups per word when the words are fewer than the threads
+    const int G = max(1, kMaskThreads / nw);
+    for (int x = tid; x < nw * G; x += kMaskThreads) {
+        const int i = x % nw, g0 = x / nw;
+        uint32_t u = 0u;
+        for (int t = g0; t < t1 - t0; t += G) u |= m0[static_cast<int64_t>(t) * nw + i];
+        if (u) atomicOr(&tun[i], u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -412,10 +426,17 @@ hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16
     uint32_t* mask = reinterpret_cast<uint32_t*>(ws);
     int4* tiles = reinterpret_cast<int4*>(ws + (maskb + 255) / 256 * 256);
     uint16_t* zeros = reinterpret_cast<uint16_t*>(ws + (maskb + 255) / 256 * 256 + (tlb + 255) / 256 * 256);
-    const size_t lds = sizeof(uint32_t) * 5 * 2 * nkt;
-    hipLaunchKernelGGL(selection_mask_kernel, dim3(static_cast<unsigned>(nqt)), dim3(kMaskThreads),
-                       lds, stream, S, Lmax, K, nkt, ntq, idx, pos, mask, tiles, zeros);
+    const int nw = 2 * nkt;
+    const int64_t nrows = static_cast<int64_t>(B) * S;
+    hipLaunchKernelGGL(selection_rows_kernel,
+                       dim3(static_cast<unsigned>((nrows + kMaskRowsPerBlock - 1) / kMaskRowsPerBlock)),
+                       dim3(kMaskThreads), sizeof(uint32_t) * kMaskRowsPerBlock * nw, stream, S, Lmax,
+                       K, nw, nrows, idx, pos, mask, zeros);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tile_lists_kernel, dim3(static_cast<unsigned>(nqt)), dim3(kMaskThreads),
+                       sizeof(uint32_t) * nw, stream, S, nkt, ntq, mask, tiles);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL(sparse_mha_kernel, dim3(static_cast<unsigned>(nqt * Hq)), dim3(kMhaThreads),

@@ -84,6 +84,13 @@ def workload(name: str) -> Workload:
 WORKLOADS = ("tiny", "decode16k", "batch32", "prefill4k", "decode128k")
 
 
+def sweep_workload(B: int) -> Workload:
+    """Supplementary batch sweep: decode16k's shapes with B rows, every row at
+    L = 16384 (seed 5)."""
+    return Workload(f"sweep-b{B}", 5, B=B, S=1, H=64, Hq=128, K=2048, Lmax=16384,
+                    lengths=[16384] * B, w_scale=64 ** -0.5 * 128 ** -0.5)
+
+
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
