@@ -581,6 +581,10 @@ def prefill_leg(reps=20):
     gemm_tflop = {"absorb_q": 2.0 * T * Hq * 128 * 512 / 1e12,
                   "absorb_o": 2.0 * T * Hq * 512 * 128 / 1e12,
                   "kv_up": 2.0 * T * 512 * Hq * 256 / 1e12}
+    # algorithmic bytes: A, B and C of each product, once (bf16)
+    gemm_bytes = {"absorb_q": 2 * (T * Hq * 128 + Hq * 128 * 512 + T * Hq * 512),
+                  "absorb_o": 2 * (T * Hq * 512 + Hq * 128 * 512 + T * Hq * 128),
+                  "kv_up": 2 * (T * 512 + Hq * 256 * 512 + T * Hq * 256)}
     mha_tflop = 2.0 * Hq * (192 + 128) * sel / 1e12
     # executed work: every listed 64-position tile of each 128-row query tile
     toff = dsa.sparse_mha_tiles_offset(1, T, T)
@@ -602,7 +606,9 @@ def prefill_leg(reps=20):
         "topk": {"GBps": round(topk_bytes / (us["topk"] * 1e-6) / 1e9, 1), "bytes": topk_bytes,
                  "frac_hbm": round(topk_bytes / (us["topk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "projections": {c: {"tflops": round(f / (us[c] * 1e-6), 1), "flop": round(f * 1e12),
-                            "frac_bf16_mfma": round(f / (us[c] * 1e-6) / BF16_MFMA_PEAK_TFLOPS, 4)}
+                            "frac_bf16_mfma": round(f / (us[c] * 1e-6) / BF16_MFMA_PEAK_TFLOPS, 4),
+                            "bytes": gemm_bytes[c],
+                            "frac_hbm": round(gemm_bytes[c] / (us[c] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
                         for c, f in gemm_tflop.items()},
         "sparse_mha": {"tflops": round(mha_tfs, 1), "flop": round(mha_tflop * 1e12),
                        "frac_bf16_mfma": round(mha_tfs / BF16_MFMA_PEAK_TFLOPS, 4),
