@@ -139,8 +139,11 @@ def calibrate_copy():
 # ------------------------------------------------------------ byte model --
 
 def algorithmic_bytes(wl, n_valid, keff):
-    """Bytes the method itself must move per call, summed over the batch
-    (the per-row figures of the byte model in the design doc)."""
+    """Bytes the method itself must move per call, summed over the batch:
+    per row, the indexer reads n_valid FP8 keys and scales, the query and
+    weights and appends one key; top-k reads n_valid scores and writes
+    k_eff indices; the attention reads k_eff indices, gathers k_eff latent
+    and rotary rows and reads the query and writes the output."""
     n_valid = np.asarray(n_valid, np.int64)
     keff = np.asarray(keff, np.int64)
     H, Hq = wl.H, wl.Hq
@@ -699,8 +702,9 @@ def _cpu_model() -> str:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(batch rows and long rows would shard across GPUs as DESIGN.md describes)",
+        print(f"bench.py: the library runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(batch rows would shard across GPUs with no exchange, long rows over the context "
+              "with one candidate all-gather and one LSE merge)",
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_counters:

@@ -3,8 +3,8 @@ Attention hot-path library declared in include/dsa.h.
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch provides device memory and the current HIP stream. The library
-must be built (``python -m sparse_attention_index_amd.build`` or
-``__graft_entry__.build()``); there is no fallback path.
+must be built (``python -m sparse_attention_index_amd.build``); there is
+no fallback path.
 
 Calls (same names as the C ABI, without the ``dsa_`` prefix):
     rope_table(P, yarn=..., ...)            -> (cos, sin) float32 [P, 32]
