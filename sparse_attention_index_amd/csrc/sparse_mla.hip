@@ -326,7 +326,12 @@ __device__ __forceinline__ float wave_incl_sum_f(float v) {
 // a wave is 512 consecutive bytes. Per head, wave w first turns the
 // (m, l, lr) triples of all splits (one split per lane) into weights
 // 2^(m_s - M) in LDS and the totals L, Lr.
-constexpr int kCombineQuarters = 4;
+#ifndef DSA_COMBINE_CFG
+#define DSA_COMBINE_CFG 408                  // feature parts per 16-head group * 100 + unroll
+#endif
+constexpr int kCombineQuarters = DSA_COMBINE_CFG / 100;
+constexpr int kCombineUnroll = DSA_COMBINE_CFG % 100;
+constexpr int kCombineT2 = kT2 / kCombineQuarters / 4;     // 16-feature tiles per wave
 
 __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
                                                       const uint16_t* __restrict__ ws_o,
@@ -363,39 +368,34 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
 
     const int m = lane & 15, g = lane >> 4;
     const int h = wg * 16 + m;
-    const int t2a = quarter * (kT2 / kCombineQuarters) + 2 * wave;
+    const int t2a = quarter * (kT2 / kCombineQuarters) + kCombineT2 * wave;
     const uint16_t* base = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + lane * 4;
     const int64_t sstride = static_cast<int64_t>(nwg) * kT2 * 64 * 4;
-    float4 a0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), a1 = a0;
-#pragma unroll 8
+    float4 a[kCombineT2];
+#pragma unroll
+    for (int u = 0; u < kCombineT2; ++u) a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll kCombineUnroll
     for (int s = 0; s < nsplit; ++s) {
         const float e = wgt[s][m];
-        const uint2 u0 = *reinterpret_cast<const uint2*>(base + s * sstride + t2a * 256);
-        const uint2 u1 = *reinterpret_cast<const uint2*>(base + s * sstride + (t2a + 1) * 256);
-        const float4 v0 = make_float4(__uint_as_float(u0.x << 16), __uint_as_float(u0.x & 0xFFFF0000u),
-                                      __uint_as_float(u0.y << 16), __uint_as_float(u0.y & 0xFFFF0000u));
-        const float4 v1 = make_float4(__uint_as_float(u1.x << 16), __uint_as_float(u1.x & 0xFFFF0000u),
-                                      __uint_as_float(u1.y << 16), __uint_as_float(u1.y & 0xFFFF0000u));
-        a0.x += e * v0.x;
-        a0.y += e * v0.y;
-        a0.z += e * v0.z;
-        a0.w += e * v0.w;
-        a1.x += e * v1.x;
-        a1.y += e * v1.y;
-        a1.z += e * v1.z;
-        a1.w += e * v1.w;
+#pragma unroll
+        for (int u = 0; u < kCombineT2; ++u) {
+            const uint2 w = *reinterpret_cast<const uint2*>(base + s * sstride + (t2a + u) * 256);
+            a[u].x += e * __uint_as_float(w.x << 16);
+            a[u].y += e * __uint_as_float(w.x & 0xFFFF0000u);
+            a[u].z += e * __uint_as_float(w.y << 16);
+            a[u].w += e * __uint_as_float(w.y & 0xFFFF0000u);
+        }
     }
     if (h >= Hq) return;
     const float Lr = s_Lr[m];
     const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
     uint16_t* oh = out + (row * Hq + h) * kDl + 4 * g;
-    auto pack = [&](float4 a) {
-        const uint32_t lo = pack_bf16x2(a.x * inv, a.y * inv);
-        const uint32_t hi = pack_bf16x2(a.z * inv, a.w * inv);
-        return make_uint2(lo, hi);
-    };
-    *reinterpret_cast<uint2*>(oh + 16 * t2a) = pack(a0);
-    *reinterpret_cast<uint2*>(oh + 16 * (t2a + 1)) = pack(a1);
+#pragma unroll
+    for (int u = 0; u < kCombineT2; ++u) {
+        const uint32_t lo = pack_bf16x2(a[u].x * inv, a[u].y * inv);
+        const uint32_t hi = pack_bf16x2(a[u].z * inv, a[u].w * inv);
+        *reinterpret_cast<uint2*>(oh + 16 * (t2a + u)) = make_uint2(lo, hi);
+    }
     if (lse != nullptr && quarter == 0 && wave == 0 && g == 0) {
         const float Ls = s_L[m];
         lse[row * Hq + h] = Ls > 0.0f ? s_M[m] * 0.69314718055994531f + logf(Ls) : -INFINITY;

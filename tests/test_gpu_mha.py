@@ -249,3 +249,26 @@ def test_prefill_both_forms_against_the_oracle():
     e2 = np.abs(host_bf16_as_f32(absorbed) - ref).max()
     say(f"  multi-head form err {e1:.3e}, absorbed form err {e2:.3e}")
     assert e1 <= MLA_ATOL and e2 <= MLA_ATOL
+
+
+def test_kv_up_and_mha_read_a_fused_cache():
+    """Latent and rotary rows read from one fused 576-wide cache (row stride
+    576 elements) by the up-projection and the multi-head attention."""
+    import torch
+    B, S, Hq, L, K = 2, 70, 8, 300, 128
+    g = synth.rng(1400)
+    W = make_w(g, Hq)
+    cache = synth.to_bf16_bits(g.standard_normal((B, L, 576), dtype=np.float32))
+    dcache = dev_bf16(cache)
+    kv = dsa.mla_kv_up(dcache[..., :512], dev_bf16(W))
+    torch.cuda.synchronize()
+    check_proj(host_bf16_as_f32(kv), oracle.kv_up(bf(cache[..., :512]), bf(W)),
+               oracle.kv_up(np.abs(bf(cache[..., :512])), np.abs(bf(W))), "kv_up fused")
+    q = synth.to_bf16_bits(g.standard_normal((B, S, Hq, 192), dtype=np.float32))
+    pos = np.broadcast_to(np.arange(L - S, L, dtype=np.int32), (B, S)).copy()
+    idx = synth.random_selection(1401, B * S, K, (pos + 1).reshape(-1), 0.5).reshape(B, S, K)
+    kv_bits = host_bf16_as_f32(kv)
+    out = dsa.sparse_mha(dev_bf16(q), kv, dcache[..., 512:], dev(idx), SCALE, pos=dev(pos))
+    torch.cuda.synchronize()
+    o = oracle_rows(q, synth.to_bf16_bits(kv_bits), cache[..., 512:], idx, pos, np.arange(S))
+    assert np.abs(host_bf16_as_f32(out) - o).max() <= MLA_ATOL
