@@ -23,8 +23,9 @@
 // Tiles are stored with XOR-swizzled 16-byte chunks so the operand reads
 // of one MFMA hit distinct banks. Each MFMA computes a tile of C^T (B rows
 // as the first operand), so a lane ends with four consecutive output
-// columns of one row: 8-byte stores. A B operand stored K x N is read
-// column-wise by the transposing LDS read.
+// columns of one row; the bf16 tile is staged through LDS and written in
+// 16-byte pieces, whole 256-byte rows per 16 threads. A B operand stored
+// K x N is read column-wise by the transposing LDS read.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -172,18 +173,31 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(bv[j], av[i], acc[i][j]);
     }
 
-    // lane holds C[64 wm + 16 i + m][64 wn + 16 j + 4 g + 0..3]
+    // Epilogue through LDS: lane holds C[64 wm + 16 i + m][64 wn + 16 j + 4 g + 0..3];
+    // the bf16 tile goes to LDS ([128][128 + 8]) and leaves in 16-byte
+    // pieces, 16 threads per 256-byte row (whole cache lines per store).
+    constexpr int kCS = kGN + 8;
+    __builtin_amdgcn_s_barrier();                  // every wave done with the ring
+    uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = m0 + 64 * wm + 16 * i + m;
-        if (row >= a.M) continue;
-        uint16_t* crow = C + static_cast<int64_t>(row) * a.ldc + n0 + 64 * wn + 4 * g;
+        const int r = 64 * wm + 16 * i + m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(ct + r * kCS + 64 * wn + 16 * j + 4 * g) = make_uint2(lo, hi);
         }
+    }
+    __syncthreads();
+    const int cr = tid >> 4, cc = (tid & 15) * 8;
+#pragma unroll
+    for (int p = 0; p < kGM / 16; ++p) {
+        const int r = 16 * p + cr;
+        const int row = m0 + r;
+        if (row < a.M)
+            *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * a.ldc + n0 + cc) =
+                *reinterpret_cast<const uint4*>(ct + r * kCS + cc);
     }
 }
 
