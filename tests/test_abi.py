@@ -294,3 +294,47 @@ def test_mha_validation():
     a.pos = None                                   # positions are optional
     a.workspace_bytes = n.value - 1
     assert call(L.dsa_sparse_mha, a) == 4
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "dsa.h"
+
+/* A C caller: the header compiles as C, the library links, and calls whose
+ * arguments fail validation return their status without touching the GPU. */
+int main(void) {
+    dsa_mha_args m;
+    dsa_mla_proj_args p;
+    dsa_topk_args t;
+    size_t n = 0;
+    int fails = 0;
+    if (dsa_abi_version() != DSA_ABI_VERSION) ++fails;
+    if (strncmp(dsa_status_str(DSA_ERR_SHAPE), "DSA_ERR_SHAPE", 13) != 0) ++fails;
+    if (dsa_sparse_mha(NULL, NULL) != DSA_ERR_NULL) ++fails;
+    memset(&m, 0, sizeof m);
+    m.B = 1; m.S = 1; m.Hq = 129; m.Lmax = 16; m.K = 4; m.scale = 0.1f;
+    if (dsa_sparse_mha_workspace(&m, &n) != DSA_ERR_SHAPE) ++fails;
+    memset(&p, 0, sizeof p);
+    p.B = 1; p.rows = 1; p.Hq = 1;
+    if (dsa_mla_kv_up(&p, NULL) != DSA_ERR_NULL) ++fails;
+    memset(&t, 0, sizeof t);
+    t.B = 1; t.S = 1; t.Lmax = 16; t.K = 4096;
+    if (dsa_topk(&t, NULL) != DSA_ERR_SHAPE) ++fails;
+    printf("%d\n", fails);
+    return fails;
+}
+"""
+
+
+def test_c_caller_links_and_validates(tmp_path):
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(dsa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I",
+                    os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o",
+                    str(exe), "-L", libdir, "-ldsa", "-Wl,-rpath," + libdir, "-L/opt/rocm/lib",
+                    "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr)
