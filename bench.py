@@ -499,7 +499,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0
 
 
-def prefill_leg(reps=20):
+def prefill_leg(reps=20, cpu=False):
     """Prefill of T = 4096 causal queries at positions 0..4095 (B = 1, L = 4096,
     H_I = 64, top-2048, 128 heads): each call timed on its own over graph
     replays. Inputs: seeded N(0,1) draws made on the GPU (torch generator,
@@ -596,8 +596,10 @@ def prefill_leg(reps=20):
     ntiles = int(tl[:, 0, 0].sum().item())
     mha_exec_tflop = 2.0 * Hq * (192 + 128) * 128 * 64 * ntiles / 1e12
     mha_tfs = mha_tflop / (us["sparse_mha"] * 1e-6)
+    cpu_rec = cpu_prefill_mla(q_mla, latent, kpe, idx, scale, K) if cpu else None
     return {
         "workload": "prefill T=4096 (B=1, L=4096, H_I=64, top-2048, 128 heads)",
+        "cpu_sparse_mla": cpu_rec,
         "call_us": {k: round(v, 1) for k, v in us.items()},
         "indexer": {"tflops": round(idx_tfs, 1), "flop": round(idx_tflop * 1e12),
                     "frac_bf16_mfma": round(idx_tfs / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -626,6 +628,30 @@ def prefill_leg(reps=20):
 
 
 # ----------------------------------------------------------- cpu oracle --
+
+def cpu_prefill_mla(q_mla, latent, kpe, idx, scale, K, stride=16):
+    """The oracle's sparse MLA (absorbed) on a stratified 1/stride of the
+    prefill's query rows (rows 0, stride, 2 stride, ...) with the GPU run's
+    inputs and selection, rated by the selected pairs of those rows."""
+    import torch
+
+    import oracle
+    T = q_mla.shape[1]
+    rows = torch.arange(0, T, stride, device=q_mla.device)
+    q = q_mla[:, rows].float().cpu().numpy().astype(np.float64)
+    lat = latent.float().cpu().numpy().astype(np.float64)
+    pe = kpe.float().cpu().numpy().astype(np.float64)
+    ix = idx[:, rows].cpu().numpy()
+    pairs = int(sum(min(K, int(t) + 1) for t in rows.tolist()))
+    t0 = time.perf_counter()
+    oracle.sparse_mla(q, lat, pe, ix, scale)
+    el = time.perf_counter() - t0
+    flop = 2.0 * q.shape[2] * (576 + 512) * pairs
+    full = 2.0 * q.shape[2] * (576 + 512) * sum(min(K, t + 1) for t in range(T))
+    return {"value": round(flop / el / 1e12, 4), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{rows.numel()} of {T} query rows (every {stride}th), "
+            f"{pairs} selected pairs, {el:.1f} s", "projected_full_s": round(full / (flop / el), 1)}
+
 
 def cpu_baseline(wl, x, seconds):
     """The oracle's decode step on the host: prepare q and the new key,
@@ -769,7 +795,7 @@ def main():
     if args.sweep:
         rec["sweep"] = sweep_leg(args)
     if not args.no_prefill:
-        rec["prefill"] = prefill_leg()
+        rec["prefill"] = prefill_leg(cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, x_host, args.cpu_seconds)
     else:
