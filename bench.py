@@ -783,6 +783,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": ab[dom],
+                     "traffic_over_algorithmic": (round(traffic / ab[dom], 2) if traffic else None),
                      "avg_launch_us": round(avg_us[dom], 3)},
         "source_hash": srch,
     }
