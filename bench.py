@@ -713,6 +713,14 @@ def cpu_baseline(wl, x, seconds):
     return rec
 
 
+def _device_record() -> dict:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
 def _cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -786,6 +794,7 @@ def main():
                      "traffic_over_algorithmic": (round(traffic / ab[dom], 2) if traffic else None),
                      "avg_launch_us": round(avg_us[dom], 3)},
         "source_hash": srch,
+        "device": _device_record(),
     }
     if not args.no_variants:
         rec["variants"] = variants_leg(wl, st)
