@@ -597,9 +597,11 @@ def prefill_leg(reps=20, cpu=False):
     mha_exec_tflop = 2.0 * Hq * (192 + 128) * 128 * 64 * ntiles / 1e12
     mha_tfs = mha_tflop / (us["sparse_mha"] * 1e-6)
     cpu_rec = cpu_prefill_mla(q_mla, latent, kpe, idx, scale, K) if cpu else None
+    cpu_mha = cpu_prefill_mha(q192, kv, kpe, idx, pos, scale, K) if cpu else None
     return {
         "workload": "prefill T=4096 (B=1, L=4096, H_I=64, top-2048, 128 heads)",
         "cpu_sparse_mla": cpu_rec,
+        "cpu_sparse_mha": cpu_mha,
         "call_us": {k: round(v, 1) for k, v in us.items()},
         "indexer": {"tflops": round(idx_tfs, 1), "flop": round(idx_tflop * 1e12),
                     "frac_bf16_mfma": round(idx_tfs / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -628,6 +630,31 @@ def prefill_leg(reps=20, cpu=False):
 
 
 # ----------------------------------------------------------- cpu oracle --
+
+def cpu_prefill_mha(q192, kv, kpe, idx, pos, scale, K, stride=16):
+    """The oracle's multi-head prefill attention on a stratified 1/stride of
+    the query rows, with the GPU run's up-projected keys/values and
+    selection, rated by the selected pairs of those rows."""
+    import torch
+
+    import oracle
+    T, Hq = q192.shape[1], q192.shape[2]
+    rows = torch.arange(0, T, stride, device=q192.device)
+    q = q192[:, rows].float().cpu().numpy().astype(np.float64)
+    kvh = kv.float().cpu().numpy().astype(np.float64)
+    pe = kpe.float().cpu().numpy().astype(np.float64)
+    ix = idx[:, rows].cpu().numpy()
+    pp = pos[:, rows].cpu().numpy()
+    pairs = int(sum(min(K, int(t) + 1) for t in rows.tolist()))
+    t0 = time.perf_counter()
+    oracle.sparse_mha(q, kvh, pe, ix, scale, pos=pp)
+    el = time.perf_counter() - t0
+    flop = 2.0 * Hq * (192 + 128) * pairs
+    full = 2.0 * Hq * (192 + 128) * sum(min(K, t + 1) for t in range(T))
+    return {"value": round(flop / el / 1e12, 4), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{rows.numel()} of {T} query rows (every {stride}th), "
+            f"{pairs} selected pairs, {el:.1f} s", "projected_full_s": round(full / (flop / el), 1)}
+
 
 def cpu_prefill_mla(q_mla, latent, kpe, idx, scale, K, stride=16):
     """The oracle's sparse MLA (absorbed) on a stratified 1/stride of the
