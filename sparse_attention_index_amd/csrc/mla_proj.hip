@@ -18,8 +18,10 @@
 // Block tile 128 x 128, 4 waves of 64 x 64 (4 x 4 MFMA 16x16x32 tiles),
 // k-slices of 32. The slices stream through a ring of LDS stages filled
 // straight from global memory (global_load_lds, 16 bytes per lane, no
-// registers), two slices ahead of the one being multiplied; raw barriers
-// and explicit vector-memory waits keep the loads in flight across them.
+// registers), the next slice loading while the current one is multiplied;
+// raw barriers and explicit vector-memory waits order them. (Two stages
+// leave room for four blocks per CU, which hides more latency than a
+// deeper ring.)
 // Tiles are stored with XOR-swizzled 16-byte chunks so the operand reads
 // of one MFMA hit distinct banks. Each MFMA computes a tile of C^T (B rows
 // as the first operand), so a lane ends with four consecutive output
@@ -31,14 +33,17 @@
 namespace dsa {
 
 #ifndef DSA_GEMM_STAGES
-#define DSA_GEMM_STAGES 3
+#define DSA_GEMM_STAGES 2
 #endif
 constexpr int kGM = 128, kGN = 128, kGK = 32;
 constexpr int kGStages = DSA_GEMM_STAGES;            // k-slices in the LDS ring
 constexpr int kGThreads = 256;
 constexpr int kGTileBytes = 128 * kGK * 2;           // one 128 x 32 (or 32 x 128) bf16 tile
 constexpr int kGStageBytes = 2 * kGTileBytes;        // A tile + B tile
-constexpr size_t kGemmLds = static_cast<size_t>(kGStages) * kGStageBytes;
+constexpr size_t kGCTileBytes = sizeof(uint16_t) * kGM * (kGN + 8);   // staged output tile
+constexpr size_t kGemmLds = static_cast<size_t>(kGStages) * kGStageBytes > kGCTileBytes
+                                ? static_cast<size_t>(kGStages) * kGStageBytes
+                                : kGCTileBytes;
 constexpr int kGLoads = 4;                           // 16-byte loads per thread per slice
 
 struct GemmArgs {
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     // the bf16 tile goes to LDS ([128][128 + 8]) and leaves in 16-byte
     // pieces, 16 threads per 256-byte row (whole cache lines per store).
     constexpr int kCS = kGN + 8;
+    static_assert(sizeof(uint16_t) * kGM * kCS <= kGemmLds, "output tile fits the LDS");
     __builtin_amdgcn_s_barrier();                  // every wave done with the ring
     uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll

@@ -38,10 +38,9 @@
 //                      between the operands), V^T by the transposing LDS
 //                      read from the row-major value rows.
 //     Tile rows are stored with XOR-swizzled 16-byte chunks so the operand
-//     reads hit distinct banks. Launch order: with Hq a multiple of 8, each
-//     XCD takes whole heads, so one head's keys and values stay in its L2;
-//     within a head the query tiles with the longest causal extent go
-//     first.
+//     reads hit distinct banks. Launch order: the heads of a query tile are
+//     adjacent, query tiles with the longest causal extent first (measured
+//     7% faster than giving each XCD whole heads).
 #include "dsa_common.h"
 
 namespace dsa {
@@ -166,17 +165,12 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     const uint16_t* __restrict__ zeros, float scale_log2, uint16_t* __restrict__ out) {
     extern __shared__ __align__(16) unsigned char kvs[];     // two tile buffers
 
-    // launch index -> (head, query tile); longest causal extent first
+    // launch index -> (head, query tile): the heads of one query tile are
+    // adjacent (they share its mask rows and tile list); longest causal
+    // extent first
     const int L = blockIdx.x;
-    int h, qtg;
-    if ((Hq & 7) == 0) {
-        const int j = L >> 3;
-        h = (j / nqt) * 8 + (L & 7);
-        qtg = nqt - 1 - (j % nqt);
-    } else {
-        h = L % Hq;
-        qtg = nqt - 1 - L / Hq;
-    }
+    const int h = L % Hq;
+    const int qtg = nqt - 1 - L / Hq;
     const int64_t b = qtg / ntq;
     const int t0 = (qtg % ntq) * kMhaRows;
     const int nw = 2 * nkt;
