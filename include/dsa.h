@@ -17,6 +17,14 @@
  * plus dsa_rope_table, which builds the rotary tables, and dsa_mla_append,
  * which writes new latent / rotary-key rows into the caches call 3 reads.
  *
+ * The prefill can also run in the multi-head (non-absorbed) form:
+ *   dsa_mla_kv_up     per-head keys and values up-projected from the latent
+ *   dsa_sparse_mha    sparse attention over them under the index and causal
+ *                     masks
+ * and the absorbed form's projections around call 3 are dsa_mla_absorb_q
+ * (query into the latent space) and dsa_mla_absorb_o (latent output back to
+ * each head's values).
+ *
  * Conventions shared by every call:
  *  - Every pointer in an args struct is a DEVICE pointer unless stated.
  *    The caller owns every buffer; the library allocates nothing, frees
