@@ -8,12 +8,14 @@
 //   out[h] = sum_j softmax(z)_j latent[p_j],  lse[h] = log sum_j exp(z_j).
 //
 // Design: one block of 4 waves serves 64 heads (16 per wave) of one query
-// row over a contiguous range ("split") of its selected positions. The two
+// row over a contiguous range ("split") of its selected positions (2 waves
+// and 32 heads in the build for the fewest blocks, below). The two
 // head-group blocks of a (row, split) get launch indices 8 apart in one 1-D
 // grid: the same XCD and back to back in dispatch order, so the second
 // block's gather is served by that XCD's L2. The split's index list is
 // staged in LDS once. Selected rows are gathered 32 at a time (8 threads
-// per row) into an LDS tile K [32][576] (row-major, padded).
+// per row, each thread one or two rows) into an LDS tile K [32][576]
+// (row-major, padded).
 // Per wave:
 //   S^T = K Q^T       bf16 MFMA 16x16x32, M = keys (2 tiles of 16), N = the
 //                     wave's 16 heads, K = features, four independent
@@ -30,11 +32,14 @@
 //                     LDS read ds_read_b64_tr_b16: within each 16-lane group,
 //                     lane 4e+q addresses features 4q..4q+3 of key e and lane
 //                     i receives feature i of keys 0..3.
-// Two builds of the kernel: when the grid has at most one block per CU
+// Three builds of the kernel: when the grid has at most one block per CU
 // (few query rows), one wave per SIMD has the CU to itself, so the gather of
 // the next tile is held in registers while the current one is computed and
-// the LDS operand reads run several MFMAs ahead; with more blocks, two
-// blocks share a CU and hide each other's latencies instead.
+// the LDS operand reads run several MFMAs ahead; with the fewest rows the
+// blocks serve 32 heads, which halves the LDS reads per CU and tile (the
+// CU's LDS bandwidth and the MFMA chain take about equal time per tile with
+// 4 waves reading every operand); with more blocks, two 64-head blocks
+// share a CU and hide each other's latencies instead.
 // With several splits per row the unnormalised partials (O, m, l) go to the
 // workspace, each wave's 16 x 512 block of O stored exactly as its registers
 // hold it, rounded to bf16 (every store instruction writes 512 consecutive
@@ -48,8 +53,8 @@ namespace dsa {
 constexpr int kDl = 512, kDq = 576;
 constexpr int kTile = 32;
 constexpr int kKtStride = kDq + 8;      // bf16 per K-tile row (1168 B, staggers banks)
-constexpr int kMlaThreads = 256;        // 4 waves x 16 heads
-constexpr int kHeadsPerBlock = 64;
+constexpr int kHeadsPerBlock = 64;      // 4 waves x 16 heads
+constexpr int kHeadsPerBlockFew = 32;   // 2 waves: the build for the fewest blocks
 constexpr int kMaxSlots = 2048;         // selected positions per split, at most
 constexpr int kMaxSplits = 64;
 constexpr int kT2 = kDl / 16;           // 16-feature output tiles per head
@@ -61,8 +66,9 @@ constexpr size_t kMlaLdsBytes = sizeof(uint16_t) * kTile * kKtStride + sizeof(in
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 #define DSA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
-template <bool PIPE>
-__global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
+// HPB = heads per block (4 HPB threads, one wave per 16 heads)
+template <bool PIPE, int HPB>
+__global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
     int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
@@ -82,7 +88,10 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const int64_t b = row / S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int wg = hg * (kHeadsPerBlock / 16) + wave;             // 16-head group
+    constexpr int kThr = 4 * HPB;                                 // threads per block
+    constexpr int kRP = kThr / 8;                                 // gathered rows per pass
+    constexpr int kNP = kTile / kRP;                              // gather passes per tile
+    const int wg = hg * (HPB / 16) + wave;                        // 16-head group
     const int h = wg * 16 + m;
     const bool active = wg * 16 < Hq;                             // wave has a real head
 
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const bool paged = cmap.table != nullptr;
     {
         const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
-        for (int i = tid; i < ntiles * kTile; i += kMlaThreads) {
+        for (int i = tid; i < ntiles * kTile; i += kThr) {
             const int p = i < count ? irow[i] : -1;
             int v = -1;
             if (p >= 0 && p < Lmax) v = paged ? static_cast<int>(cmap.row(b, p)) : p;
@@ -127,31 +136,39 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     const uint16_t* rope_b = rope + (paged ? 0 : b * rope_bs);
     __syncthreads();                               // sidx ready
 
-    // Gather mapping: 8 threads per key row (wave w loads keys 8w..8w+7);
+    // Gather mapping: 8 threads per key row (in each pass over kRP rows,
+    // wave w loads keys 8w..8w+7);
     // thread sub = tid % 8 loads latent chunks sub + 8i (i < 8, 8 features
     // each) and rope chunk sub: one row pointer per thread, immediate offsets,
     // 128 contiguous bytes per 8 lanes. Unselected slots read row 0 and are
     // zeroed (no divergent branches).
     const int gkey = tid >> 3, gsub = tid & 7;
-    uint4 GA[9];
-    auto fetch_tile = [&](int t, uint4 (&G)[9]) {
-        const int p = sidx[t * kTile + gkey];
-        const int pc = p >= 0 ? p : 0;
-        const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
-        const uint16_t* rrow = rope_b + static_cast<int64_t>(pc) * rope_rs + gsub * 8;
+    uint4 GA[kNP][9];
+    auto fetch_tile = [&](int t, uint4 (&G)[kNP][9]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) G[i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
-        G[8] = *reinterpret_cast<const uint4*>(rrow);
-    };
-    auto store_tile = [&](int t, uint4 (&G)[9]) {
-        if (sidx[t * kTile + gkey] < 0) {
+        for (int pp = 0; pp < kNP; ++pp) {
+            const int p = sidx[t * kTile + gkey + kRP * pp];
+            const int pc = p >= 0 ? p : 0;
+            const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
+            const uint16_t* rrow = rope_b + static_cast<int64_t>(pc) * rope_rs + gsub * 8;
 #pragma unroll
-            for (int i = 0; i < 9; ++i) G[i] = make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < 8; ++i) G[pp][i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
+            G[pp][8] = *reinterpret_cast<const uint4*>(rrow);
         }
-        uint16_t* dst = Kt + gkey * kKtStride + gsub * 8;
+    };
+    auto store_tile = [&](int t, uint4 (&G)[kNP][9]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 64 * i) = G[i];
-        *reinterpret_cast<uint4*>(dst + 512) = G[8];
+        for (int pp = 0; pp < kNP; ++pp) {
+            const int key = gkey + kRP * pp;
+            if (sidx[t * kTile + key] < 0) {
+#pragma unroll
+                for (int i = 0; i < 9; ++i) G[pp][i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            uint16_t* dst = Kt + key * kKtStride + gsub * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 64 * i) = G[pp][i];
+            *reinterpret_cast<uint4*>(dst + 512) = G[pp][8];
+        }
     };
 
     // transposing-read addresses (bf16 units within the tile): lane 4e+q of
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(kMlaThreads, PIPE ? 1 : 2) void sparse_mla_kernel(
     // PIPE: the gather of the next tile is in flight in registers while the
     // current one is computed
     if (PIPE && ntiles > 0) fetch_tile(0, GA);
-    auto tile_step = [&](int t, uint4 (&G)[9]) {
+    auto tile_step = [&](int t, uint4 (&G)[kNP][9]) {
         __syncthreads();                           // previous tile fully consumed
         if (!PIPE) fetch_tile(t, G);
         store_tile(t, G);
@@ -429,7 +446,7 @@ size_t mla_workspace_bytes(int rows, int Hq, int K) {
     return blocks * kT2 * 64 * 4 * sizeof(uint16_t) + slots * 4 * sizeof(float) + 256;
 }
 
-template <bool PIPE>
+template <bool PIPE, int HPB>
 static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq, int Lmax,
                                     int K, int sps, int ns, int nitems, int hgroups,
                                     const uint16_t* q, const uint16_t* latent, int64_t lat_rs,
@@ -439,10 +456,10 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
                                     CacheMap cmap) {
     // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE>),
+        reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE, HPB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(sparse_mla_kernel<PIPE>, grid, dim3(kMlaThreads), kMlaLdsBytes, stream, S,
+    hipLaunchKernelGGL((sparse_mla_kernel<PIPE, HPB>), grid, dim3(4 * HPB), kMlaLdsBytes, stream, S,
                        Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
                        rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
     return hipGetLastError();
@@ -467,16 +484,27 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     const int nitems = rows * ns;
     const int hgroups = (Hq + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const int nblocks = ((nitems + 7) / 8) * 8 * hgroups;
-    // at most one block per CU: the pipelined one-block-per-CU build
-    const bool pipe = nblocks <= 256;
-    hipError_t e = pipe ? launch_mla_kernel<true>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
-                                                  nitems, hgroups, q, latent, lat_rs, lat_bs,
-                                                  rope, rope_rs, rope_bs, idx, scale_log2, out,
-                                                  lse, ws_o, ws_ml, cmap)
-                        : launch_mla_kernel<false>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns,
-                                                   nitems, hgroups, q, latent, lat_rs, lat_bs,
-                                                   rope, rope_rs, rope_bs, idx, scale_log2, out,
-                                                   lse, ws_o, ws_ml, cmap);
+    const int hg_few = (Hq + kHeadsPerBlockFew - 1) / kHeadsPerBlockFew;
+    const int nb_few = ((nitems + 7) / 8) * 8 * hg_few;
+    hipError_t e;
+    if (nb_few <= 256) {
+        // fewest blocks: 32 heads (2 waves) per block, one block per CU; twice
+        // the blocks of the 64-head build and half its LDS operand reads per
+        // CU and tile (the two head groups of a (row, split) gather the same
+        // rows, the second from L2)
+        e = launch_mla_kernel<true, kHeadsPerBlockFew>(
+            dim3(nb_few), stream, S, Hq, Lmax, K, sps, ns, nitems, hg_few, q, latent, lat_rs,
+            lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    } else if (nblocks <= 256) {
+        // at most one block per CU: the pipelined one-block-per-CU build
+        e = launch_mla_kernel<true, kHeadsPerBlock>(
+            dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs,
+            lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    } else {
+        e = launch_mla_kernel<false, kHeadsPerBlock>(
+            dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs,
+            lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    }
     if (e != hipSuccess) return e;
     if (ns > 1) {
         hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
