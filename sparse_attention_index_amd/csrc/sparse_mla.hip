@@ -45,7 +45,8 @@
 // hold it, rounded to bf16 (every store instruction writes 512 consecutive
 // bytes; halving the partials' bytes shortens the call more than the extra
 // rounding, at most 2^-9 of the split's weighted |latent|, costs), and
-// combine_kernel merges them in float32 with the log-sum-exp rule.
+// combine_kernel (merge_few_kernel for the fewest rows) merges them in
+// float32 with the log-sum-exp rule.
 #include "dsa_common.h"
 
 namespace dsa {
@@ -419,6 +420,89 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
     }
 }
 
+// Merge for the fewest rows (the grid of the 32-head build): one 64-thread
+// block per (row, 16-head group, 16-feature tile t2), so that even one row's
+// merge spreads over the whole chip, with no LDS and no barrier. Lane
+// l = 16 g + m reads what lane l of each producing wave stored (head m,
+// features 16 t2 + 4 g .. +3) and its head's (m, l, lr) triple; every load of
+// a chunk of CH splits is issued before the first is used, so a row's merge
+// costs one memory round trip per chunk instead of one for the weights and
+// more for the partials. The accumulators follow the running maximum of m
+// (log-sum-exp rule); with a single chunk each split is weighted by
+// 2^(m_s - max m) directly, as in combine_kernel.
+template <int CH>
+__global__ __launch_bounds__(64) void merge_few_kernel(int Hq, int nsplit,
+                                                       const uint16_t* __restrict__ ws_o,
+                                                       const float* __restrict__ ws_ml,
+                                                       uint16_t* __restrict__ out,
+                                                       float* __restrict__ lse) {
+    const int nwg = (Hq + 15) / 16;
+    const int lane = threadIdx.x;
+    const int t2 = static_cast<int>(blockIdx.x % kT2);
+    const int wg = static_cast<int>((blockIdx.x / kT2) % nwg);
+    const int64_t row = blockIdx.x / (kT2 * nwg);
+    const int m = lane & 15, g = lane >> 4;
+    const int h = wg * 16 + m;
+    const int hc = h < Hq ? h : Hq - 1;
+    const uint16_t* pb = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + t2 * 256 + lane * 4;
+    const int64_t ps = static_cast<int64_t>(nwg) * kT2 * 64 * 4;   // split stride of the partials
+    const float* mb = ws_ml + (row * nsplit * Hq + hc) * 4;
+    const int64_t ms = static_cast<int64_t>(Hq) * 4;               // split stride of the triples
+
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float M = -INFINITY, Ls = 0.0f, Lr = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += CH) {
+        float4 ml[CH];
+        uint2 w[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            ml[c] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+            w[c] = make_uint2(0u, 0u);
+            if (s0 + c < nsplit) {
+                ml[c] = *reinterpret_cast<const float4*>(mb + (s0 + c) * ms);
+                w[c] = *reinterpret_cast<const uint2*>(pb + (s0 + c) * ps);
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, ml[c].x);
+        const float r = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+        M = Mn;
+        Ls *= r;
+        Lr *= r;
+        a.x *= r;
+        a.y *= r;
+        a.z *= r;
+        a.w *= r;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const float e = ml[c].x == -INFINITY ? 0.0f : exp2f(ml[c].x - Mn);
+            Ls += ml[c].y * e;
+            Lr += ml[c].z * e;
+            a.x += e * __uint_as_float(w[c].x << 16);
+            a.y += e * __uint_as_float(w[c].x & 0xFFFF0000u);
+            a.z += e * __uint_as_float(w[c].y << 16);
+            a.w += e * __uint_as_float(w[c].y & 0xFFFF0000u);
+        }
+    }
+    if (h >= Hq) return;
+    const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
+    *reinterpret_cast<uint2*>(out + (row * Hq + h) * kDl + 16 * t2 + 4 * g) =
+        make_uint2(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv));
+    if (lse != nullptr && t2 == 0 && g == 0)
+        lse[row * Hq + h] = Ls > 0.0f ? M * 0.69314718055994531f + logf(Ls) : -INFINITY;
+}
+
+template <int CH>
+static hipError_t launch_merge_few(hipStream_t stream, int rows, int Hq, int ns,
+                                   const uint16_t* ws_o, const float* ws_ml, uint16_t* out,
+                                   float* lse) {
+    const unsigned blocks = static_cast<unsigned>(rows) * ((Hq + 15) / 16) * kT2;
+    hipLaunchKernelGGL(merge_few_kernel<CH>, dim3(blocks), dim3(64), 0, stream, Hq, ns, ws_o, ws_ml,
+                       out, lse);
+    return hipGetLastError();
+}
+
 // Split plan: enough (row, split) blocks to occupy the chip, each split a
 // whole number of 32-key tiles and at least two of them (fewer, longer splits
 // cost more per block than the extra partials cost the merge; measured at
@@ -486,8 +570,9 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     const int nblocks = ((nitems + 7) / 8) * 8 * hgroups;
     const int hg_few = (Hq + kHeadsPerBlockFew - 1) / kHeadsPerBlockFew;
     const int nb_few = ((nitems + 7) / 8) * 8 * hg_few;
+    const bool few = nb_few <= 256;
     hipError_t e;
-    if (nb_few <= 256) {
+    if (few) {
         // fewest blocks: 32 heads (2 waves) per block, one block per CU; twice
         // the blocks of the 64-head build and half its LDS operand reads per
         // CU and tile (the two head groups of a (row, split) gather the same
@@ -507,9 +592,15 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     }
     if (e != hipSuccess) return e;
     if (ns > 1) {
-        hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
-                           stream, Hq, ns, ws_o, ws_ml, out, lse);
-        e = hipGetLastError();
+        if (few) {
+            e = ns <= 8    ? launch_merge_few<8>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse)
+                : ns <= 16 ? launch_merge_few<16>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse)
+                           : launch_merge_few<32>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse);
+        } else {
+            hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
+                               stream, Hq, ns, ws_o, ws_ml, out, lse);
+            e = hipGetLastError();
+        }
     }
     return e;
 }

@@ -63,6 +63,11 @@ CASES = [
     ("long-rows", 1, 300, 128, 1200, 1024, 1200, 0.6),
     ("long-heads80", 1, 272, 80, 700, 512, 700, 0.5),
     ("long-split", 1, 130, 128, 2500, 2048, 2500, 0.9),
+    # few rows (32-head blocks, one-wave merge): 16 splits; 25 splits (a
+    # partial chunk of the merge); two short rows with empty splits
+    ("few-split16", 1, 1, 128, 3000, 1024, 3000, 0.7),
+    ("few-split25", 1, 1, 64, 4000, 1600, 4000, 0.5),
+    ("few-short-rows", 1, 2, 128, 300, 2048, 300, 1.0),
 ]
 
 
