@@ -539,20 +539,10 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     __shared__ float kscale_new;
 
     const int row = blockIdx.y;
-    const int p = pos[row];
-    if (p < 0 || p >= Lmax || p >= P) return;
-    const int n_valid = p + 1;
-    const int nchunks = (n_valid + kChunkKeys - 1) / kChunkKeys;
-    const int stride = static_cast<int>(gridDim.x);
-    int chunk = blockIdx.x;
-    if (chunk >= nchunks) return;
-
+    const int chunk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     const int64_t b = row;
-    const int64_t prow = cmap.row(b, p);                              // the new key's row
-    const int chunk_p = p / kChunkKeys;                               // chunk holding p
-    const bool has_new = k_raw != nullptr && prow >= 0 && chunk_p % stride == chunk;
     // the key (within the wave's 16 U) whose score this lane stores
     const int own = U == 4 ? lane : (U == 2 ? 16 * (g >> 1) + m : m);
     const bool stores = U == 4 ? true : (U == 2 ? (g & 1) == 0 : g == 0);
@@ -560,18 +550,66 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     const uint8_t* kc_row = kcache + (dense ? b * cmap.batch_rows * 128 : 0);
     const float* ks_row = kscale + (dense ? b * cmap.batch_rows : 0);
 
+    // Loads that need no position, issued before the row's position arrives:
+    // the first chunk's key rows (dense cache, chunk inside it; keys at or
+    // past n_valid are scored but never stored), the head weights and the
+    // raw query.
+    auto load_rows = [&](int wkey0, DecChunk<U>& d) {
+        const uint4* src =
+            reinterpret_cast<const uint4*>(kc_row + static_cast<int64_t>(wkey0 + m) * 128 + g * 32);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            d.k[u][0] = src[u * 128];
+            d.k[u][1] = src[u * 128 + 1];
+        }
+        d.ks = ks_row[wkey0 + own];
+    };
+    DecChunk<U> A, Bc;
+    const int wkeyA = chunk * kChunkKeys + wave * 16 * U;
+    const bool specA = dense && wkeyA + 16 * U <= Lmax;
+    if (specA) load_rows(wkeyA, A);
+    float wraw[4][4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = hg * 16 + 4 * g + i;
+            wraw[hg][i] = h < H ? w[static_cast<int64_t>(row) * H + h] : 0.0f;
+        }
+    constexpr int kHalf = kTPH / 2;
+    const int hh = tid / kTPH, e = tid % kTPH;
+    float qv[kFPT];
+    if (hh < H) {
+        const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128;
+        if (e < kHalf) {
+            const int j0 = (kFPT / 2) * e;
+#pragma unroll
+            for (int j = 0; j < kFPT / 2; ++j) {
+                qv[j] = load_act<BF16_IN>(q_raw, base + j0 + j);
+                qv[kFPT / 2 + j] = load_act<BF16_IN>(q_raw, base + j0 + j + 32);
+            }
+        } else {
+            const int f0 = 64 + kFPT * (e - kHalf);
+#pragma unroll
+            for (int j = 0; j < kFPT; ++j) qv[j] = load_act<BF16_IN>(q_raw, base + f0 + j);
+        }
+    }
+
+    const int p = pos[row];
+    if (p < 0 || p >= Lmax || p >= P) return;
+    const int n_valid = p + 1;
+    const int nchunks = (n_valid + kChunkKeys - 1) / kChunkKeys;
+    const int stride = static_cast<int>(gridDim.x);
+    if (chunk >= nchunks) return;
+    const int64_t prow = cmap.row(b, p);                              // the new key's row
+    const int chunk_p = p / kChunkKeys;                               // chunk holding p
+    const bool has_new = k_raw != nullptr && prow >= 0 && chunk_p % stride == chunk;
+
     // 1. key loads of chunk c (the new key, if any, is taken from LDS later)
     auto load_chunk = [&](int c, DecChunk<U>& d) {
         const int wkey0 = c * kChunkKeys + wave * 16 * U;
         if (dense && wkey0 + 16 * U <= n_valid) {
-            const uint4* src =
-                reinterpret_cast<const uint4*>(kc_row + static_cast<int64_t>(wkey0 + m) * 128 + g * 32);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                d.k[u][0] = src[u * 128];
-                d.k[u][1] = src[u * 128 + 1];
-            }
-            d.ks = ks_row[wkey0 + own];
+            load_rows(wkey0, d);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -589,8 +627,7 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
             d.ks = orow >= 0 ? kscale[orow] : -INFINITY;
         }
     };
-    DecChunk<U> A, Bc;
-    load_chunk(chunk, A);
+    if (!specA) load_chunk(chunk, A);
     if constexpr (LOOP) {                    // two chunks in flight during the quantisation
         if (chunk + stride < nchunks) load_chunk(chunk + stride, Bc);
     }
@@ -598,29 +635,25 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     // 2. quantise the row's query heads into LDS
     {
 #pragma clang fp contract(off)
-        constexpr int kHalf = kTPH / 2;
-        const int hh = tid / kTPH, e = tid % kTPH;
         float v[kFPT];
         float amax = 0.0f;
         if (hh < H) {
-            const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128;
             if (e < kHalf) {
                 const int j0 = (kFPT / 2) * e;
                 const float* c = cos_t + static_cast<int64_t>(p) * 32 + j0;
                 const float* sn = sin_t + static_cast<int64_t>(p) * 32 + j0;
 #pragma unroll
                 for (int j = 0; j < kFPT / 2; ++j) {
-                    const float a = load_act<BF16_IN>(q_raw, base + j0 + j);
-                    const float bb = load_act<BF16_IN>(q_raw, base + j0 + j + 32);
+                    const float a = qv[j];
+                    const float bb = qv[kFPT / 2 + j];
                     const float ac = a * c[j], bs = bb * sn[j];
                     const float as = a * sn[j], bc = bb * c[j];
                     v[j] = round_act<BF16_IN>(ac - bs);
                     v[kFPT / 2 + j] = round_act<BF16_IN>(as + bc);
                 }
             } else {
-                const int f0 = 64 + kFPT * (e - kHalf);
 #pragma unroll
-                for (int j = 0; j < kFPT; ++j) v[j] = load_act<BF16_IN>(q_raw, base + f0 + j);
+                for (int j = 0; j < kFPT; ++j) v[j] = qv[j];
             }
 #pragma unroll
             for (int j = 0; j < kFPT; ++j) amax = fmaxf(amax, fabsf(v[j]));
@@ -704,7 +737,7 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = hg * 16 + 4 * g + i;
-            wq2[hg][i] = h < H ? 0.5f * (w[static_cast<int64_t>(row) * H + h] * qscale[h]) : 0.0f;
+            wq2[hg][i] = h < H ? 0.5f * (wraw[hg][i] * qscale[h]) : 0.0f;
         }
     }
     float* out = scores + static_cast<int64_t>(row) * ld;
