@@ -74,7 +74,7 @@ def parse():
 KERNELS_OF_CALL = {
     "indexer": ["decode_score_kernel"],
     "topk": ["topk_select_kernel"],
-    "sparse_mla": ["sparse_mla_kernel", "combine_kernel"],
+    "sparse_mla": ["sparse_mla_kernel", "merge_few_kernel", "combine_kernel"],
 }
 
 
@@ -93,9 +93,11 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, wor
                     d[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
         return d
 
-    def mean_of(d, sub):
+    def mean_of(d, sub, required=True):
         vals = [v for k, vs in d.items() if sub in k for v in vs]
         if not vals:
+            if not required:
+                return None, 0
             raise SystemExit(f"no dispatch of a kernel named like {sub!r}")
         return sum(vals) / len(vals), len(vals)
 
@@ -109,12 +111,16 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, wor
         ent = {"kernels": {}}
         tf = tw = 0.0
         for sub in subs:
-            fb, n = mean_of(fetch, sub)
+            fb, n = mean_of(fetch, sub, required=False)       # a call's kernels vary with its shape
+            if fb is None:
+                continue
             wb, _ = mean_of(write, sub)
             ent["kernels"][sub] = {"fetch_bytes": round(fb * f_scale), "write_bytes": round(wb * w_scale),
                                    "dispatches": n}
             tf += fb * f_scale
             tw += wb * w_scale
+        if not ent["kernels"]:
+            raise SystemExit(f"no dispatch of a kernel of call {call!r}")
         ent.update(fetch_bytes=round(tf), write_bytes=round(tw), bytes_per_launch=round(tf + tw))
         rec[call] = ent
     out = os.path.join(ROOT, "profiles", "counters.json")
