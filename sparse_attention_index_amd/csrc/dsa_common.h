@@ -62,6 +62,21 @@ __device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, floa
     return static_cast<uint32_t>(w);
 }
 
+// Quotients x / s rounded to nearest (the float32 division) for the E4M3
+// codes above. With a normal, finite s, y = 1 / s (itself the rounded
+// quotient) gives each one in four instructions instead of the division
+// sequence: q0 = x y is within an ulp of x / s, the fma residual x - q0 s is
+// exact, and q0 + (x - q0 s) y rounded once is the correctly rounded quotient
+// (Markstein's division theorem); the sign is x's, which also keeps -0 / s
+// at -0 (the residual step alone would give +0). Other s take the division.
+__device__ __forceinline__ float quotient_rn(float x, float s, float y) {
+    const float q0 = x * y;
+    return copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, x), y, q0), x);
+}
+__device__ __forceinline__ bool quotient_fast(float s) {
+    return s >= 1.17549435e-38f && s < INFINITY;       // normal, finite
+}
+
 // ---- wave reductions (wave64) ---------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

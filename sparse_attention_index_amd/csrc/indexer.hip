@@ -178,8 +178,17 @@ __global__ __launch_bounds__(256) void prepare_rows_kernel(
         float scale = amax / 448.0f;
         if (pow2) scale = scale > 0.0f ? pow2_ceil(scale) : 1.0f;
         else if (!(scale > 0.0f)) scale = 1.0f;
-        const uint32_t w0 = e4m3_encode4(y[0] / scale, y[1] / scale, y[2] / scale, y[3] / scale);
-        const uint32_t w1 = e4m3_encode4(y[4] / scale, y[5] / scale, y[6] / scale, y[7] / scale);
+        uint32_t w0, w1;
+        if (quotient_fast(scale)) {
+            const float rs = 1.0f / scale;
+            w0 = e4m3_encode4(quotient_rn(y[0], scale, rs), quotient_rn(y[1], scale, rs),
+                              quotient_rn(y[2], scale, rs), quotient_rn(y[3], scale, rs));
+            w1 = e4m3_encode4(quotient_rn(y[4], scale, rs), quotient_rn(y[5], scale, rs),
+                              quotient_rn(y[6], scale, rs), quotient_rn(y[7], scale, rs));
+        } else {
+            w0 = e4m3_encode4(y[0] / scale, y[1] / scale, y[2] / scale, y[3] / scale);
+            w1 = e4m3_encode4(y[4] / scale, y[5] / scale, y[6] / scale, y[7] / scale);
+        }
         if (!ok) continue;
         int64_t dst;
         if (TO_CACHE) {
@@ -663,12 +672,22 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
         float scale = amax / 448.0f;
         if (!(scale > 0.0f)) scale = 1.0f;
         uint32_t pk[kFPT / 4];
+        if (quotient_fast(scale)) {
+            const float rs = 1.0f / scale;
 #pragma unroll
-        for (int i = 0; i < kFPT / 4; ++i) {
-            const uint32_t word = e4m3_encode4(v[4 * i] / scale, v[4 * i + 1] / scale,
-                                               v[4 * i + 2] / scale, v[4 * i + 3] / scale);
-            pk[i] = hh < H ? word : 0u;
+            for (int i = 0; i < kFPT / 4; ++i)
+                pk[i] = e4m3_encode4(quotient_rn(v[4 * i], scale, rs),
+                                     quotient_rn(v[4 * i + 1], scale, rs),
+                                     quotient_rn(v[4 * i + 2], scale, rs),
+                                     quotient_rn(v[4 * i + 3], scale, rs));
+        } else {
+#pragma unroll
+            for (int i = 0; i < kFPT / 4; ++i)
+                pk[i] = e4m3_encode4(v[4 * i] / scale, v[4 * i + 1] / scale, v[4 * i + 2] / scale,
+                                     v[4 * i + 3] / scale);
         }
+#pragma unroll
+        for (int i = 0; i < kFPT / 4; ++i) pk[i] = hh < H ? pk[i] : 0u;
         // parts e < TPH/2: bytes [j0, j0 + FPT/2) and [32 + j0, ...); others [f0, f0 + FPT)
         uint8_t* dst = qcodes + hh * 128;
         const int off0 = e < kHalf ? (kFPT / 2) * e : 64 + kFPT * (e - kHalf);
