@@ -51,6 +51,7 @@
 
 namespace dsa {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kDl = 512, kDq = 576;
 constexpr int kTile = 32;
 constexpr int kKtStride = kDq + 8;      // bf16 per K-tile row (1168 B, staggers banks)
@@ -316,7 +317,12 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         for (int t2 = 0; t2 < kT2; ++t2) {
             const uint32_t lo = pack_bf16x2(acc[t2][0], acc[t2][1]);
             const uint32_t hi = pack_bf16x2(acc[t2][2], acc[t2][3]);
-            *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
+            // fewest rows: streamed past L2 (measured 0.2 us shorter for one
+            // row, slower for 32 rows)
+            if constexpr (PIPE && HPB == kHeadsPerBlockFew)
+                __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(wo + t2 * 256));
+            else
+                *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
         }
         if (g == 0 && h < Hq)
             *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
