@@ -161,8 +161,11 @@ void orc_round_bf16_array(int64_t n, const float* x, float* out) {
  * Reading: theta and the blend are evaluated in double and rounded once to
  * float32; cos/sin are evaluated in double and rounded to float32.
  * Pinned by: closed-form cos/sin for the plain table; YaRN invariants
- * (ratio 1 at pair 0, 1/factor at the last pair, monotone). The exact
- * low/high rounding of the ramp is parity unpinned.
+ * (ratio 1 at pair 0, 1/factor at the last pair, monotone); the ramp's end
+ * points by [YaRN]'s rule in wavelengths (a pair turning more than
+ * beta_fast times over the original context is kept, less than beta_slow
+ * times fully interpolated, blended in between), which fixes the floor of
+ * low and the ceiling of high, and the ramp's linearity in the pair index.
  * ---------------------------------------------------------------------- */
 static double yarn_corr_dim(double rotations, int dim, double base, int orig) {
     return (double)dim * log((double)orig / (rotations * 2.0 * acos(-1.0))) / (2.0 * log(base));
@@ -318,37 +321,43 @@ void orc_quantize_rows_pow2(int64_t nrows, const float* x, uint8_t* codes, float
  * the indexer's rotated q and k are multiplied by H_128 / sqrt(128) before
  * quantisation; page "Rotate first features": rotate_activation(q),
  * rotate_activation(k) ahead of act_quant]. H_128 is the Sylvester Hadamard
- * matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), symmetric, so
- * y = H x / sqrt(128) row by row.
- * Reading (the order of float32 operations is not on the pages): the fast
- * Walsh-Hadamard transform in float32 with butterfly strides 1, 2, 4, ...,
- * 64 (x[i], x[i+s]) -> (x[i] + x[i+s], x[i] - x[i+s]), then one float32
- * multiplication by fl32(128^-0.5); with out_bf16 the row is rounded to
- * bfloat16 afterwards, like every step of the indexer's preparation.
- * Pinned by: a float64 matrix product with scipy's Hadamard matrix (within
- * the float32 rounding bound of the transform), H e_0 = 128^-0.5 (all
- * ones), orthonormality (norm preserved, H H x = x).
+ * matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), whose entry (i, j)
+ * is (-1)^popcount(i & j); it is symmetric, so y = H x / sqrt(128) row by
+ * row.
+ * The definition written out: each output is the double-precision sum of
+ * the 128 signed inputs times 1/sqrt(128), rounded once to float32; with
+ * out_bf16 that float32 value is then cast to bfloat16 (the activation
+ * dtype), like every other step of the indexer's preparation. How a fast
+ * transform orders its float32 additions is not on the pages; a GPU result
+ * is judged against this one within the rounding bound of its own order.
+ * Pinned by: scipy's Hadamard matrix in a float64 product (equal after one
+ * rounding), H e_i = column i of H, orthonormality (norm preserved,
+ * H H x = x).
  * ---------------------------------------------------------------------- */
+static int orc_popcount7(int v) {
+    int c = 0;
+    while (v) {
+        c += v & 1;
+        v >>= 1;
+    }
+    return c;
+}
+
 void orc_hadamard_rows(int64_t nrows, const float* x, int out_bf16, float* y) {
     int64_t r;
-    const float inv = (float)(1.0 / sqrt(128.0));
+    const double inv = 1.0 / sqrt(128.0);
 #pragma omp parallel for schedule(static)
     for (r = 0; r < nrows; ++r) {
-        float v[128];
-        int i, s;
-        for (i = 0; i < 128; ++i) v[i] = x[r * 128 + i];
-        for (s = 1; s < 128; s <<= 1) {
-            for (i = 0; i < 128; ++i) {
-                if (i & s) continue;
-                {
-                    float a = v[i], b = v[i + s];
-                    v[i] = a + b;
-                    v[i + s] = a - b;
-                }
-            }
-        }
+        const float* xr = x + r * 128;
+        int i, j;
         for (i = 0; i < 128; ++i) {
-            float o = v[i] * inv;
+            double acc = 0.0;
+            float o;
+            for (j = 0; j < 128; ++j) {
+                double v = (double)xr[j];
+                acc += (orc_popcount7(i & j) & 1) ? -v : v;
+            }
+            o = (float)(acc * inv);
             y[r * 128 + i] = out_bf16 ? orc_round_bf16(o) : o;
         }
     }
@@ -383,13 +392,19 @@ void orc_indexer_scores(int B, int S, int H, int D, int Lmax, const double* q,
                         const double* w, const double* k, const int32_t* n_valid,
                         double* out) {
     int64_t r, nrows = (int64_t)B * S;
-#pragma omp parallel for schedule(dynamic, 1)
+    /* The (row, key) entries are independent. With at least as many rows as
+     * threads the rows are shared out; with fewer (a decode step) each row's
+     * keys are, so every thread works either way. The arithmetic of an entry
+     * is the same in both cases. */
+    const int by_rows = nrows >= orc_num_threads();
+#pragma omp parallel for schedule(dynamic, 1) if (by_rows)
     for (r = 0; r < nrows; ++r) {
         int64_t b = r / S;
         const double* qr = q + r * H * D;
         const double* wr = w + r * H;
         const double* kb = k + b * (int64_t)Lmax * D;
         int s;
+#pragma omp parallel for schedule(static) if (!by_rows)
         for (s = 0; s < n_valid[r]; ++s) {
             const double* ks = kb + (int64_t)s * D;
             double total = 0.0;

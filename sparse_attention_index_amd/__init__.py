@@ -22,7 +22,6 @@ Calls (same names as the C ABI, without the ``dsa_`` prefix):
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -563,14 +562,3 @@ def sparse_mha(q, kv, rope, idx, scale: float, pos=None, out=None, workspace=Non
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(lib().dsa_sparse_mha(ctypes.byref(a), _stream()))
     return out
-
-
-def softmax_scale(qk_head_dim: int = 192, yarn: bool = False, rope_factor: float = 40.0,
-                  mscale: float = 1.0) -> float:
-    """qk_head_dim^-0.5, times m^2 with m = 1 + 0.1*mscale*ln(rope_factor) when
-    the YaRN correction applies (page "RoPE coefficients", MLA __init__)."""
-    s = qk_head_dim ** -0.5
-    if yarn:
-        m = 0.1 * mscale * math.log(rope_factor) + 1.0
-        s *= m * m
-    return s

@@ -113,3 +113,53 @@ def check_topk_properties(scores, idx, n_valid, K, label=""):
         ties_in = np.nonzero(mask & (s == thr))[0]
         if ties_out.size:
             assert ties_in.max() < ties_out.min(), (label, r)
+
+
+def check_rotated_codes(x_pre, g_codes, g_scales, act_bf16, pow2, label=""):
+    """Codes and scales of Hadamard-rotated rows, judged against the oracle's
+    rotation (the definition H x / sqrt(128): a float64 sum rounded once) with
+    an allowance for the GPU's float32 fast transform.
+
+    x_pre: float32 [N, 128], the rows fed to the rotation. The GPU adds
+    a +- b in float32 at 7 levels and multiplies by fl32(128^-0.5): its value
+    lies within delta = 10 u sum|x| / sqrt(128) of the exact product (7
+    additions, the constant's and the product's rounding, u = 2^-24; the
+    oracle's own rounding adds u |y|). A GPU value is therefore any float32
+    in [y - delta, y + delta], cast to bfloat16 when the activations are
+    bf16. The scale must come from an amax inside the range those values
+    allow, and each code must be the E4M3 encoding of the quotient of one of
+    them by the GPU's own scale. Returns (fraction of codes equal to the
+    oracle's, fraction of scales equal)."""
+    import oracle
+    u = 2.0 ** -24
+    x = np.asarray(x_pre, np.float32).reshape(-1, 128)
+    codes = np.asarray(g_codes, np.uint8).reshape(-1, 128)
+    scales = np.asarray(g_scales, np.float32).reshape(-1)
+    y = oracle.hadamard(x).astype(np.float64)
+    delta = 10 * u * np.abs(x.astype(np.float64)).sum(axis=1, keepdims=True) / np.sqrt(128.0) \
+        + u * np.abs(y)
+    lo = np.nextafter((y - delta).astype(np.float32), np.float32(-np.inf))
+    hi = np.nextafter((y + delta).astype(np.float32), np.float32(np.inf))
+    if act_bf16:
+        lo, hi = oracle.round_bf16(lo), oracle.round_bf16(hi)
+    lo64, hi64 = lo.astype(np.float64), hi.astype(np.float64)
+    straddle = (lo64 <= 0) & (hi64 >= 0)
+    amin = np.where(straddle, 0.0, np.minimum(np.abs(lo64), np.abs(hi64)))
+    amax_lo = amin.max(axis=1)
+    amax_hi = np.maximum(np.abs(lo64), np.abs(hi64)).max(axis=1)
+    s_lo = (amax_lo.astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    s_hi = (amax_hi.astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    if pow2:
+        p2 = lambda s: np.where(s > 0, 2.0 ** np.ceil(np.log2(np.maximum(s, 1e-45))), 1.0)
+        s_lo, s_hi = p2(s_lo.astype(np.float64)), p2(s_hi.astype(np.float64))
+    bad_s = np.nonzero((scales < s_lo) | (scales > s_hi))[0]
+    assert bad_s.size == 0, (label, "scale outside the allowance", bad_s[:4],
+                             scales[bad_s[:4]], s_lo[bad_s[:4]], s_hi[bad_s[:4]])
+    sc = scales[:, None]
+    q_lo = oracle.e4m3_decode(oracle.e4m3_encode(lo / sc))
+    q_hi = oracle.e4m3_decode(oracle.e4m3_encode(hi / sc))
+    got = oracle.e4m3_decode(codes)
+    bad = np.argwhere((got < q_lo) | (got > q_hi))
+    assert bad.size == 0, (label, "code outside the allowance", bad[:4])
+    o_codes, o_scales = oracle.quantize(oracle.hadamard(x, out_bf16=act_bf16), pow2=pow2)
+    return float(np.mean(codes == o_codes)), float(np.mean(scales == o_scales))

@@ -86,13 +86,19 @@ def compare_mla(wl, x, gidx, oidx, gout, glse, b, rows, label):
         g[bad] = host_bf16_as_f32(out2)[0]
         gl[bad] = host(lse2)[0]
     err = np.abs(g - o).max()
-    say(f"  {label}: mla max abs err {err:.3e}, rows with a different selection: {int((~same).sum())}")
+    lerr = np.abs(gl - ol)[np.isfinite(ol)].max(initial=0.0)
+    say(f"  {label}: mla max abs err {err:.3e}, lse max abs err {lerr:.3e}, rows with a "
+        f"different selection: {int((~same).sum())}")
     assert err <= MLA_ATOL
     assert np.allclose(gl, ol, atol=1e-3, rtol=1e-4)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode16k", "batch32"])
+@pytest.mark.parametrize("name", ["tiny", "decode16k", "batch32", "decode128k"])
 def test_decode_step_end_to_end(name):
+    """The whole step against the oracle's whole step: at decode128k the
+    oracle scores all 4 x 131,072 keys, selects its own top-2048 and attends
+    over that selection (the pages' topk(min(index_topk, end_pos)) followed by
+    attention over the selected rows)."""
     wl = synth.workload(name)
     say(f"e2e decode {name}: B={wl.B} Lmax={wl.Lmax} H={wl.H} Hq={wl.Hq} K={wl.K}")
     x = synth.make_inputs(wl)
@@ -141,35 +147,3 @@ def test_prefill_sampled_rows():
     oidx = oracle.topk(np.nan_to_num(osc[0]), n_valid, wl.K)
     check_topk_membership(g_idx[rows], oidx, osc[0], n_valid, wl.K, "prefill")
     compare_mla(wl, x, g_idx[rows], oidx, g_out[rows], g_lse[rows], 0, rows, "prefill")
-
-
-def test_decode128k_sampled_keys():
-    """Long-context decode at full size (B=4, L=131072, YaRN table): scores
-    at sampled key positions against the oracle, top-k by its defining
-    properties on the GPU scores, attention output finite."""
-    import torch
-    wl = synth.workload("decode128k")
-    say("e2e decode128k (sampled keys)")
-    x = synth.make_inputs(wl)
-    cos, sin = oracle.rope_table(wl.Lmax, yarn=True)
-    g = gpu_decode(wl, x, cos, sin)
-    B, L = wl.B, wl.Lmax
-    rng = synth.rng(5)
-    keys = np.unique(np.concatenate([np.arange(64), L - 64 + np.arange(64),
-                                     rng.choice(L, 4096, replace=False)]))
-    k8, kss, _ = oracle.indexer_prepare(x["k_raw"][:, keys], keys[None].astype(np.int32), cos,
-                                        sin, True)
-    for b in range(B):
-        assert np.array_equal(g["kc"][b, keys], k8[b]) and np.array_equal(g["ks"][b, keys], kss[b])
-    q8, qs, _ = oracle.indexer_prepare(x["q_raw"], x["pos"][..., None], cos, sin, True)
-    osc = oracle.indexer_scores(oracle.dequantize(q8, qs), x["w"], oracle.dequantize(k8, kss),
-                                np.full((B, 1), keys.size, np.int32))
-    gsc = g["scores"].reshape(B, L)
-    for b in range(B):
-        o = osc[b, 0]
-        floor = 0.01 * np.abs(o).max()       # sampled maximum: no looser than the full row's
-        den = np.maximum(np.abs(o), floor)
-        assert np.all(np.abs(gsc[b, keys] - o) <= 1e-3 * den), b
-    n_valid = (x["pos"] + 1).reshape(-1)
-    check_topk_properties(gsc, g["idx"].reshape(B, -1), n_valid, wl.K, "decode128k")
-    assert np.all(np.isfinite(g["out"])) and np.all(np.isfinite(g["lse"]))

@@ -267,8 +267,10 @@ def test_kv_up_and_mha_read_a_fused_cache():
     q = synth.to_bf16_bits(g.standard_normal((B, S, Hq, 192), dtype=np.float32))
     pos = np.broadcast_to(np.arange(L - S, L, dtype=np.int32), (B, S)).copy()
     idx = synth.random_selection(1401, B * S, K, (pos + 1).reshape(-1), 0.5).reshape(B, S, K)
-    kv_bits = host_bf16_as_f32(kv)
     out = dsa.sparse_mha(dev_bf16(q), kv, dcache[..., 512:], dev(idx), SCALE, pos=dev(pos))
     torch.cuda.synchronize()
-    o = oracle_rows(q, synth.to_bf16_bits(kv_bits), cache[..., 512:], idx, pos, np.arange(S))
+    # the oracle attends over its own up-projection, rounded to bf16 as the
+    # cached keys and values are
+    okv = synth.to_bf16_bits(oracle.kv_up(bf(cache[..., :512]), bf(W)).astype(np.float32))
+    o = oracle_rows(q, okv, cache[..., 512:], idx, pos, np.arange(S))
     assert np.abs(host_bf16_as_f32(out) - o).max() <= MLA_ATOL

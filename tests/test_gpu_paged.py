@@ -1,8 +1,8 @@
 """Paged caches (block table): every call that reads or writes a
 per-position cache gives, on a page pool addressed through a block table,
 bit-for-bit the result it gives on the equivalent dense cache (the same
-arithmetic on the same values, only the addresses differ), and the dense
-results are the oracle-checked ones. Positions on a page whose table entry
+arithmetic on the same values, only the addresses differ), and both the
+paged and the dense results are checked against the oracle directly. Positions on a page whose table entry
 is outside the pool are "not present": the indexer scores them -inf, the
 attention skips them, nothing is written there. (Paged variants are named
 on the aipricedb page, indexer logit kernels paragraph; the layout is the
@@ -13,7 +13,8 @@ import pytest
 import oracle
 import sparse_attention_index_amd as dsa
 import synth
-from gpu_util import MLA_ATOL, check_scores, dev, dev_bf16, host, host_bf16_as_f32, say
+from gpu_util import (INDEXER_RTOL, MLA_ATOL, check_scores, dev, dev_bf16, host, host_bf16_as_f32,
+                      say, score_errors)
 from test_gpu_mla import oracle_on_selection
 
 pytestmark = pytest.mark.gpu
@@ -94,12 +95,24 @@ def test_indexer_paged_matches_dense(S, page, Lmax):
             h = hole[b, :n]
             assert np.array_equal(d[~h], p[~h])
             assert np.all(p[h] == -np.inf)
-    # and the dense scores are the oracle's (sanity, the full check lives elsewhere)
+    # the pool's codes and scales and the paged scores against the oracle
+    # directly, and the dense scores too
     k8, ks8, _ = oracle.indexer_prepare(k_all, np.broadcast_to(np.arange(Lmax), (B, Lmax)), cos,
                                         sin, True)
+    assert np.array_equal(scatter_pool(k8, table, page, num_pages), pk)
+    assert np.array_equal(scatter_pool(ks8, table, page, num_pages), pks)
     q8, qs8, _ = oracle.indexer_prepare(q_raw, pos[..., None], cos, sin, True)
     o = oracle.indexer_scores(oracle.dequantize(q8, qs8), w, oracle.dequantize(k8, ks8), pos + 1)
     check_scores(dsc.reshape(B * S, Lmax), o.reshape(B * S, Lmax), (pos + 1).reshape(-1), "dense")
+    worst = 0.0
+    for b in range(B):
+        for s in range(S):
+            n = pos[b, s] + 1
+            h = hole[b, :n]
+            e = score_errors(psc[b, s, :n], o[b, s, :n])[~h]
+            worst = max(worst, float(e.max()))
+    assert worst <= INDEXER_RTOL
+    say(f"  paged worst normalised score error {worst:.2e}")
 
 
 def dev_bf(values_f32):
@@ -134,11 +147,17 @@ def test_mla_paged_matches_dense(S, page, K):
     torch.cuda.synchronize()
     assert np.array_equal(host(out_p.view(torch.int16)), host(out_r.view(torch.int16)))
     assert np.array_equal(host(lse_p), host(lse_r))
-    # the dense run on the full selection still matches the oracle
-    if S <= 2:
-        o, l = oracle_on_selection(q, lat, kpe, idx, scale)
-        assert np.max(np.abs(host_bf16_as_f32(out_d) - o)) <= MLA_ATOL
-        assert np.allclose(host(lse_d), l, rtol=0, atol=1e-3)
+    # the paged output against the oracle on the selection without the
+    # unmapped page, and the dense run on the full selection
+    o, l = oracle_on_selection(q, lat, kpe, idx_drop, scale)
+    ep = np.max(np.abs(host_bf16_as_f32(out_p) - o))
+    assert ep <= MLA_ATOL
+    assert np.allclose(host(lse_p), l, rtol=0, atol=1e-3)
+    o, l = oracle_on_selection(q, lat, kpe, idx, scale)
+    ed = np.max(np.abs(host_bf16_as_f32(out_d) - o))
+    assert ed <= MLA_ATOL
+    assert np.allclose(host(lse_d), l, rtol=0, atol=1e-3)
+    say(f"  paged max abs err {ep:.3e}, dense {ed:.3e}")
 
 
 def test_mla_append_paged_matches_dense():
@@ -168,3 +187,23 @@ def test_mla_append_paged_matches_dense():
     dense[1, 32:64] = 0                                      # the unmapped page gets nothing
     assert np.array_equal(scatter_pool(dense, table, page, num_pages), bits(pool))
     assert np.array_equal(bits(q_p), bits(q_d))              # q is rotated either way
+    # the paged pool and q against the oracle directly: latent rows copied,
+    # rotary keys and the queries' rope parts rotated with the interleaved
+    # pairing (page "RoPE coefficients"), bf16, nothing else written
+    f = synth.bf16_bits_to_f32
+    kpe_rot = synth.to_bf16_bits(oracle.rope(f(kpe_new), pos, cos, sin, rope_dim=64,
+                                             interleaved=True, out_bf16=True))
+    q_rot = q.copy()
+    q_rot[..., 512:] = synth.to_bf16_bits(oracle.rope(f(q[..., 512:]), pos[..., None], cos, sin,
+                                                      rope_dim=64, interleaved=True,
+                                                      out_bf16=True))
+    assert np.array_equal(bits(q_p), q_rot)
+    expect = np.zeros((num_pages, page, 576), np.uint16)
+    for b in range(B):
+        for s in range(S):
+            pg = table[b, pos[b, s] // page]
+            if pg < 0:
+                continue
+            expect[pg, pos[b, s] % page, :512] = lat_new[b, s]
+            expect[pg, pos[b, s] % page, 512:] = kpe_rot[b, s]
+    assert np.array_equal(bits(pool), expect)

@@ -15,13 +15,30 @@ def _rows(seed, n, scale=1.0):
 
 
 def test_hadamard_matches_library_matrix_product():
-    # scipy's Sylvester Hadamard matrix, float64 product, against the float32
-    # transform: each output is a 128-term signed sum, rounded at 7 levels
+    # scipy's Sylvester Hadamard matrix in a float64 product: the oracle's
+    # output is that value rounded once to float32 (a double rounding through
+    # the float64 sum could move it by at most one float32 unit)
     x = _rows(0, 64)
     ref = x.astype(np.float64) @ scipy.linalg.hadamard(128).astype(np.float64).T / np.sqrt(128.0)
-    got = oracle.hadamard(x).astype(np.float64)
-    bound = 8 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / np.sqrt(128)
-    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    got = oracle.hadamard(x)
+    assert got.dtype == np.float32
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 2.0 ** -24 * np.abs(ref))
+    assert np.mean(got == ref.astype(np.float32)) > 0.999
+
+
+def test_hadamard_worked_example():
+    # x = (1, 2, ..., 128): H x / sqrt(128) has y[0] = 8256 / sqrt(128) (the
+    # sum 1 + ... + 128) and, for i = 2^m, y[i] = -(2^m * 64) / sqrt(128)
+    # (the row of H for a power of two alternates in blocks of 2^m, and each
+    # block pair differs by 2^m in each of its 64 terms)
+    x = np.arange(1, 129, dtype=np.float32)[None]
+    y = oracle.hadamard(x).astype(np.float64)[0] * np.sqrt(128.0)
+    assert abs(y[0] - 8256.0) <= 1e-3
+    for m in range(7):
+        assert abs(y[1 << m] + (1 << m) * 64.0) <= 1e-3, m
+    # every other index (not 0, not a power of two) sums to zero
+    others = [i for i in range(1, 128) if i & (i - 1)]
+    assert np.all(np.abs(y[others]) <= 1e-3)
 
 
 def test_hadamard_unit_vectors_and_signs():

@@ -129,6 +129,39 @@ def test_yarn_frequency_invariants():
     assert np.all(np.abs(plain - ref) <= ref * 2.0 ** -24)
 
 
+@pytest.mark.parametrize("orig,factor,bf,bs", [(4096, 40.0, 32.0, 1.0), (4096, 40.0, 16.0, 2.0),
+                                                 (8192, 8.0, 32.0, 1.0)])
+def test_yarn_ramp_follows_rotation_counts(orig, factor, bf, bs):
+    """The YaRN ramp's end points, pinned by the YaRN paper's rule stated in
+    wavelengths (Peng et al. 2023): a pair that turns more than beta_fast
+    times over the original context keeps its frequency, one that turns less
+    than beta_slow times is fully interpolated (divided by the factor), and
+    the pairs in between are blended; the page's excerpt makes the blend
+    linear in the pair index (linear_ramp_factor(low, high, dim // 2)).
+    Rotation counts come from the wavelength 2 pi / theta_i here, not from
+    the oracle's correction-dimension formula, so a low rounded up or a
+    high rounded down (or swapped betas) fails."""
+    plain = oracle.rope_freqs(64).astype(np.float64)
+    yarn = oracle.rope_freqs(64, yarn=True, orig_len=orig, factor=factor, beta_fast=bf,
+                             beta_slow=bs).astype(np.float64)
+    ratio = yarn / plain
+    theta = np.array([10000.0 ** (-2.0 * i / 64) for i in range(32)])
+    turns = orig / (2 * np.pi / theta)                    # rotations over the original context
+    keep = turns > bf
+    full = turns < bs
+    assert keep.any() and full.any()
+    assert np.all(ratio[keep] == 1.0)
+    assert np.allclose(ratio[full], 1 / factor, rtol=1e-6)
+    mid = ~keep & ~full
+    assert np.all((ratio[mid] > 1 / factor * (1 + 1e-6)) & (ratio[mid] < 1.0))
+    # linear in the index between the last kept pair (smooth 1) and the first
+    # fully interpolated pair (smooth 0)
+    low, high = np.nonzero(keep)[0].max(), np.nonzero(full)[0].min()
+    smooth = (ratio - 1 / factor) / (1 - 1 / factor)
+    i = np.arange(low, high + 1)
+    assert np.allclose(smooth[i], 1 - (i - low) / (high - low), atol=1e-6)
+
+
 def test_yarn_table_is_plain_table_with_yarn_frequencies():
     cos_y, sin_y = oracle.rope_table(5000, yarn=True)
     f = oracle.rope_freqs(64, yarn=True).astype(np.float64)
