@@ -28,7 +28,10 @@
  * Conventions shared by every call:
  *  - Every pointer in an args struct is a DEVICE pointer unless stated.
  *    The caller owns every buffer; the library allocates nothing, frees
- *    nothing, keeps no state between calls and never synchronises.
+ *    nothing and never synchronises. Its only state across calls is
+ *    one-time set-up, kept per device under a lock: which kernels have been
+ *    opted in to more than 64 KiB of LDS, and where the static scratch of
+ *    dsa_sparse_mla_noalloc lives.
  *  - Work is enqueued on `stream` in order; results are ready when the
  *    stream reaches the end of the call's work. Calls on one stream see each
  *    other's results in order.
@@ -67,7 +70,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 /* Fixed head geometry (page "Sparse latent attention": 64 indexer heads of
  * 128 features, one shared 128-feature key per position, a 512-feature
@@ -87,7 +90,8 @@ typedef enum dsa_status {
     DSA_ERR_UNSUPPORTED = 3, /* unknown dtype or flag */
     DSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     DSA_ERR_ALIGN = 5,       /* a pointer or stride is not 16-byte aligned */
-    DSA_ERR_HIP = 6          /* a HIP launch failed */
+    DSA_ERR_HIP = 6,         /* a HIP launch failed */
+    DSA_ERR_SCRATCH = 7      /* the no-allocation call's static scratch is too small */
 } dsa_status;
 
 enum { DSA_DTYPE_F32 = 0, DSA_DTYPE_BF16 = 1 };
@@ -287,6 +291,28 @@ typedef struct dsa_mla_args {
 
 dsa_status dsa_sparse_mla_workspace(const dsa_mla_args* args, size_t* bytes);
 dsa_status dsa_sparse_mla(const dsa_mla_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_sparse_mla without allocation or workspace. For callers that cannot
+ * allocate device memory or hand over a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as dsa_sparse_mla (bit for bit); the
+ * workspace fields are ignored. The key-split partial results go to a
+ * static device array of DSA_MLA_NOALLOC_MAX_BYTES that every GPU the
+ * library runs on holds from the library's load until the process ends.
+ * Its address is looked up once per device, on the first call with that
+ * device current. The call itself allocates and frees nothing.
+ * Limit: the call needs dsa_sparse_mla_workspace() bytes of that array; a
+ * larger need (221 to 255 query rows B*S at 128 heads and K = 2048; every
+ * call with at most 220 rows, or at least 256, fits) is rejected with
+ * DSA_ERR_SCRATCH before anything is launched.
+ * Concurrency: every call on one GPU shares that GPU's array, and nothing
+ * in it needs to start at any value. Calls that overlap on one GPU (on
+ * different streams, or from different host threads without ordering)
+ * race on it; calls ordered on one stream do not.
+ * ---------------------------------------------------------------------- */
+#define DSA_MLA_NOALLOC_MAX_BYTES ((size_t)56 << 20)
+dsa_status dsa_sparse_mla_noalloc(const dsa_mla_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * MLA-side cache append (the step that fills the caches call 3 reads).

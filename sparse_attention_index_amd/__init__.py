@@ -12,6 +12,8 @@ Calls (same names as the C ABI, without the ``dsa_`` prefix):
                                             -> scores float32 [B, S, Lmax]
     topk(scores, pos, K)                    -> idx int32 [B, S, K]
     sparse_mla(q, latent, rope, idx, scale) -> out bf16 [B, S, Hq, 512] (, lse)
+    sparse_mla_noalloc(q, latent, rope, idx, scale, out, lse=None)
+                                            (no workspace, nothing allocated)
     mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None)
     mla_kv_up(latent, wkv_b)                -> kv bf16 [B, L, Hq, 256]
     mla_absorb_q(q_nope, wkv_b)             -> bf16 [B, S, Hq, 512]
@@ -28,6 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK = 0
+DSA_ERR_SCRATCH = 7
+MLA_NOALLOC_MAX_BYTES = 56 << 20
 DSA_DTYPE_F32 = 0
 DSA_DTYPE_BF16 = 1
 INDEX_DIM = 128
@@ -101,7 +105,7 @@ class MhaArgs(ctypes.Structure):
 EXPORTS = ("dsa_rope_table", "dsa_indexer_workspace", "dsa_indexer", "dsa_topk_workspace",
            "dsa_topk", "dsa_sparse_mla_workspace", "dsa_sparse_mla", "dsa_mla_append",
            "dsa_mla_kv_up", "dsa_mla_absorb_q", "dsa_mla_absorb_o", "dsa_sparse_mha_workspace",
-           "dsa_sparse_mha", "dsa_status_str", "dsa_abi_version")
+           "dsa_sparse_mha", "dsa_sparse_mla_noalloc", "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -137,6 +141,8 @@ def lib():
             ws = getattr(L, f"dsa_{name}_workspace")
             ws.restype = ctypes.c_int
             ws.argtypes = [ctypes.POINTER(st), ctypes.POINTER(_sz)]
+    L.dsa_sparse_mla_noalloc.restype = ctypes.c_int
+    L.dsa_sparse_mla_noalloc.argtypes = [ctypes.POINTER(MlaArgs), _vp]
     _lib = L
     return L
 
@@ -414,6 +420,15 @@ def sparse_mla(q, latent, rope, idx, scale: float, out=None, lse=None, workspace
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     _check(lib().dsa_sparse_mla(ctypes.byref(a), _stream()))
     return (out, lse) if return_lse else out
+
+
+def sparse_mla_noalloc(q, latent, rope, idx, scale: float, out, lse=None, paging=None):
+    """Call 3 through dsa_sparse_mla_noalloc: the caller passes the outputs
+    (out [B, S, Hq, 512] bf16, optional lse [B, S, Hq] float32); the key-split
+    partials go to the library's static scratch, nothing is allocated."""
+    a = mla_args(q, latent, rope, idx, scale, out, lse, None, paging)
+    _check(lib().dsa_sparse_mla_noalloc(ctypes.byref(a), _stream()))
+    return out
 
 
 def mla_append(latent_new, kpe_new, pos, cos, sin, latent, rope, q=None, paging=None):

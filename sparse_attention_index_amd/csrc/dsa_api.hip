@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 namespace dsa {
 hipError_t launch_rope_table(int P, int npairs, double base, int yarn, double low, double high,
@@ -50,6 +51,31 @@ hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16
                              const uint16_t* kv, const uint16_t* rope, int64_t rope_rs,
                              int64_t rope_bs, const int32_t* idx, const int32_t* pos, float scale,
                              uint16_t* out, void* workspace, hipStream_t stream);
+}  // namespace dsa
+
+namespace dsa {
+
+hipError_t set_dynamic_lds_limit(const void* kernel, int bytes) {
+    constexpr int kMaxEntries = 256;
+    struct Done {
+        const void* kernel;
+        int device;
+    };
+    static std::mutex mu;
+    static Done done[kMaxEntries];
+    static int ndone = 0;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < ndone; ++i)
+        if (done[i].kernel == kernel && done[i].device == dev) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    if (ndone < kMaxEntries) done[ndone++] = Done{kernel, dev};
+    return hipSuccess;
+}
+
 }  // namespace dsa
 
 namespace {
@@ -240,6 +266,33 @@ dsa_status check_mha(const dsa_mha_args* a) {
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// ------------------------------------------------- no-allocation scratch ---
+// The static device array behind dsa_sparse_mla_noalloc. In host code its
+// name is only a host-side stand-in: every use goes through the device
+// address looked up below, once per device (each GPU holds its own copy).
+static __device__ __align__(256) unsigned char scratch[DSA_MLA_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call per device, with that device current).
+dsa_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return DSA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
 dsa_status run_mla_proj(const dsa_mla_proj_args* a, int mode, hipStream_t stream) {
     const dsa_status st = check_mla_proj(a, mode);
     if (st != DSA_OK) return st;
@@ -264,6 +317,9 @@ const char* dsa_status_str(dsa_status s) {
         case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
         case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: pointer or stride not aligned";
         case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP launch failed";
+        case DSA_ERR_SCRATCH:
+            return "DSA_ERR_SCRATCH: the call needs more than the no-allocation call's static "
+                   "scratch (DSA_MLA_NOALLOC_MAX_BYTES)";
     }
     return "unknown dsa_status";
 }
@@ -388,6 +444,23 @@ dsa_status dsa_sparse_mla(const dsa_mla_args* a, hipStream_t stream) {
         a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->latent, a->latent_row_stride,
         a->latent_batch_stride, a->rope, a->rope_row_stride, a->rope_batch_stride, a->idx,
         a->scale, a->out, a->lse, a->workspace,
+        make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, 0), stream));
+}
+
+dsa_status dsa_sparse_mla_noalloc(const dsa_mla_args* a, hipStream_t stream) {
+    dsa_status st = check_mla(a);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::mla_workspace_bytes(a->B * a->S, a->Hq, a->K);
+    if (need > DSA_MLA_NOALLOC_MAX_BYTES) return DSA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st != DSA_OK) return st;
+    }
+    return hip_status(dsa::launch_sparse_mla(
+        a->B, a->S, a->Hq, a->Lmax, a->K, a->q, a->latent, a->latent_row_stride,
+        a->latent_batch_stride, a->rope, a->rope_row_stride, a->rope_batch_stride, a->idx,
+        a->scale, a->out, a->lse, ws,
         make_map(a->block_table, a->page_size, a->max_pages, a->num_pages, 0), stream));
 }
 

@@ -16,6 +16,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Opt a kernel in to `bytes` of dynamic LDS (above the 64 KiB default) on
+// the current device. The attribute is per device, so it is set once for
+// each (kernel, device) pair that launches; a small table under a mutex
+// remembers which pairs are done (host code only).
+hipError_t set_dynamic_lds_limit(const void* kernel, int bytes);
+
 // ---- bf16 <-> float ------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

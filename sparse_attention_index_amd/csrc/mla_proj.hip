@@ -209,9 +209,9 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
 
 template <int MODE>
 static hipError_t run_gemm(const GemmArgs& a, int nbatch, hipStream_t stream) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_kernel<MODE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kGemmLds));
+    // more than 64 KiB of dynamic LDS (set once per device)
+    const hipError_t attr = set_dynamic_lds_limit(
+        reinterpret_cast<const void*>(&gemm_bf16_kernel<MODE>), static_cast<int>(kGemmLds));
     if (attr != hipSuccess) return attr;
     const int ntiles = a.N / kGN;
     hipLaunchKernelGGL(gemm_bf16_kernel<MODE>, dim3(static_cast<unsigned>(a.mtiles * ntiles),

@@ -407,9 +407,9 @@ hipError_t launch_sparse_mha(int B, int S, int Hq, int Lmax, int K, const uint16
                              const uint16_t* kv, const uint16_t* rope, int64_t rope_rs,
                              int64_t rope_bs, const int32_t* idx, const int32_t* pos, float scale,
                              uint16_t* out, void* workspace, hipStream_t stream) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_mha_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMhaLds));
+    // more than 64 KiB of dynamic LDS (set once per device)
+    const hipError_t attr = set_dynamic_lds_limit(
+        reinterpret_cast<const void*>(&sparse_mha_kernel), static_cast<int>(kMhaLds));
     if (attr != hipSuccess) return attr;
     const int nkt = (Lmax + kMhaKeys - 1) / kMhaKeys;
     const int ntq = (S + kMhaRows - 1) / kMhaRows;

@@ -544,10 +544,9 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
                                     int64_t rope_bs, const int32_t* idx, float scale_log2,
                                     uint16_t* out, float* lse, uint16_t* ws_o, float* ws_ml,
                                     CacheMap cmap) {
-    // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE, HPB>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMlaLdsBytes));
+    // more than 64 KiB of dynamic LDS (set once per device)
+    const hipError_t attr = set_dynamic_lds_limit(
+        reinterpret_cast<const void*>(&sparse_mla_kernel<PIPE, HPB>), static_cast<int>(kMlaLdsBytes));
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((sparse_mla_kernel<PIPE, HPB>), grid, dim3(4 * HPB), kMlaLdsBytes, stream, S,
                        Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -40,8 +40,8 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = dsa.lib()
-    assert L.dsa_abi_version() == 2
-    for code in range(7):
+    assert L.dsa_abi_version() == 3
+    for code in range(8):
         assert dsa.status_str(code).startswith("DSA_")
     assert dsa.status_str(99) == "unknown dsa_status"
 
@@ -179,6 +179,28 @@ def test_mla_validation():
     a = good_mla(B=1, S=4096)
     assert L.dsa_sparse_mla_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
     assert n.value == 0
+
+
+def test_mla_noalloc_validation():
+    """The no-allocation call validates like dsa_sparse_mla and rejects a
+    call whose key-split partials exceed its static scratch, before any HIP
+    call (so it needs no GPU here)."""
+    L = dsa.lib()
+    for change, code in [(dict(Hq=129), 2), (dict(K=4096), 2), (dict(q=FAKE + 4), 5),
+                         (dict(out=None), 1)]:
+        a = good_mla()
+        for k, v in change.items():
+            setattr(a, k, v)
+        assert call(L.dsa_sparse_mla_noalloc, a) == code, change
+    n = ctypes.c_size_t(0)
+    for rows, fits in ((1, True), (32, True), (220, True), (221, False), (255, False),
+                       (256, True)):
+        a = good_mla(B=rows)
+        assert L.dsa_sparse_mla_workspace(ctypes.byref(a), ctypes.byref(n)) == 0
+        assert (n.value <= dsa.MLA_NOALLOC_MAX_BYTES) == fits, rows
+        if not fits:
+            assert call(L.dsa_sparse_mla_noalloc, a) == dsa.DSA_ERR_SCRATCH
+            assert dsa.status_str(dsa.DSA_ERR_SCRATCH).startswith("DSA_ERR_SCRATCH")
 
 
 def test_rope_table_validation():
