@@ -460,6 +460,38 @@ def variants_leg(wl, st, page=64):
 
     chained_us = _graph_us(dense_step, R)
 
+    # the same dense step launched eagerly: three C-ABI calls per step on the
+    # stream (argument structs built once, outside the timed region)
+    L = dsa.lib()
+    ia, ta, ma = [], [], []
+    for rep in st["reps"]:
+        ia.append(dsa.indexer_args(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"],
+                                   rep["kc"], rep["ks"], st["scores"], k_raw=st["k_new"],
+                                   q_fp8=st["q8"], q_scale=st["qs"]))
+        ma.append(dsa.mla_args(st["q_mla"], rep["latent"], rep["kpe"], st["idx"],
+                               wl.softmax_scale, st["out"], workspace=st["mla_ws"]))
+    ta = dsa.topk_args(st["scores"], st["pos"], wl.K, st["idx"], workspace=st["topk_ws"])
+    import ctypes
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    byref = ctypes.byref
+
+    def eager_steps(n):
+        for i in range(n):
+            r = i % R
+            L.dsa_indexer(byref(ia[r]), sp)
+            L.dsa_topk(byref(ta), sp)
+            L.dsa_sparse_mla(byref(ma[r]), sp)
+
+    eager_steps(R)
+    torch.cuda.synchronize()
+    n_eager = max(200, 2 * R)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    eager_steps(n_eager)
+    b_ev.record()
+    torch.cuda.synchronize()
+    eager_us = a_ev.elapsed_time(b_ev) * 1000.0 / n_eager
+
     def had_idx(r):
         rep = st["reps"][r % R]
         dsa.indexer(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], rep["kc"], rep["ks"],
@@ -486,6 +518,11 @@ def variants_leg(wl, st, page=64):
                            "unit": "queries/s",
                            "note": "the same dense step, one graph holding one step per "
                                    "replica back to back (no per-step graph launch)"},
+        "eager_decode": {"us_per_step": round(eager_us, 2),
+                         "value": round(B * wl.S / (eager_us * 1e-6), 1),
+                         "unit": "queries/s",
+                         "note": f"the same dense step, {n_eager} steps launched eagerly "
+                                 "(three C-ABI calls per step on the stream, no graph)"},
         "paged_decode": {"workload": f"{wl.name} on paged caches (page_size {page}, permuted "
                                     f"pool of {num_pages} pages)",
                          "value": round(B * wl.S / (paged_us * 1e-6), 1), "unit": "queries/s",

@@ -128,6 +128,18 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 
 __device__ __forceinline__ float wave_min_dpp(float v) { return -wave_max_dpp(-v); }
 
+// Sum of a float over the wave, returned to every lane (same lane moves).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    int x = __float_as_int(v);
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr1, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr2, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr4, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowShr8, 0xF>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowBcast15, 0xA>(0, x)));
+    x = __float_as_int(__int_as_float(x) + __int_as_float(dpp_move<kDppRowBcast31, 0xC>(0, x)));
+    return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
 // Exact conversion of four packed E4M3 bytes to four bf16 values.
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t packed, bf16x2& lo, bf16x2& hi) {
     lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false);

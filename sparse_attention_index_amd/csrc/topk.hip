@@ -43,6 +43,8 @@
 // tie rule (lower position first) and the ascending output carry through.
 #include "dsa_common.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 constexpr int kRegItems = 16;                           // scores per thread
@@ -123,9 +125,13 @@ __device__ __forceinline__ void clear_hist(RegShared& sh) {
     for (int b = threadIdx.x; b < kBuckets; b += blockDim.x) sh.hist[b] = 0u;
 }
 
-__device__ __forceinline__ int bucket_of(float v, float vmin, float scale) {
-    const float f = (v - vmin) * scale;
-    const int b = static_cast<int>(f);
+// Bucket of v under the map floor(v * scale + off) (off = -vmin * scale),
+// clamped to [0, kBuckets - 1]: one fma, correctly rounded, so the map is
+// monotone non-decreasing in v (the histogram and every later membership
+// test use this one function). At v = vmin the fma gives the tiny rounding
+// residual of vmin * scale, which truncates to bucket 0.
+__device__ __forceinline__ int bucket_of(float v, float scale, float off) {
+    const int b = static_cast<int>(__builtin_fmaf(v, scale, off));
     return b < kBuckets - 1 ? b : kBuckets - 1;
 }
 
@@ -279,13 +285,28 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         if constexpr (CAND_IN) return (vmask >> j) & 1u;
         else return item(j) < M;
     };
+    // every item of the wave is valid (wave-uniform): the per-item loops
+    // below then skip the validity tests (the work is VALU-bound: 16 waves
+    // of one CU run every per-item instruction)
+    bool wave_full;
+    if constexpr (CAND_IN) wave_full = __ballot(vmask != 0xFFFFu) == 0ull;
+    else wave_full = (wave + 1) * (kWave * kRegItems) <= M;
     float vmin = INFINITY, vmax = -INFINITY;
+    if (wave_full) {
 #pragma unroll
-    for (int j = 0; j < kRegItems; ++j) {
-        v[j] = v[j] + 0.0f;
-        if (valid(j)) {
+        for (int j = 0; j < kRegItems; ++j) {
+            v[j] = v[j] + 0.0f;
             vmin = fminf(vmin, v[j]);
             vmax = fmaxf(vmax, v[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) {
+            v[j] = v[j] + 0.0f;
+            if (valid(j)) {
+                vmin = fminf(vmin, v[j]);
+                vmax = fmaxf(vmax, v[j]);
+            }
         }
     }
     vmin = wave_min_dpp(vmin);
@@ -305,14 +326,14 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     if (tid == 0) sh.ccount = 0;
     clear_hist(sh);
     __syncthreads();
-    vmin = sh.wmin[0];
-    vmax = sh.wmax[0];
-    if constexpr (CAND_IN) M = sh.wn[0];
-    for (int w = 1; w < nw; ++w) {
-        vmin = fminf(vmin, sh.wmin[w]);
-        vmax = fmaxf(vmax, sh.wmax[w]);
-        if constexpr (CAND_IN) M += sh.wn[w];
-    }
+    // block totals: lane l < nw reads wave l's figures and wave reductions
+    // combine them (one LDS round trip instead of one per wave)
+    const bool wl_ok = lane < nw;
+    const int wl = wl_ok ? lane : 0;
+    vmin = wave_min_dpp(wl_ok ? sh.wmin[wl] : INFINITY);
+    vmax = wave_max_dpp(wl_ok ? sh.wmax[wl] : -INFINITY);
+    if constexpr (CAND_IN)
+        M = __builtin_amdgcn_readlane(wave_incl_scan_add(wl_ok ? sh.wn[wl] : 0), 63);
     const int keff = M < K ? M : K;
 
     uint32_t T = 0u;                        // threshold order key
@@ -326,16 +347,26 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     } else {
         const float range = vmax - vmin;
         const float scale = static_cast<float>(kBuckets) / range;
-        const bool bucketed = isfinite(range) && isfinite(scale) && scale > 0.0f;
+        const float off = -vmin * scale;
+        const bool bucketed = isfinite(range) && isfinite(scale) && scale > 0.0f &&
+                              isfinite(off);
         int want = keff;
         int bstar = -1;
         if (bucketed) {
             // 2. bucket histogram, threshold bucket (-1: not valid)
             int bk[kRegItems];
+            if (wave_full) {
 #pragma unroll
-            for (int j = 0; j < kRegItems; ++j) {
-                bk[j] = valid(j) ? bucket_of(v[j], vmin, scale) : -1;
-                if (bk[j] >= 0) atomicAdd(&sh.hist[bk[j]], 1u);
+                for (int j = 0; j < kRegItems; ++j) {
+                    bk[j] = bucket_of(v[j], scale, off);
+                    atomicAdd(&sh.hist[bk[j]], 1u);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kRegItems; ++j) {
+                    bk[j] = valid(j) ? bucket_of(v[j], scale, off) : -1;
+                    if (bk[j] >= 0) atomicAdd(&sh.hist[bk[j]], 1u);
+                }
             }
             __syncthreads();
             if (wave == 0) find_digit_wave0<kBuckets>(sh, keff);
@@ -400,7 +431,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
 #pragma unroll
             for (int j = 0; j < kRegItems; ++j) {
                 const bool in = valid(j) &&
-                                (bstar < 0 || bucket_of(v[j], vmin, scale) == bstar);
+                                (bstar < 0 || bucket_of(v[j], scale, off) == bstar);
                 memb |= in ? (1u << j) : 0u;
             }
             uint32_t prefix = 0u, mask = 0u;
@@ -451,10 +482,13 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
         }
         __syncthreads();
     }
-    int gp = 0, ep = 0;
-    for (int w = 0; w < wave; ++w) {
-        gp += sh.wa[w];
-        ep += sh.wb[w];
+    // counts of the waves before this one: lane l reads wave l's, an
+    // exclusive prefix sum over the lanes, read at lane `wave`
+    int gp, ep;
+    {
+        const int ga = wl_ok ? sh.wa[wl] : 0, gb = wl_ok ? sh.wb[wl] : 0;
+        gp = __builtin_amdgcn_readlane(wave_incl_scan_add(ga) - ga, wave);
+        ep = __builtin_amdgcn_readlane(wave_incl_scan_add(gb) - gb, wave);
     }
     int o = gp + (ep < eq_take ? ep : eq_take);
     int e = ep;
@@ -462,54 +496,68 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     int64_t ob = 0;
     if constexpr (CAND_OUT) ob = (static_cast<int64_t>(row) * a.nparts + part) << kps;
     else out = a.idx + static_cast<int64_t>(row) * K;
+    // Per group of four items per lane (item order: lane, then q): the
+    // ballots of the taken items give each item's slot as the taken items
+    // at lower lanes (mbcnt) plus those before it in its lane; ties at T
+    // are ranked the same way among the equal items.
+    auto compact = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
-        bool tk[4], eqv[4];
-        int ne = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            tk[q] = above(4 * g4 + q);
-            eqv[q] = equal(4 * g4 + q);
-            ne += eqv[q] ? 1 : 0;
-        }
-        if (__ballot(ne > 0) != 0ull) {     // wave-uniform: ties at T are rare
-            // rank of each equal item among the equal items in item order
-            const int ein = wave_incl_scan_add(ne);
-            int er = e + ein - ne;
+        for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
+            bool tk[4], eqv[4];
+            uint64_t E[4];
+            uint64_t any_eq = 0ull;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (eqv[q]) {
-                    tk[q] = er < eq_take;
-                    ++er;
-                }
+                const int j = 4 * g4 + q;
+                const bool ok = FULL || valid(j);
+                tk[q] = ok && (take_all || v[j] > Tf);
+                eqv[q] = ok && !take_all && v[j] == Tf;
+                E[q] = __ballot(eqv[q]);
+                any_eq |= E[q];
             }
-            e += __builtin_amdgcn_readlane(ein, 63);
-        }
-        int nt = 0;
+            if (any_eq != 0ull) {           // wave-uniform: ties at T are rare
+                int er = e;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) nt += tk[q] ? 1 : 0;
-        const int tin = wave_incl_scan_add(nt);
-        int slot = o + tin - nt;
+                for (int q = 0; q < 4; ++q) er += lanes_below(E[q]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (tk[q]) {
-                if (slot < keff) {
-                    const int j = 4 * g4 + q;
-                    int32_t p;
-                    if constexpr (CAND_IN) p = pv[j];
-                    else p = start + item(j);
-                    if constexpr (CAND_OUT) {
-                        a.out_key[ob + slot] = v[j];
-                        a.out_pos[ob + slot] = p;
-                    } else {
-                        out[slot] = p;
+                for (int q = 0; q < 4; ++q) {
+                    if (eqv[q]) {
+                        tk[q] = er < eq_take;
+                        ++er;
                     }
+                    e += __popcll(E[q]);
                 }
-                ++slot;
+            }
+            int slot = o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint64_t tm = __ballot(tk[q]);
+                slot += lanes_below(tm);
+                o += __popcll(tm);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (tk[q]) {
+                    if (slot < keff) {
+                        const int j = 4 * g4 + q;
+                        int32_t p;
+                        if constexpr (CAND_IN) p = pv[j];
+                        else p = start + item(j);
+                        if constexpr (CAND_OUT) {
+                            a.out_key[ob + slot] = v[j];
+                            a.out_pos[ob + slot] = p;
+                        } else {
+                            out[slot] = p;
+                        }
+                    }
+                    ++slot;
+                }
             }
         }
-        o += __builtin_amdgcn_readlane(tin, 63);
-    }
+    };
+    if (wave_full) compact(std::true_type{});
+    else compact(std::false_type{});
     if constexpr (CAND_OUT) {
         if (tid == 0) a.out_cnt[static_cast<int64_t>(row) * a.nparts + part] = keff;
     } else {
