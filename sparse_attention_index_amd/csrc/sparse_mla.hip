@@ -326,7 +326,253 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         }
         if (g == 0 && h < Hq)
             *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
-                make_float4(m_run, l_tot, lr_tot, 0.0f);
+                make_float4(m_run, lr_tot, l_tot, 0.0f);
+    }
+}
+
+// The build for the fewest blocks when every split holds at most 64
+// selected slots (one or two rows at K = 2048): 2 waves of 16 heads, and
+// all 64 keys of the split at once instead of two 32-key tiles in turn.
+// Both tiles' rows are requested together (each thread reads its rows'
+// indices itself, so the gather starts as soon as they arrive, without an
+// LDS round trip), S^T is computed for the 64 keys, one softmax runs over
+// them (no running maximum to carry or rescale: the block sees its keys
+// once), and the value product takes two 32-key MFMA steps per feature
+// tile. Against the tile loop this removes one gather round trip, one
+// softmax and two barriers from each block's dependent chain.
+constexpr int kPairKeys = 2 * kTile;
+constexpr size_t kPairLdsBytes =
+    sizeof(uint16_t) * kPairKeys * kKtStride + sizeof(int) * kPairKeys;
+
+__global__ __launch_bounds__(2 * kWave, 1) void sparse_mla_pair_kernel(
+    int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
+    int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
+    const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml, CacheMap cmap) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);
+    int* sidx = reinterpret_cast<int*>(Kt + kPairKeys * kKtStride);
+    constexpr int kThr = 2 * kWave;
+    constexpr int kRP = kThr / 8;                                 // rows per gather pass
+    constexpr int kNP = kPairKeys / kRP;                          // gather passes (4)
+
+    const int L = blockIdx.x;
+    const int item = (L / (8 * hgroups)) * 8 + (L & 7);
+    const int hg = (L / 8) % hgroups;
+    if (item >= nitems) return;
+    const int row = item / nsplit, split = item - row * nsplit;
+    const int64_t b = row / S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int wg = hg * 2 + wave;                                 // 16-head group
+    const int h = wg * 16 + m;
+    const bool active = wg * 16 < Hq;
+    const int j_begin = split * slots_per_split;
+    const int count = min(K, j_begin + slots_per_split) - j_begin;   // 1..64
+    const bool paged = cmap.table != nullptr;
+    const uint16_t* lat_b = latent + (paged ? 0 : b * lat_bs);
+    const uint16_t* rope_b = rope + (paged ? 0 : b * rope_bs);
+    const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
+
+    // Cache rows of the slots (-1: unselected, out of range or page not
+    // present). Every index (and page-table) load is issued unconditionally
+    // at a clamped address and masked afterwards: a lane-dependent branch
+    // around a load makes the compiler wait for it before the next one.
+    const int gkey = tid >> 3, gsub = tid & 7;
+    constexpr int kNI = kNP + 1;                  // the gather rows, then slot tid
+    int sl[kNI], pidx[kNI];
+#pragma unroll
+    for (int u = 0; u < kNI; ++u) {
+        sl[u] = u < kNP ? gkey + kRP * u : tid;
+        pidx[u] = irow[min(sl[u], count - 1)];
+    }
+    if (paged) {
+        int pg[kNI];
+#pragma unroll
+        for (int u = 0; u < kNI; ++u) {
+            const int pc = min(max(pidx[u], 0), Lmax - 1);
+            pg[u] = cmap.table[b * cmap.max_pages + (pc >> cmap.page_shift)];
+        }
+#pragma unroll
+        for (int u = 0; u < kNI; ++u) {
+            const int p = pidx[u];
+            const bool ok = sl[u] < count && p >= 0 && p < Lmax && pg[u] >= 0 &&
+                            pg[u] < cmap.num_pages;
+            pidx[u] = ok ? static_cast<int>((static_cast<int64_t>(pg[u]) << cmap.page_shift) |
+                                            (p & ((1 << cmap.page_shift) - 1)))
+                         : -1;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kNI; ++u) {
+            const int p = pidx[u];
+            pidx[u] = (sl[u] < count && p >= 0 && p < Lmax) ? p : -1;
+        }
+    }
+    int prow[kNP];
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp) prow[pp] = pidx[pp];
+    if (tid < kPairKeys) sidx[tid] = pidx[kNP];
+    uint4 G[kNP][9];
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp) {
+        const int pc = prow[pp] >= 0 ? prow[pp] : 0;
+        const uint16_t* lrow = lat_b + static_cast<int64_t>(pc) * lat_rs + gsub * 8;
+        const uint16_t* rrow = rope_b + static_cast<int64_t>(pc) * rope_rs + gsub * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) G[pp][i] = *reinterpret_cast<const uint4*>(lrow + 64 * i);
+        G[pp][8] = *reinterpret_cast<const uint4*>(rrow);
+    }
+    // Q^T operand: lane (head h, chunk g) holds q[h][32 ks + 8 g .. +7]
+    bf16x8 qreg[kDq / 32];
+    {
+        const uint16_t* qh =
+            q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kDq / 32; ++ks) {
+            uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
+            if (h >= Hq) v = make_uint4(0u, 0u, 0u, 0u);
+            qreg[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp) {
+        const int key = gkey + kRP * pp;
+        if (prow[pp] < 0) {
+#pragma unroll
+            for (int i = 0; i < 9; ++i) G[pp][i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint16_t* dst = Kt + key * kKtStride + gsub * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + 64 * i) = G[pp][i];
+        *reinterpret_cast<uint4*>(dst + 512) = G[pp][8];
+    }
+    __syncthreads();
+
+    float m_tot = -INFINITY, l_tot = 0.0f, lr_tot = 0.0f;
+    v4f acc[kT2];
+#pragma unroll
+    for (int t2 = 0; t2 < kT2; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (active) {
+        // S^T for keys 16 kt .. 16 kt + 15 (kt < 4); lane holds keys 16 kt + 4 g + i
+        v4f s[4];
+        {
+            v4f c[4][2];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) c[kt][0] = c[kt][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            constexpr int kPipe = 2;
+            bf16x8 a[4][kPipe];
+#pragma unroll
+            for (int d = 0; d < kPipe; ++d)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    a[kt][d] = *reinterpret_cast<const bf16x8*>(
+                        Kt + (16 * kt + m) * kKtStride + 8 * g + d * 32);
+#pragma unroll
+            for (int ks = 0; ks < kDq / 32; ++ks) {
+                const int sl = ks % kPipe;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    c[kt][ks & 1] = mfma_bf16_16x16x32(a[kt][sl], qreg[ks], c[kt][ks & 1]);
+                if (ks + kPipe < kDq / 32) {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+                        a[kt][sl] = *reinterpret_cast<const bf16x8*>(
+                            Kt + (16 * kt + m) * kKtStride + 8 * g + (ks + kPipe) * 32);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s[kt] = c[kt][0] + c[kt][1];
+        }
+        // one softmax over the 64 keys (log2 units)
+        float z[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * kt + 4 * g + i;
+                z[4 * kt + i] = sidx[key] >= 0 ? s[kt][i] * scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, z[4 * kt + i]);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        m_tot = tmax;
+        // P^T operands of the two 32-key steps: step u holds keys
+        // 32 u + 4 g + i (i < 4) and 32 u + 16 + 4 g + i, the order of the V^T
+        // transposing reads below
+        bf16x8 pv[2];
+        float psum = 0.0f, prsum = 0.0f;
+        const bool live = tmax != -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float pe = live ? __builtin_amdgcn_exp2f(z[8 * u + i] - tmax) : 0.0f;
+                const __bf16 pb = static_cast<__bf16>(pe);
+                pv[u][i] = pb;
+                psum += pe;
+                prsum += static_cast<float>(pb);
+            }
+        l_tot = psum + __shfl_xor(psum, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        lr_tot = prsum + __shfl_xor(prsum, 16);
+        lr_tot += __shfl_xor(lr_tot, 32);
+        // O^T += V^T P^T over the two 32-key steps
+        const int tr_off = (4 * g + ((lane >> 2) & 3)) * kKtStride + 4 * (lane & 3);
+        auto read_v = [&](int u, int t2) -> bf16x8 {
+            const uint16_t* base = Kt + 32 * u * kKtStride + tr_off + 16 * t2;
+            const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(base));
+            const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(base + 16 * kKtStride));
+            return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        };
+        constexpr int kPipeV = 4;
+        bf16x8 va[kPipeV][2];
+#pragma unroll
+        for (int d = 0; d < kPipeV; ++d) {
+            va[d][0] = read_v(0, d);
+            va[d][1] = read_v(1, d);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const int sl = t2 % kPipeV;
+            acc[t2] = mfma_bf16_16x16x32(va[sl][0], pv[0], acc[t2]);
+            acc[t2] = mfma_bf16_16x16x32(va[sl][1], pv[1], acc[t2]);
+            if (t2 + kPipeV < kT2) {
+                va[sl][0] = read_v(0, t2 + kPipeV);
+                va[sl][1] = read_v(1, t2 + kPipeV);
+            }
+        }
+    }
+    if (!active) return;
+    // lane holds O^T[16 t2 + 4 g + i][h], i = 0..3
+    if (nsplit == 1) {
+        if (h >= Hq) return;
+        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+        uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const uint32_t lo = pack_bf16x2(acc[t2][0] * inv, acc[t2][1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[t2][2] * inv, acc[t2][3] * inv);
+            *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
+        }
+        if (lse != nullptr && g == 0)
+            lse[static_cast<int64_t>(row) * Hq + h] =
+                l_tot > 0.0f ? m_tot * 0.69314718055994531f + logf(l_tot) : -INFINITY;
+    } else {
+        const int nwg = (Hq + 15) / 16;
+        const int64_t blk = (static_cast<int64_t>(row) * nsplit + split) * nwg + wg;
+        uint16_t* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const uint32_t lo = pack_bf16x2(acc[t2][0], acc[t2][1]);
+            const uint32_t hi = pack_bf16x2(acc[t2][2], acc[t2][3]);
+            __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(wo + t2 * 256));
+        }
+        if (g == 0 && h < Hq)
+            *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
+                make_float4(m_tot, lr_tot, l_tot, 0.0f);
     }
 }
 
@@ -380,8 +626,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
         const float M = wave_max_dpp(ml.x);
         const float e = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
         if (lane < nsplit) wgt[lane][mm] = e;
-        const float Ls = wave_incl_sum_f(ml.y * e);
-        const float Lrs = wave_incl_sum_f(ml.z * e);
+        const float Ls = wave_incl_sum_f(ml.z * e);
+        const float Lrs = wave_incl_sum_f(ml.y * e);
         if (lane == 63) {
             s_M[mm] = M;
             s_L[mm] = Ls;
@@ -426,22 +672,26 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
     }
 }
 
-// Merge for the fewest rows (the grid of the 32-head build): one 64-thread
-// block per (row, 16-head group, 16-feature tile t2), so that even one row's
-// merge spreads over the whole chip, with no LDS and no barrier. Lane
-// l = 16 g + m reads what lane l of each producing wave stored (head m,
-// features 16 t2 + 4 g .. +3) and its head's (m, l, lr) triple; every load of
-// a chunk of CH splits is issued before the first is used, so a row's merge
-// costs one memory round trip per chunk instead of one for the weights and
-// more for the partials. The accumulators follow the running maximum of m
-// (log-sum-exp rule); with a single chunk each split is weighted by
-// 2^(m_s - max m) directly, as in combine_kernel.
-template <int CH>
+// Merge for the fewest rows (the grid of the 32-head builds, at most 32
+// splits): one 64-thread block per (row, 16-head group, 16-feature tile t2),
+// so that even one row's merge spreads over the whole chip, with no barrier
+// across waves. Lane l = 16 g + m reads what lane l of each producing wave
+// stored (head m, features 16 t2 + 4 g .. +3). The (m, lr) pairs of head m
+// are shared out over its four lanes (lane g loads splits g, g + 4, ...), so
+// each pair is read once per block instead of once per lane; the head's
+// maximum and its normalisation come from two lane exchanges, and the
+// per-split weights 2^(m_s - M) go through LDS to the lanes that scale the
+// partials. Every load (pairs and partials) is issued before the first one
+// is used: one memory round trip.
+constexpr int kMergeMaxSplits = 32;
+
 __global__ __launch_bounds__(64) void merge_few_kernel(int Hq, int nsplit,
                                                        const uint16_t* __restrict__ ws_o,
                                                        const float* __restrict__ ws_ml,
                                                        uint16_t* __restrict__ out,
                                                        float* __restrict__ lse) {
+    __shared__ float wgt[16][kMergeMaxSplits + 1];
+    constexpr int kPer = kMergeMaxSplits / 4;                    // splits per lane
     const int nwg = (Hq + 15) / 16;
     const int lane = threadIdx.x;
     const int t2 = static_cast<int>(blockIdx.x % kT2);
@@ -454,57 +704,74 @@ __global__ __launch_bounds__(64) void merge_few_kernel(int Hq, int nsplit,
     const int64_t ps = static_cast<int64_t>(nwg) * kT2 * 64 * 4;   // split stride of the partials
     const float* mb = ws_ml + (row * nsplit * Hq + hc) * 4;
     const int64_t ms = static_cast<int64_t>(Hq) * 4;               // split stride of the triples
+    const bool want_lse = lse != nullptr && t2 == 0;
 
+    // loads at clamped split indices, masked after arrival (a lane-dependent
+    // branch around each load would make the compiler wait for every one)
+    float2 mlr[kPer];
+    float lsum[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int sp = min(g + 4 * k, nsplit - 1);
+        mlr[k] = *reinterpret_cast<const float2*>(mb + sp * ms);
+        lsum[k] = mb[sp * ms + 2];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        if (g + 4 * k >= nsplit) {
+            mlr[k] = make_float2(-INFINITY, 0.0f);
+            lsum[k] = 0.0f;
+        }
+    }
+    uint2 w[kMergeMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMergeMaxSplits; ++sp)
+        w[sp] = *reinterpret_cast<const uint2*>(pb + min(sp, nsplit - 1) * ps);
+
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) M = fmaxf(M, mlr[k].x);
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    float Lr = 0.0f, Ls = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const float e = mlr[k].x == -INFINITY ? 0.0f : exp2f(mlr[k].x - M);
+        if (g + 4 * k < nsplit) wgt[m][g + 4 * k] = e;
+        Lr += mlr[k].y * e;
+        Ls += lsum[k] * e;
+    }
+    Lr += __shfl_xor(Lr, 16);
+    Lr += __shfl_xor(Lr, 32);
+    __syncthreads();
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float M = -INFINITY, Ls = 0.0f, Lr = 0.0f;
-    for (int s0 = 0; s0 < nsplit; s0 += CH) {
-        float4 ml[CH];
-        uint2 w[CH];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            ml[c] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
-            w[c] = make_uint2(0u, 0u);
-            if (s0 + c < nsplit) {
-                ml[c] = *reinterpret_cast<const float4*>(mb + (s0 + c) * ms);
-                w[c] = *reinterpret_cast<const uint2*>(pb + (s0 + c) * ps);
-            }
+    for (int sp = 0; sp < kMergeMaxSplits; ++sp) {
+        if (sp < nsplit) {                      // uniform
+            const float e = wgt[m][sp];
+            a.x += e * __uint_as_float(w[sp].x << 16);
+            a.y += e * __uint_as_float(w[sp].x & 0xFFFF0000u);
+            a.z += e * __uint_as_float(w[sp].y << 16);
+            a.w += e * __uint_as_float(w[sp].y & 0xFFFF0000u);
         }
-        float Mn = M;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, ml[c].x);
-        const float r = M == -INFINITY ? 0.0f : exp2f(M - Mn);
-        M = Mn;
-        Ls *= r;
-        Lr *= r;
-        a.x *= r;
-        a.y *= r;
-        a.z *= r;
-        a.w *= r;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const float e = ml[c].x == -INFINITY ? 0.0f : exp2f(ml[c].x - Mn);
-            Ls += ml[c].y * e;
-            Lr += ml[c].z * e;
-            a.x += e * __uint_as_float(w[c].x << 16);
-            a.y += e * __uint_as_float(w[c].x & 0xFFFF0000u);
-            a.z += e * __uint_as_float(w[c].y << 16);
-            a.w += e * __uint_as_float(w[c].y & 0xFFFF0000u);
-        }
+    }
+    if (want_lse) {
+        Ls += __shfl_xor(Ls, 16);
+        Ls += __shfl_xor(Ls, 32);
     }
     if (h >= Hq) return;
     const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
     *reinterpret_cast<uint2*>(out + (row * Hq + h) * kDl + 16 * t2 + 4 * g) =
         make_uint2(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv));
-    if (lse != nullptr && t2 == 0 && g == 0)
+    if (want_lse && g == 0)
         lse[row * Hq + h] = Ls > 0.0f ? M * 0.69314718055994531f + logf(Ls) : -INFINITY;
 }
 
-template <int CH>
 static hipError_t launch_merge_few(hipStream_t stream, int rows, int Hq, int ns,
                                    const uint16_t* ws_o, const float* ws_ml, uint16_t* out,
                                    float* lse) {
     const unsigned blocks = static_cast<unsigned>(rows) * ((Hq + 15) / 16) * kT2;
-    hipLaunchKernelGGL(merge_few_kernel<CH>, dim3(blocks), dim3(64), 0, stream, Hq, ns, ws_o, ws_ml,
+    hipLaunchKernelGGL(merge_few_kernel, dim3(blocks), dim3(64), 0, stream, Hq, ns, ws_o, ws_ml,
                        out, lse);
     return hipGetLastError();
 }
@@ -577,7 +844,18 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     const int nb_few = ((nitems + 7) / 8) * 8 * hg_few;
     const bool few = nb_few <= 256;
     hipError_t e;
-    if (few) {
+    if (few && sps <= kPairKeys) {
+        // fewest blocks, splits of at most 64 slots: all of a split's keys at
+        // once, 32 heads (2 waves) per block
+        e = set_dynamic_lds_limit(reinterpret_cast<const void*>(&sparse_mla_pair_kernel),
+                                  static_cast<int>(kPairLdsBytes));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sparse_mla_pair_kernel, dim3(nb_few), dim3(2 * kWave), kPairLdsBytes,
+                           stream, S, Hq, Lmax, K, sps, ns, nitems, hg_few, q, latent, lat_rs,
+                           lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml,
+                           cmap);
+        e = hipGetLastError();
+    } else if (few) {
         // fewest blocks: 32 heads (2 waves) per block, one block per CU; twice
         // the blocks of the 64-head build and half its LDS operand reads per
         // CU and tile (the two head groups of a (row, split) gather the same
@@ -597,10 +875,8 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     }
     if (e != hipSuccess) return e;
     if (ns > 1) {
-        if (few) {
-            e = ns <= 8    ? launch_merge_few<8>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse)
-                : ns <= 16 ? launch_merge_few<16>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse)
-                           : launch_merge_few<32>(stream, rows, Hq, ns, ws_o, ws_ml, out, lse);
+        if (few && ns <= kMergeMaxSplits) {
+            e = launch_merge_few(stream, rows, Hq, ns, ws_o, ws_ml, out, lse);
         } else {
             hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
                                stream, Hq, ns, ws_o, ws_ml, out, lse);
