@@ -1,9 +1,11 @@
 """Benchmark of the DSA hot path on one MI355X.
 
 One step = one decode step of the whole path on one batch of synthetic
-queries, replayed as one captured HIP graph per cache replica: call 1
-(append the new key, quantise q, lightning-indexer score), call 2 (causal
-top-2048), call 3 (sparse absorbed MLA). The default workload
+queries, launched as a serving loop issues it: the three C-ABI calls on the
+stream, call 1 (append the new key, quantise q, lightning-indexer score),
+call 2 (causal top-2048), call 3 (sparse absorbed MLA), with argument
+structs built once per cache replica outside the timed region. The same
+steps replayed as one captured HIP graph per step are reported beside it. The default workload
 is decode at L = 16384 (B = 1), the configuration the headline metric is
 quoted on; --workload selects another one (batch32, decode128k).
 
@@ -271,10 +273,45 @@ def capture(fn):
 
 # ------------------------------------------------------------- timing --
 
+def eager_stepper(wl, st):
+    """The step as a serving loop issues it: the three C-ABI calls launched on
+    the stream, argument structs built once per replica outside the timed
+    region. Returns steps(first, n), which enqueues steps first..first+n-1."""
+    import ctypes
+
+    import torch
+
+    import sparse_attention_index_amd as dsa
+
+    L = dsa.lib()
+    ia = [dsa.indexer_args(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], rep["kc"],
+                           rep["ks"], st["scores"], k_raw=st["k_new"], q_fp8=st["q8"],
+                           q_scale=st["qs"]) for rep in st["reps"]]
+    ma = [dsa.mla_args(st["q_mla"], rep["latent"], rep["kpe"], st["idx"], wl.softmax_scale,
+                       st["out"], workspace=st["mla_ws"]) for rep in st["reps"]]
+    ta = dsa.topk_args(st["scores"], st["pos"], wl.K, st["idx"], workspace=st["topk_ws"])
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    byref = ctypes.byref
+    R = st["R"]
+    st["eager_args"] = (ia, ta, ma)               # kept alive with the state
+
+    def steps(first, n):
+        for i in range(first, first + n):
+            r = i % R
+            c1 = L.dsa_indexer(byref(ia[r]), sp)
+            c2 = L.dsa_topk(byref(ta), sp)
+            c3 = L.dsa_sparse_mla(byref(ma[r]), sp)
+            if c1 or c2 or c3:
+                raise RuntimeError(f"step {i}: status {c1} {c2} {c3}")
+
+    return steps
+
+
 def measure(wl, st, steps, warmup):
-    """Time `steps` steps (one captured graph per replica, replayed in
-    rotation) and each call's average device time; returns the figures of
-    the bench record."""
+    """Time `steps` steps launched eagerly (three C-ABI calls per step, the
+    replicas in rotation), the same steps replayed as one captured graph per
+    step, and each call's average device time; returns the figures of the
+    bench record."""
     import torch
 
     calls = make_calls(wl, st)
@@ -291,17 +328,14 @@ def measure(wl, st, steps, warmup):
     for r in range(min(R, 3)):
         step(r)
     torch.cuda.synchronize()
-    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
-    call_graphs = {c: capture(lambda c=c: [calls[c](r) for r in range(R)]) for c in calls}
-    for i in range(warmup):
-        step_graphs[i % R].replay()
+    run = eager_stepper(wl, st)
+    run(0, warmup)
     torch.cuda.synchronize()
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(steps):
-        step_graphs[i % R].replay()
+    run(warmup, steps)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -310,14 +344,28 @@ def measure(wl, st, steps, warmup):
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
-        step_graphs[i % R].replay()
+        run(i, 1)
         evs[i + 1].record()
     torch.cuda.synchronize()
     per_step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(steps)])
     quantiles = {k: round(float(np.percentile(per_step_us, q)), 2)
                  for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
 
+    # the same steps as one captured graph per step, replayed in rotation
+    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    for i in range(min(warmup, R)):
+        step_graphs[i % R].replay()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step_graphs[i % R].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop)
+    del step_graphs
+
     # per-call device time: each call graph runs the call once per replica
+    call_graphs = {c: capture(lambda c=c: [calls[c](r) for r in range(R)]) for c in calls}
     reps_call = max(1, (steps + R - 1) // R)
     avg_us = {}
     for c, g in call_graphs.items():
@@ -330,7 +378,7 @@ def measure(wl, st, steps, warmup):
         b.record()
         torch.cuda.synchronize()
         avg_us[c] = a.elapsed_time(b) * 1000.0 / (reps_call * R)
-    del step_graphs, call_graphs
+    del call_graphs
 
     n_valid = [int(p) + 1 for p in st["x"]["pos"].reshape(-1)]
     keff = [min(wl.K, n) for n in n_valid]
@@ -340,6 +388,7 @@ def measure(wl, st, steps, warmup):
     return dict(ab=ab, dom=dom, avg_us=avg_us, ms_per_step=ms_per_step, quantiles=quantiles,
                 achieved=ab[dom] / (avg_us[dom] * 1e-6) / 1e9,
                 value=wl.B * wl.S * steps / (total_ms / 1000.0),
+                graph_us_per_step=graph_ms * 1000.0 / steps,
                 step_hbm_frac=round(ab["step"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
 
@@ -359,6 +408,7 @@ def other_workloads_leg(args):
         out[name] = {
             "value": round(m["value"], 1), "unit": "queries/s",
             "ms_per_step": round(m["ms_per_step"], 5),
+            "graph_per_step_us": round(m["graph_us_per_step"], 2),
             "step_us_quantiles": m["quantiles"],
             "config": {"B": wl.B, "L": wl.Lmax, "topk": wl.K, "replicas": st["R"],
                        "replica_bytes": st["per_replica"]},
@@ -460,38 +510,6 @@ def variants_leg(wl, st, page=64):
 
     chained_us = _graph_us(dense_step, R)
 
-    # the same dense step launched eagerly: three C-ABI calls per step on the
-    # stream (argument structs built once, outside the timed region)
-    L = dsa.lib()
-    ia, ta, ma = [], [], []
-    for rep in st["reps"]:
-        ia.append(dsa.indexer_args(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"],
-                                   rep["kc"], rep["ks"], st["scores"], k_raw=st["k_new"],
-                                   q_fp8=st["q8"], q_scale=st["qs"]))
-        ma.append(dsa.mla_args(st["q_mla"], rep["latent"], rep["kpe"], st["idx"],
-                               wl.softmax_scale, st["out"], workspace=st["mla_ws"]))
-    ta = dsa.topk_args(st["scores"], st["pos"], wl.K, st["idx"], workspace=st["topk_ws"])
-    import ctypes
-    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    byref = ctypes.byref
-
-    def eager_steps(n):
-        for i in range(n):
-            r = i % R
-            L.dsa_indexer(byref(ia[r]), sp)
-            L.dsa_topk(byref(ta), sp)
-            L.dsa_sparse_mla(byref(ma[r]), sp)
-
-    eager_steps(R)
-    torch.cuda.synchronize()
-    n_eager = max(200, 2 * R)
-    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a_ev.record()
-    eager_steps(n_eager)
-    b_ev.record()
-    torch.cuda.synchronize()
-    eager_us = a_ev.elapsed_time(b_ev) * 1000.0 / n_eager
-
     def had_idx(r):
         rep = st["reps"][r % R]
         dsa.indexer(st["q_raw"], st["w"], st["pos"], st["cos"], st["sin"], rep["kc"], rep["ks"],
@@ -518,11 +536,6 @@ def variants_leg(wl, st, page=64):
                            "unit": "queries/s",
                            "note": "the same dense step, one graph holding one step per "
                                    "replica back to back (no per-step graph launch)"},
-        "eager_decode": {"us_per_step": round(eager_us, 2),
-                         "value": round(B * wl.S / (eager_us * 1e-6), 1),
-                         "unit": "queries/s",
-                         "note": f"the same dense step, {n_eager} steps launched eagerly "
-                                 "(three C-ABI calls per step on the stream, no graph)"},
         "paged_decode": {"workload": f"{wl.name} on paged caches (page_size {page}, permuted "
                                     f"pool of {num_pages} pages)",
                          "value": round(B * wl.S / (paged_us * 1e-6), 1), "unit": "queries/s",
@@ -853,7 +866,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations and caches; no trained weights)",
         "config": {"workload": wl.name, "B": wl.B, "L": wl.Lmax, "indexer_heads": wl.H,
                    "attn_heads": wl.Hq, "topk": wl.K, "replicas": st["R"],
-                   "replica_bytes": st["per_replica"], "launch": "one HIP graph per step"},
+                   "replica_bytes": st["per_replica"],
+                   "launch": "eager: three C-ABI calls per step on the stream"},
         "step_us_quantiles": m["quantiles"],
         "step_algorithmic_bytes": ab["step"],
         "step_hbm_frac": m["step_hbm_frac"],
@@ -868,6 +882,11 @@ def main():
     }
     if not args.no_variants:
         rec["variants"] = variants_leg(wl, st)
+        rec["variants"]["graph_per_step"] = {
+            "us_per_step": round(m["graph_us_per_step"], 2),
+            "value": round(wl.B * wl.S / (m["graph_us_per_step"] * 1e-6), 1),
+            "unit": "queries/s",
+            "note": "the same timed steps, each replayed as one captured HIP graph"}
     del st, m
     torch.cuda.empty_cache()
     if not args.no_others:

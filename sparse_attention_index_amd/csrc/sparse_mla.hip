@@ -344,7 +344,8 @@ constexpr int kPairKeys = 2 * kTile;
 constexpr size_t kPairLdsBytes =
     sizeof(uint16_t) * kPairKeys * kKtStride + sizeof(int) * kPairKeys;
 
-__global__ __launch_bounds__(2 * kWave, 1) void sparse_mla_pair_kernel(
+template <int HPB>
+__global__ __launch_bounds__(4 * HPB, 1) void sparse_mla_pair_kernel(
     int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
     int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
@@ -353,9 +354,9 @@ __global__ __launch_bounds__(2 * kWave, 1) void sparse_mla_pair_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* Kt = reinterpret_cast<uint16_t*>(smem);
     int* sidx = reinterpret_cast<int*>(Kt + kPairKeys * kKtStride);
-    constexpr int kThr = 2 * kWave;
+    constexpr int kThr = 4 * HPB;                                 // one wave per 16 heads
     constexpr int kRP = kThr / 8;                                 // rows per gather pass
-    constexpr int kNP = kPairKeys / kRP;                          // gather passes (4)
+    constexpr int kNP = kPairKeys / kRP;                          // gather passes (4 or 2)
 
     const int L = blockIdx.x;
     const int item = (L / (8 * hgroups)) * 8 + (L & 7);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(2 * kWave, 1) void sparse_mla_pair_kernel(
     const int64_t b = row / S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int wg = hg * 2 + wave;                                 // 16-head group
+    const int wg = hg * (HPB / 16) + wave;                        // 16-head group
     const int h = wg * 16 + m;
     const bool active = wg * 16 < Hq;
     const int j_begin = split * slots_per_split;
@@ -821,6 +822,22 @@ static hipError_t launch_mla_kernel(dim3 grid, hipStream_t stream, int S, int Hq
     return hipGetLastError();
 }
 
+template <int HPB>
+static hipError_t launch_pair(dim3 grid, hipStream_t stream, int S, int Hq, int Lmax, int K,
+                              int sps, int ns, int nitems, int hgroups, const uint16_t* q,
+                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
+                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
+                              const int32_t* idx, float scale_log2, uint16_t* out, float* lse,
+                              uint16_t* ws_o, float* ws_ml, CacheMap cmap) {
+    const hipError_t attr = set_dynamic_lds_limit(
+        reinterpret_cast<const void*>(&sparse_mla_pair_kernel<HPB>), static_cast<int>(kPairLdsBytes));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((sparse_mla_pair_kernel<HPB>), grid, dim3(4 * HPB), kPairLdsBytes, stream, S,
+                       Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs, lat_bs, rope,
+                       rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16_t* q,
                              const uint16_t* latent, int64_t lat_rs, int64_t lat_bs,
                              const uint16_t* rope, int64_t rope_rs, int64_t rope_bs,
@@ -847,14 +864,15 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     if (few && sps <= kPairKeys) {
         // fewest blocks, splits of at most 64 slots: all of a split's keys at
         // once, 32 heads (2 waves) per block
-        e = set_dynamic_lds_limit(reinterpret_cast<const void*>(&sparse_mla_pair_kernel),
-                                  static_cast<int>(kPairLdsBytes));
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(sparse_mla_pair_kernel, dim3(nb_few), dim3(2 * kWave), kPairLdsBytes,
-                           stream, S, Hq, Lmax, K, sps, ns, nitems, hg_few, q, latent, lat_rs,
-                           lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml,
-                           cmap);
-        e = hipGetLastError();
+        e = launch_pair<kHeadsPerBlockFew>(dim3(nb_few), stream, S, Hq, Lmax, K, sps, ns, nitems,
+                                           hg_few, q, latent, lat_rs, lat_bs, rope, rope_rs,
+                                           rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    } else if (nblocks <= 256 && sps <= kPairKeys) {
+        // at most one block per CU, splits of at most 64 slots: the same with
+        // 64 heads (4 waves) per block
+        e = launch_pair<kHeadsPerBlock>(dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns, nitems,
+                                        hgroups, q, latent, lat_rs, lat_bs, rope, rope_rs,
+                                        rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
     } else if (few) {
         // fewest blocks: 32 heads (2 waves) per block, one block per CU; twice
         // the blocks of the 64-head build and half its LDS operand reads per
@@ -875,7 +893,8 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
     }
     if (e != hipSuccess) return e;
     if (ns > 1) {
-        if (few && ns <= kMergeMaxSplits) {
+        const int64_t merge_blocks = static_cast<int64_t>(rows) * nwg * kT2;
+        if (ns <= kMergeMaxSplits && merge_blocks <= 2048) {
             e = launch_merge_few(stream, rows, Hq, ns, ws_o, ws_ml, out, lse);
         } else {
             hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
