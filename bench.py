@@ -542,7 +542,7 @@ def variants_leg(wl, st, page=64):
                          "us_per_step": round(paged_us, 2),
                          "note": "timed like chained_decode"},
         "indexer_hadamard_pow2": {"avg_us": round(had_us, 2),
-                                  "note": "three launches (prepare k, prepare q, score)"},
+                                  "note": "one fused launch (rotate, quantise and append the key, rotate and quantise q, score)"},
         "mla_append": {"avg_us": round(app_us, 2),
                        "bytes": int(B * wl.S * (1024 * 2 + 128 * 2 + wl.Hq * 128 * 2)),
                        "note": "latent row copy, rotary key and 128 query rope parts"},

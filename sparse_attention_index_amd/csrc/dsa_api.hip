@@ -26,7 +26,8 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                                const void* k_raw, const int32_t* pos, const float* cos_t,
                                const float* sin_t, const float* w, uint8_t* kcache,
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
-                               int64_t ld, CacheMap cmap, hipStream_t stream);
+                               int64_t ld, CacheMap cmap, bool hadamard, bool pow2,
+                               hipStream_t stream);
 hipError_t launch_topk(int rows, int Lmax, int K, const float* scores, int64_t ld,
                        const int32_t* pos, int32_t* idx, int32_t* count, void* workspace,
                        hipStream_t stream);
@@ -145,10 +146,10 @@ dsa_status check_indexer(const dsa_indexer_args* a) {
     return check_paging(a->block_table, a->page_size, a->max_pages, a->num_pages, a->Lmax);
 }
 
-// the fused single-row decode launch covers the plain preparation only
+// one query row per batch row: the fused decode launch (with or without the
+// Hadamard and power-of-two options)
 bool fused_decode(const dsa_indexer_args* a) {
-    return a->S == 1 &&
-           !(a->flags & (DSA_INDEXER_APPEND_ONLY | DSA_INDEXER_HADAMARD | DSA_INDEXER_POW2_SCALE));
+    return a->S == 1 && !(a->flags & DSA_INDEXER_APPEND_ONLY);
 }
 
 size_t indexer_ws(const dsa_indexer_args* a) {
@@ -386,7 +387,8 @@ dsa_status dsa_indexer(const dsa_indexer_args* a, hipStream_t stream) {
         // decode: one fused launch (quantise q, append the new key, score)
         e = dsa::launch_decode_score(bf16, a->B, a->H, a->Lmax, a->P, a->q_raw, a->k_raw, a->pos,
                                      a->rope_cos, a->rope_sin, a->w, a->k_cache, a->k_scale,
-                                     a->q_fp8, a->q_scale, a->scores, a->ld_scores, cmap, stream);
+                                     a->q_fp8, a->q_scale, a->scores, a->ld_scores, cmap, had,
+                                     pow2, stream);
         return hip_status(e);
     }
     if (a->k_raw != nullptr) {

@@ -525,6 +525,41 @@ __device__ __forceinline__ float round_act(float v) {
     return BF16_IN ? bf16_bits_to_float(float_to_bf16_bits(v)) : v;
 }
 
+// the same for two values at once with the hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even, as the bit rule above for every
+// finite float)
+template <bool BF16_IN>
+__device__ __forceinline__ void round_act2(float& a, float& b) {
+    if constexpr (BF16_IN) {
+        const uint32_t pk = pack_bf16x2(a, b);
+        a = __uint_as_float(pk << 16);
+        b = __uint_as_float(pk & 0xFFFF0000u);
+    }
+}
+
+// v of the lane whose index differs in bit M: quad permutations (DPP, no
+// LDS traffic) for M = 1, 2, a cross-lane shuffle otherwise
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    if constexpr (M == 1)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    else if constexpr (M == 2)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    else
+        return __shfl_xor(v, M);
+}
+
+// one butterfly stage across the lanes whose index differs in bit M (M < TPH)
+template <int M, int N>
+__device__ __forceinline__ void wht_xlanes(float (&v)[N], int e) {
+    const bool upper = (e & M) != 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const float pa = lane_xor<M>(v[j]);
+        v[j] = upper ? pa - v[j] : v[j] + pa;
+    }
+}
+
 template <int U>
 struct DecChunk {
     uint4 k[U][2];      // key codes: lane (m, g), key 16 u + m, bytes [32 g, 32 g + 32)
@@ -537,7 +572,7 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
     const float* __restrict__ sin_t, const float* __restrict__ w, uint8_t* __restrict__ kcache,
     float* __restrict__ kscale, uint8_t* __restrict__ q8_out, float* __restrict__ qs_out,
-    float* __restrict__ scores, int64_t ld, CacheMap cmap) {
+    float* __restrict__ scores, int64_t ld, CacheMap cmap, int had, int pow2) {
     constexpr int kThreads = NW * 64;
     constexpr int kTPH = kThreads / 64;                 // threads per query head
     constexpr int kFPT = 128 / kTPH;                    // features per thread
@@ -588,7 +623,14 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     constexpr int kHalf = kTPH / 2;
     const int hh = tid / kTPH, e = tid % kTPH;
     float qv[kFPT];
-    if (hh < H) {
+#pragma unroll
+    for (int j = 0; j < kFPT; ++j) qv[j] = 0.0f;
+    if (hh < H && had) {
+        // Hadamard option: thread e holds the contiguous features [FPT e, FPT e + FPT)
+        const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128 + kFPT * e;
+#pragma unroll
+        for (int j = 0; j < kFPT; ++j) qv[j] = load_act<BF16_IN>(q_raw, base + j);
+    } else if (hh < H) {
         const int64_t base = (static_cast<int64_t>(row) * H + hh) * 128;
         if (e < kHalf) {
             const int j0 = (kFPT / 2) * e;
@@ -646,7 +688,60 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
 #pragma clang fp contract(off)
         float v[kFPT];
         float amax = 0.0f;
-        if (hh < H) {
+        if (had) {
+            // contiguous layout: the rotary partner of feature f < 64 (f +- 32)
+            // sits in thread e ^ (32 / FPT) at the same j; every lane takes
+            // part in the exchanges (a head's threads are adjacent lanes)
+            constexpr int kPairX = 32 / kFPT;
+            const bool rot = kFPT * e < 64, lower = kFPT * e < 32;
+            const int64_t tb = static_cast<int64_t>(p) * 32 + ((kFPT * e) & 31);
+#pragma unroll
+            for (int j = 0; j < kFPT; ++j) {
+                const float other = lane_xor<kPairX>(qv[j]);
+                float r = qv[j];
+                if (rot) {
+                    const float c = cos_t[tb + j], sn = sin_t[tb + j];
+                    if (lower) {
+                        const float ac = qv[j] * c, bs = other * sn;
+                        r = ac - bs;
+                    } else {
+                        const float as = other * sn, bc = qv[j] * c;
+                        r = as + bc;
+                    }
+                }
+                v[j] = r;
+            }
+            // cast back to the activation dtype (the non-rotary values are
+            // already representable, so rounding them changes nothing)
+#pragma unroll
+            for (int j = 0; j < kFPT; j += 2) round_act2<BF16_IN>(v[j], v[j + 1]);
+            // H_128 x / sqrt(128): butterflies (x[f], x[f + s]) -> (sum,
+            // difference) over every bit of the feature index; strides below
+            // FPT inside the thread, the others across the head's lanes
+#pragma unroll
+            for (int st = 1; st < kFPT; st <<= 1)
+#pragma unroll
+                for (int j = 0; j < kFPT; ++j)
+                    if ((j & st) == 0) {
+                        const float lo = v[j], hi = v[j + st];
+                        v[j] = lo + hi;
+                        v[j + st] = lo - hi;
+                    }
+            wht_xlanes<1>(v, e);
+            if constexpr (kTPH > 2) wht_xlanes<2>(v, e);
+            if constexpr (kTPH > 4) wht_xlanes<4>(v, e);
+            static_assert(kTPH <= 8, "a head spans at most 8 lanes");
+#pragma unroll
+            for (int j = 0; j < kFPT; j += 2) {
+                v[j] *= kInvSqrt128;
+                v[j + 1] *= kInvSqrt128;
+                round_act2<BF16_IN>(v[j], v[j + 1]);
+            }
+            if (hh < H) {
+#pragma unroll
+                for (int j = 0; j < kFPT; ++j) amax = fmaxf(amax, fabsf(v[j]));
+            }
+        } else if (hh < H) {
             if (e < kHalf) {
                 const int j0 = (kFPT / 2) * e;
                 const float* c = cos_t + static_cast<int64_t>(p) * 32 + j0;
@@ -657,8 +752,9 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
                     const float bb = qv[kFPT / 2 + j];
                     const float ac = a * c[j], bs = bb * sn[j];
                     const float as = a * sn[j], bc = bb * c[j];
-                    v[j] = round_act<BF16_IN>(ac - bs);
-                    v[kFPT / 2 + j] = round_act<BF16_IN>(as + bc);
+                    v[j] = ac - bs;
+                    v[kFPT / 2 + j] = as + bc;
+                    round_act2<BF16_IN>(v[j], v[kFPT / 2 + j]);
                 }
             } else {
 #pragma unroll
@@ -670,7 +766,8 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
 #pragma unroll
         for (int o = 1; o < kTPH; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
         float scale = amax / 448.0f;
-        if (!(scale > 0.0f)) scale = 1.0f;
+        if (pow2) scale = scale > 0.0f ? pow2_ceil(scale) : 1.0f;
+        else if (!(scale > 0.0f)) scale = 1.0f;
         uint32_t pk[kFPT / 4];
         if (quotient_fast(scale)) {
             const float rs = 1.0f / scale;
@@ -689,9 +786,11 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
 #pragma unroll
         for (int i = 0; i < kFPT / 4; ++i) pk[i] = hh < H ? pk[i] : 0u;
         // parts e < TPH/2: bytes [j0, j0 + FPT/2) and [32 + j0, ...); others [f0, f0 + FPT)
+        // (Hadamard option: every part [FPT e, FPT e + FPT))
         uint8_t* dst = qcodes + hh * 128;
-        const int off0 = e < kHalf ? (kFPT / 2) * e : 64 + kFPT * (e - kHalf);
-        const int off1 = e < kHalf ? 32 + (kFPT / 2) * e : off0 + kFPT / 2;
+        const int off0 = had ? kFPT * e : (e < kHalf ? (kFPT / 2) * e : 64 + kFPT * (e - kHalf));
+        const int off1 = had ? kFPT * e + kFPT / 2
+                             : (e < kHalf ? 32 + (kFPT / 2) * e : off0 + kFPT / 2);
 #pragma unroll
         for (int i = 0; i < kFPT / 16; ++i) {          // FPT/2 bytes per half, 8 per store
             reinterpret_cast<uint2*>(dst + off0)[i] = make_uint2(pk[2 * i], pk[2 * i + 1]);
@@ -719,10 +818,27 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
             y0 = as + bc;
         }
         y0 = round_act<BF16_IN>(y0);
-        const float amax = wave_max(fmaxf(fabsf(y0), fabsf(x1)));
+        float y1 = x1;
+        if (had) {
+            // H_128 x / sqrt(128): stride 64 inside the lane, 1 .. 32 across lanes
+            const float lo = y0 + y1, hi = y0 - y1;
+            y0 = lo;
+            y1 = hi;
+#pragma unroll
+            for (int st = 1; st < 64; st <<= 1) {
+                const bool upper = (lane & st) != 0;
+                const float p0 = __shfl_xor(y0, st), p1 = __shfl_xor(y1, st);
+                y0 = upper ? p0 - y0 : y0 + p0;
+                y1 = upper ? p1 - y1 : y1 + p1;
+            }
+            y0 = round_act<BF16_IN>(y0 * kInvSqrt128);
+            y1 = round_act<BF16_IN>(y1 * kInvSqrt128);
+        }
+        const float amax = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
         float scale = amax / 448.0f;
-        if (!(scale > 0.0f)) scale = 1.0f;
-        const uint8_t c0 = e4m3_encode(y0 / scale), c1 = e4m3_encode(x1 / scale);
+        if (pow2) scale = scale > 0.0f ? pow2_ceil(scale) : 1.0f;
+        else if (!(scale > 0.0f)) scale = 1.0f;
+        const uint8_t c0 = e4m3_encode(y0 / scale), c1 = e4m3_encode(y1 / scale);
         kcodes[lane] = c0;
         kcodes[lane + 64] = c1;
         uint8_t* kdst = kcache + prow * 128;
@@ -850,7 +966,8 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                                const void* k_raw, const int32_t* pos, const float* cos_t,
                                const float* sin_t, const float* w, uint8_t* kcache,
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
-                               int64_t ld, CacheMap cmap, hipStream_t stream) {
+                               int64_t ld, CacheMap cmap, bool hadamard, bool pow2,
+                               hipStream_t stream) {
     constexpr int kLoopChunk = DSA_DEC_LOOP_NW * 64;
     const int chunksl = (Lmax + kLoopChunk - 1) / kLoopChunk;
     const bool loop = static_cast<int64_t>(B) * chunksl > DSA_DEC_LOOP_BLOCKS;
@@ -870,7 +987,7 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
 #define DSA_DEC(UU, NWW, LP, BF)                                                                 \
     hipLaunchKernelGGL((decode_score_kernel<UU, NWW, LP, BF>), grid, dim3(threads), 0, stream, H, \
                        Lmax, P, q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out,    \
-                       qs_out, scores, ld, cmap)
+                       qs_out, scores, ld, cmap, hadamard ? 1 : 0, pow2 ? 1 : 0)
     if (bf16_in) {
         if (loop) DSA_DEC(4, DSA_DEC_LOOP_NW, true, true);
         else if (U == 4) DSA_DEC(4, 4, false, true);

@@ -252,6 +252,13 @@ FLAG_CASES = [
     ("had-pow2-tail", 2, 1, 64, 4133, [[4132], [2000]], True, 114, True, True),
     ("had-decode", 1, 1, 64, 2048, [[2047]], True, 115, True, False),
     ("had-pow2-tiles", 1, 20, 64, 300, [list(range(280, 300))], True, 116, True, True),
+    # one query row per batch row: the fused decode kernel with the options
+    # (looping grid for many key chunks; float32 activations; fewer heads)
+    ("had-pow2-loop", 6, 1, 64, 30000, [[29999], [12345], [0], [20000], [1792], [255]], True,
+     117, True, True),
+    ("had-f32-decode", 1, 1, 64, 700, [[699]], False, 118, True, False),
+    ("pow2-decode-h20", 2, 1, 20, 1000, [[999], [5]], True, 119, False, True),
+    ("had-decode-h20", 2, 1, 20, 1000, [[999], [5]], True, 120, True, False),
 ]
 
 
