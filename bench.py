@@ -107,8 +107,15 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, wor
     f_scale = copy_bytes / mean_of(per_kernel(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")[0]
     w_scale = copy_bytes / mean_of(per_kernel(copy_write_csv, "WRITE_SIZE"), "copyBuffer")[0]
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    rec = {"source_hash": source_hash(), "workload": workload,
-           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    out = os.path.join(ROOT, "profiles", "counters.json")
+    srch = source_hash()
+    try:
+        allrec = json.load(open(out))
+    except (OSError, ValueError):
+        allrec = {}
+    if allrec.get("source_hash") != srch or "workloads" not in allrec:
+        allrec = {"source_hash": srch, "workloads": {}}
+    rec = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     for call, subs in KERNELS_OF_CALL.items():
         ent = {"kernels": {}}
         tf = tw = 0.0
@@ -125,9 +132,9 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, wor
             raise SystemExit(f"no dispatch of a kernel of call {call!r}")
         ent.update(fetch_bytes=round(tf), write_bytes=round(tw), bytes_per_launch=round(tf + tw))
         rec[call] = ent
-    out = os.path.join(ROOT, "profiles", "counters.json")
+    allrec["workloads"][workload] = rec
     with open(out, "w") as fh:
-        json.dump(rec, fh, indent=1)
+        json.dump(allrec, fh, indent=1)
         fh.write("\n")
     print(json.dumps(rec))
 
@@ -173,18 +180,19 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_call, srchash):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources."""
+def load_traffic(kernel_call, srchash, workload):
+    """HBM traffic per launch of a call on a workload from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    ent = rec.get(kernel_call)
-    if not ent or rec.get("source_hash") != srchash:
+    if rec.get("source_hash") != srchash:
         return None
-    return ent.get("bytes_per_launch")
+    ent = rec.get("workloads", {}).get(workload, {}).get(kernel_call)
+    return ent.get("bytes_per_launch") if ent else None
 
 
 # ----------------------------------------------------------------- setup --
@@ -417,7 +425,8 @@ def other_workloads_leg(args):
             "call_avg_us": {k: round(v, 2) for k, v in m["avg_us"].items()},
             "dominant": {"kernel": dom, "achieved_gbs": round(m["achieved"], 1),
                          "frac": round(m["achieved"] / HBM_PEAK_GBS, 4),
-                         "bytes_per_launch": m["ab"][dom]},
+                         "bytes_per_launch": m["ab"][dom],
+                         "traffic": load_traffic(dom, source_hash(), name)},
         }
         del st, m
         torch.cuda.empty_cache()
@@ -847,7 +856,7 @@ def main():
     ab, dom, avg_us = m["ab"], m["dom"], m["avg_us"]
     achieved = m["achieved"]
     srch = source_hash()
-    traffic = load_traffic(dom, srch)
+    traffic = load_traffic(dom, srch, wl.name)
     ms_per_step = m["ms_per_step"]
     value = m["value"]
 
