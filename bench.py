@@ -76,7 +76,8 @@ def parse():
 KERNELS_OF_CALL = {
     "indexer": ["decode_score_kernel"],
     "topk": ["topk_select_kernel"],
-    "sparse_mla": ["sparse_mla_kernel", "merge_few_kernel", "combine_kernel"],
+    "sparse_mla": ["sparse_mla_kernel", "sparse_mla_pair_kernel", "merge_few_kernel",
+                   "combine_kernel"],
 }
 
 
@@ -95,17 +96,32 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, wor
                     d[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
         return d
 
+    def name_matches(k, sub):
+        # the kernel's own name (before its template arguments) is `sub`
+        base = k.split("(")[0].split("<")[0]
+        return base.endswith("::" + sub) or base == sub
+
     def mean_of(d, sub, required=True):
-        vals = [v for k, vs in d.items() if sub in k for v in vs]
-        if not vals:
+        """Bytes per launch of the kernels named `sub`: the mean over the
+        dispatches of each instantiation, summed over the instantiations (a
+        call may launch several, e.g. the two levels of a long-row top-k)."""
+        names = [k for k in d if name_matches(k, sub)]
+        if not names:
             if not required:
                 return None, 0
             raise SystemExit(f"no dispatch of a kernel named like {sub!r}")
-        return sum(vals) / len(vals), len(vals)
+        return (sum(sum(d[k]) / len(d[k]) for k in names),
+                min(len(d[k]) for k in names))
 
     copy_bytes = float(512 << 20)
-    f_scale = copy_bytes / mean_of(per_kernel(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")[0]
-    w_scale = copy_bytes / mean_of(per_kernel(copy_write_csv, "WRITE_SIZE"), "copyBuffer")[0]
+    def copy_mean(d):
+        vals = [v for k, vs in d.items() if "copyBuffer" in k for v in vs]
+        if not vals:
+            raise SystemExit("no dispatch of the device copy")
+        return sum(vals) / len(vals)
+
+    f_scale = copy_bytes / copy_mean(per_kernel(copy_fetch_csv, "FETCH_SIZE"))
+    w_scale = copy_bytes / copy_mean(per_kernel(copy_write_csv, "WRITE_SIZE"))
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     out = os.path.join(ROOT, "profiles", "counters.json")
     srch = source_hash()
