@@ -167,6 +167,23 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))));
 }
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l writes bytes 16 l .. 16 l + 15 after the
+// wave-uniform LDS address `dst`. Completion is counted by vmcnt.
+__device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* dst) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(
+        src, reinterpret_cast<lds_void*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
+                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))),
+        16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -58,22 +58,6 @@ struct GemmArgs {
     int64_t ldc, c_s1, c_s2;
 };
 
-// s_waitcnt with only the vector-memory counter limited to n (n < 64)
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l writes
-// bytes 16 l .. 16 l + 15 after the wave-uniform LDS address `dst`.
-__device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* dst) {
-    typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_global_load_lds(
-        src, reinterpret_cast<lds_void*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
-                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))),
-        16, 0, 0);
-}
-
 // MODE 0: kv up-projection, 1: query absorption (B stored K x N),
 // 2: output absorption; one instantiation each, so profiles tell them apart
 template <int MODE>

@@ -143,21 +143,6 @@ __global__ __launch_bounds__(kMaskThreads) void tile_lists_kernel(
 }
 
 // ---- 2. attention over the listed key tiles ---------------------------------
-// 16 bytes per lane from global memory straight into LDS: lane l writes
-// bytes 16 l .. 16 l + 15 after the wave-uniform LDS address `dst`.
-__device__ __forceinline__ void load_to_lds(const uint16_t* src, unsigned char* dst) {
-    typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_global_load_lds(
-        src, reinterpret_cast<lds_void*>(reinterpret_cast<__attribute__((address_space(3))) char*>(
-                 static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)))),
-        16, 0, 0);
-}
-
-// wait until every vector-memory load of this wave has completed
-__device__ __forceinline__ void wait_vmcnt0() {
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-}
-
 __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
     int S, int Hq, int Lmax, int nkt, int ntq, int nqt, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ rope, int64_t rope_rs,
@@ -272,7 +257,7 @@ __global__ __launch_bounds__(kMhaThreads, 2) void sparse_mha_kernel(
 
     if (ntile > 0) issue(0);
     for (int it = 0; it < ntile; ++it) {
-        wait_vmcnt0();                                 // this tile's loads (own)
+        wait_vmcnt<0>();                                 // this tile's loads (own)
         __builtin_amdgcn_s_barrier();                  // everyone's; previous tile consumed
         const uint2 mcur[2] = {mw[0], mw[1]};
         if (it + 1 < ntile) issue(it + 1);

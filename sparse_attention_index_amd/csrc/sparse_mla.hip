@@ -73,6 +73,182 @@ constexpr size_t kMlaLdsBytes = sizeof(uint16_t) * kTile * kKtStride + sizeof(in
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 #define DSA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
+// One 32-key tile for one wave's 16 heads: S^T = K Q^T, the online-softmax
+// update and O^T += V^T P^T. Kt: the tile, latent features of key row r at
+// Kt + r kPitch; the rotary part of the score operand (k-steps 16 and 17) at
+// Kt + rope16 / rope17 for row m = lane % 16, kRopeHalf further for row 16 + m
+// (bf16 units). sk: the tile's cache rows (negative: unselected, scored
+// -inf). kPipe / kPipeV: LDS operand reads kept in flight ahead of the score
+// / value MFMAs.
+template <int kPipe, int kPipeV, int kPitch, int kRopeHalf, int kChains = 2>
+__device__ __forceinline__ void mla_tile_math(const uint16_t* Kt, int rope16, int rope17,
+                                              const int* sk, int lane,
+                                              const bf16x8 (&qreg)[kDq / 32], v4f (&acc)[kT2],
+                                              float scale_log2, float& m_run, float& l_run,
+                                              float& lr_run) {
+    const int m = lane & 15, g = lane >> 4;
+    // transposing-read addresses (bf16 units within the tile): lane 4e+q of
+    // group g reads features 4q.. of key 4g+e (k-step keys 0..15) and of key
+    // 16+4g+e (keys 16..31)
+    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+    auto read_v = [&](int t2) -> bf16x8 {
+        // whole-register bit casts: element-wise 16-bit extraction here was
+        // mis-scheduled into a lane-mixing permute
+        const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
+        const uint2 hi =
+            __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kPitch + 16 * t2));
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    // score operand of k-step ks (compile-time) for keys m (h = 0) and 16 + m
+    const int lat_off = m * kPitch + 8 * g;
+    auto kop = [&](int ks, int hh) -> bf16x8 {
+        const int off = ks < kDl / 32 ? lat_off + 32 * ks + hh * 16 * kPitch
+                                      : (ks == kDl / 32 ? rope16 : rope17) + hh * kRopeHalf;
+        return *reinterpret_cast<const bf16x8*>(Kt + off);
+    };
+
+    // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
+    // Even and odd k-steps accumulate separately (four MFMA chains).
+    v4f s0, s1;
+    {
+        v4f c0[kChains], c1[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) {
+            c0[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            c1[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        bf16x8 a0[kPipe], a1[kPipe];
+#pragma unroll
+        for (int d = 0; d < kPipe; ++d) {
+            a0[d] = kop(d, 0);
+            a1[d] = kop(d, 1);
+        }
+        DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipe);
+#pragma unroll
+        for (int ks = 0; ks < kDq / 32; ++ks) {
+            const int sl = ks % kPipe;
+            c0[ks % kChains] = mfma_bf16_16x16x32(a0[sl], qreg[ks], c0[ks % kChains]);
+            c1[ks % kChains] = mfma_bf16_16x16x32(a1[sl], qreg[ks], c1[ks % kChains]);
+            DSA_SCHED_GROUP(kSchedMfma, 2);
+            if (ks + kPipe < kDq / 32) {
+                a0[sl] = kop(ks + kPipe, 0);
+                a1[sl] = kop(ks + kPipe, 1);
+                DSA_SCHED_GROUP(kSchedDsRead, 2);
+            }
+        }
+        s0 = c0[0];
+        s1 = c1[0];
+#pragma unroll
+        for (int c = 1; c < kChains; ++c) {
+            s0 += c0[c];
+            s1 += c1[c];
+        }
+    }
+    // the first V^T operands are read while the softmax runs
+    bf16x8 va[kPipeV];
+#pragma unroll
+    for (int d = 0; d < kPipeV; ++d) va[d] = read_v(d);
+    DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipeV);
+
+    float z[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        z[i] = sk[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
+        z[4 + i] = sk[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // Lazy rescaling: probabilities are taken relative to a reference
+    // maximum m_run that only moves when the running maximum exceeds it
+    // by more than 8 (so p <= 2^8, exact enough in float and bf16).
+    if (tmax > m_run + 8.0f) {
+        const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
+        l_run *= corr;
+        lr_run *= corr;
+        m_run = tmax;
+        if (__ballot(corr != 1.0f)) {
+#pragma unroll
+            for (int t2 = 0; t2 < kT2; ++t2) acc[t2] *= corr;
+        }
+    }
+    bf16x8 pv;
+    {
+        const bool live = m_run != -INFINITY;
+        float psum = 0.0f, prsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run) : 0.0f;
+            const __bf16 pb = static_cast<__bf16>(pe);
+            pv[i] = pb;
+            psum += pe;
+            prsum += static_cast<float>(pb);
+        }
+        l_run += psum;
+        lr_run += prsum;
+    }
+    // O^T += V^T P^T, V^T operands by transposing reads of the K tile
+#pragma unroll
+    for (int t2 = 0; t2 < kT2; ++t2) {
+        const int sl = t2 % kPipeV;
+        acc[t2] = mfma_bf16_16x16x32(va[sl], pv, acc[t2]);
+        DSA_SCHED_GROUP(kSchedMfma, 1);
+        if (t2 + kPipeV < kT2) {
+            va[sl] = read_v(t2 + kPipeV);
+            DSA_SCHED_GROUP(kSchedDsRead, 2);
+        }
+    }
+}
+
+// A wave's result for its 16 heads (lane holds O^T[16 t2 + 4 g + i][h],
+// i = 0..3): with one split the normalised bf16 output and the lse; else the
+// unnormalised bf16 partial block and its (m, lr, l) for the merge. kStream:
+// partials stored past L2.
+template <bool kStream>
+__device__ __forceinline__ void mla_store_result(const v4f (&acc)[kT2], float m_run, float l_tot,
+                                                 float lr_tot, int lane, int wg, int Hq, int row,
+                                                 int split, int nsplit, uint16_t* __restrict__ out,
+                                                 float* __restrict__ lse,
+                                                 uint16_t* __restrict__ ws_o,
+                                                 float* __restrict__ ws_ml) {
+    const int g = lane >> 4, h = wg * 16 + (lane & 15);
+    if (nsplit == 1) {
+        if (h >= Hq) return;
+        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+        uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const uint32_t lo = pack_bf16x2(acc[t2][0] * inv, acc[t2][1] * inv);
+            const uint32_t hi = pack_bf16x2(acc[t2][2] * inv, acc[t2][3] * inv);
+            *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
+        }
+        if (lse != nullptr && g == 0)
+            lse[static_cast<int64_t>(row) * Hq + h] =
+                l_tot > 0.0f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
+    } else {
+        // partial block of (row, split, 16-head group): [t2][lane] 4 x bf16
+        const int nwg = (Hq + 15) / 16;
+        const int64_t blk = (static_cast<int64_t>(row) * nsplit + split) * nwg + wg;
+        uint16_t* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) {
+            const uint32_t lo = pack_bf16x2(acc[t2][0], acc[t2][1]);
+            const uint32_t hi = pack_bf16x2(acc[t2][2], acc[t2][3]);
+            // fewest rows: streamed past L2 (measured 0.2 us shorter for one
+            // row, slower for 32 rows)
+            if constexpr (kStream)
+                __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(wo + t2 * 256));
+            else
+                *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
+        }
+        if (g == 0 && h < Hq)
+            *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
+                make_float4(m_run, lr_tot, l_tot, 0.0f);
+    }
+}
+
 // HPB = heads per block (4 HPB threads, one wave per 16 heads)
 template <bool PIPE, int HPB>
 __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
@@ -178,21 +354,6 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         }
     };
 
-    // transposing-read addresses (bf16 units within the tile): lane 4e+q of
-    // group g reads features 4q.. of key 4g+e (k-step keys 0..15) and of key
-    // 16+4g+e (keys 16..31)
-    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kKtStride + 4 * (lane & 3);
-    auto read_v = [&](int t2) -> bf16x8 {
-        // whole-register bit casts: element-wise 16-bit extraction here was
-        // mis-scheduled into a lane-mixing permute
-        const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
-        const uint2 hi =
-            __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kKtStride + 16 * t2));
-        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    };
-    const uint16_t* ka_row = Kt + m * kKtStride + 8 * g;
-    const uint16_t* kb_row = Kt + (16 + m) * kKtStride + 8 * g;
-
     // LDS operand reads in flight ahead of their MFMAs
     constexpr int kPipe = PIPE ? 4 : 2;       // S: K-operand pairs
     constexpr int kPipeV = PIPE ? 6 : 3;      // O: V^T operands
@@ -206,91 +367,9 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         __syncthreads();
         if (PIPE && t + 1 < ntiles) fetch_tile(t + 1, G);
         if (!active) return;
-
-        // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
-        // Even and odd k-steps accumulate separately (four MFMA chains).
-        v4f s0, s1;
-        {
-            v4f c0[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-            v4f c1[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-            bf16x8 a0[kPipe], a1[kPipe];
-#pragma unroll
-            for (int d = 0; d < kPipe; ++d) {
-                a0[d] = *reinterpret_cast<const bf16x8*>(ka_row + d * 32);
-                a1[d] = *reinterpret_cast<const bf16x8*>(kb_row + d * 32);
-            }
-            DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipe);
-#pragma unroll
-            for (int ks = 0; ks < kDq / 32; ++ks) {
-                const int sl = ks % kPipe;
-                c0[ks & 1] = mfma_bf16_16x16x32(a0[sl], qreg[ks], c0[ks & 1]);
-                c1[ks & 1] = mfma_bf16_16x16x32(a1[sl], qreg[ks], c1[ks & 1]);
-                DSA_SCHED_GROUP(kSchedMfma, 2);
-                if (ks + kPipe < kDq / 32) {
-                    a0[sl] = *reinterpret_cast<const bf16x8*>(ka_row + (ks + kPipe) * 32);
-                    a1[sl] = *reinterpret_cast<const bf16x8*>(kb_row + (ks + kPipe) * 32);
-                    DSA_SCHED_GROUP(kSchedDsRead, 2);
-                }
-            }
-            s0 = c0[0] + c0[1];
-            s1 = c1[0] + c1[1];
-        }
-        // the first V^T operands are read while the softmax runs
-        bf16x8 va[kPipeV];
-#pragma unroll
-        for (int d = 0; d < kPipeV; ++d) va[d] = read_v(d);
-        DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipeV);
-
-        float z[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = sidx[t * kTile + 4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
-            z[4 + i] = sidx[t * kTile + 16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        // Lazy rescaling: probabilities are taken relative to a reference
-        // maximum m_run that only moves when the running maximum exceeds it
-        // by more than 8 (so p <= 2^8, exact enough in float and bf16).
-        if (tmax > m_run + 8.0f) {
-            const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
-            l_run *= corr;
-            lr_run *= corr;
-            m_run = tmax;
-            if (__ballot(corr != 1.0f)) {
-#pragma unroll
-                for (int t2 = 0; t2 < kT2; ++t2) acc[t2] *= corr;
-            }
-        }
-        bf16x8 pv;
-        {
-            const bool live = m_run != -INFINITY;
-            float psum = 0.0f, prsum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run) : 0.0f;
-                const __bf16 pb = static_cast<__bf16>(pe);
-                pv[i] = pb;
-                psum += pe;
-                prsum += static_cast<float>(pb);
-            }
-            l_run += psum;
-            lr_run += prsum;
-        }
-        // O^T += V^T P^T, V^T operands by transposing reads of the K tile
-#pragma unroll
-        for (int t2 = 0; t2 < kT2; ++t2) {
-            const int sl = t2 % kPipeV;
-            acc[t2] = mfma_bf16_16x16x32(va[sl], pv, acc[t2]);
-            DSA_SCHED_GROUP(kSchedMfma, 1);
-            if (t2 + kPipeV < kT2) {
-                va[sl] = read_v(t2 + kPipeV);
-                DSA_SCHED_GROUP(kSchedDsRead, 2);
-            }
-        }
+        mla_tile_math<kPipe, kPipeV, kKtStride, 16 * kKtStride>(
+            Kt, m * kKtStride + 8 * g + kDl, m * kKtStride + 8 * g + kDl + 32, sidx + t * kTile,
+            lane, qreg, acc, scale_log2, m_run, l_run, lr_run);
     };
     for (int t = 0; t < ntiles; ++t) tile_step(t, GA);
 
@@ -299,40 +378,218 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
     float lr_tot = lr_run + __shfl_xor(lr_run, 16);
     lr_tot += __shfl_xor(lr_tot, 32);
     if (!active) return;
-    // lane holds O^T[16 t2 + 4 g + i][h], i = 0..3
-    if (nsplit == 1) {
-        if (h >= Hq) return;
-        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
-        uint16_t* oh = out + (static_cast<int64_t>(row) * Hq + h) * kDl + 4 * g;
+    mla_store_result<PIPE && HPB == kHeadsPerBlockFew>(acc, m_run, l_tot, lr_tot, lane, wg, Hq, row,
+                                                       split, nsplit, out, lse, ws_o, ws_ml);
+}
+
+// The build for grids of more than one block per CU with more than 64 heads
+// (batched decode, prefill): 8 waves serve 128 heads of one (row, split), so
+// every selected row is gathered once for all its heads, and the gather runs
+// two tiles ahead of the math through a ring of three LDS tiles filled
+// straight from global memory (global_load_lds, 16 bytes per lane, no
+// registers held). A ring tile keeps the latent and rotary parts apart:
+//   latent: 32 rows of 1024 B at a 1056-B pitch (32 B past a multiple of
+//           256 B: the score operand and transposing value reads are free of
+//           bank conflicts, measured), one load instruction per row, whose
+//           64 lanes read the row's 64 chunks from one scalar base address;
+//   rotary: wave w's 1 KiB block holds rows 4w..4w+3, 128 B each, 16-byte
+//           chunk c of row r stored at c ^ (r & 6) (conflict free as well),
+//           filled by the first 32 lanes of one instruction (the other 32
+//           repeat them into the unused half).
+// Wave w loads rows 4w..4w+3: four latent instructions and one rotary, the
+// same five per wave and tile. Unselected rows read a block of zeros.
+constexpr int kRingWaves = 8;
+constexpr int kRingHeads = 16 * kRingWaves;
+constexpr int kRingStages = 3;
+constexpr int kRingLoads = 5;                                  // per wave and tile
+constexpr int kLatPitch = kDl + 16;                            // bf16 (1056 B)
+constexpr int kRingLatBytes = kTile * kLatPitch * 2;           // 33,792
+constexpr int kRingStageBytes = kRingLatBytes + kRingWaves * 1024;
+constexpr int kRopeHalfRows = 16 / 4 * 512;                    // bf16 from row m to 16 + m
+static_assert(kRingWaves * 4 == kTile, "four rows per wave");
+constexpr size_t kRingLdsBytes =
+    static_cast<size_t>(kRingStages) * kRingStageBytes + sizeof(int) * (kMaxSlots + kRingWaves);
+
+__device__ uint4 mla_zero_kb[64];    // 1 KiB of zeros (zero-initialised, never written)
+
+// The ring's loads, waits and barrier are inline asm that the compiler sees
+// only as opaque memory operations. Written with the global_load_lds builtin
+// the compiler cannot tell the ring stages apart, and makes the first
+// transposing LDS read of every tile wait for all loads in flight, the next
+// tiles' included (vmcnt(0)), which leaves nothing in flight during the math.
+// Here the waits are exactly the ring's: before a tile is read, every load
+// but those of the next tile has landed (vector-memory loads complete in
+// issue order), then the barrier makes all waves' loads visible.
+// 16 bytes per lane to LDS address m0 + 16 lane: from base + voff (scalar
+// base, per-lane 32-bit offset) or from a per-lane 64-bit address.
+__device__ __forceinline__ void ring_load_s(uint64_t base, uint32_t voff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_dst)
+                 : "memory");
+}
+__device__ __forceinline__ void ring_load_v(uint64_t addr, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(addr), "s"(lds_dst)
+                 : "memory");
+}
+template <int n>
+__device__ __forceinline__ void ring_wait_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(n) : "memory");
+}
+
+__global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
+    int S, int Hq, int Lmax, int K, int slots_per_split, int nsplit, int nitems, int hgroups,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent, int64_t lat_rs,
+    int64_t lat_bs, const uint16_t* __restrict__ rope, int64_t rope_rs, int64_t rope_bs,
+    const int32_t* __restrict__ idx, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml, CacheMap cmap) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    int* sidx = reinterpret_cast<int*>(smem + kRingStages * kRingStageBytes);
+
+    // launch index -> (work item = row * nsplit + split, head group), as in
+    // the tile kernel
+    const int L = blockIdx.x;
+    const int item = (L / (8 * hgroups)) * 8 + (L & 7);
+    const int hg = (L / 8) % hgroups;
+    if (item >= nitems) return;
+    const int row = item / nsplit, split = item - row * nsplit;
+    const int64_t b = row / S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    constexpr int kThr = 64 * kRingWaves;
+    const int wg = hg * kRingWaves + wave;                         // 16-head group
+    const int h = wg * 16 + m;
+    const bool active = wg * 16 < Hq;
+
+    const int j_begin = split * slots_per_split;
+    const int j_end = min(K, j_begin + slots_per_split);
+    const int count = j_end - j_begin;
+    const bool paged = cmap.table != nullptr;
+    // the split's cache rows, compacted: the selected, present rows first (in
+    // slot order), so tiles of unselected slots (a causal row shorter than
+    // the top-k count, say) are never loaded or computed; the tail of the
+    // last tile is -1
+    int nvalid = 0;
+    {
+        int* wcnt = sidx + kMaxSlots;                              // per-wave counts
+        const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
+        for (int base = 0; base < count; base += kThr) {
+            const int i = base + tid;
+            const int p = i < count ? irow[i] : -1;
+            int v = -1;
+            if (p >= 0 && p < Lmax) v = paged ? static_cast<int>(cmap.row(b, p)) : p;
+            const uint64_t bal = __ballot(v >= 0);
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+            if (lane == 0) wcnt[wave] = __popcll(bal);
+            __syncthreads();
+            int off = nvalid, tot = 0;
 #pragma unroll
-        for (int t2 = 0; t2 < kT2; ++t2) {
-            const uint32_t lo = pack_bf16x2(acc[t2][0] * inv, acc[t2][1] * inv);
-            const uint32_t hi = pack_bf16x2(acc[t2][2] * inv, acc[t2][3] * inv);
-            *reinterpret_cast<uint2*>(oh + 16 * t2) = make_uint2(lo, hi);
+            for (int w = 0; w < kRingWaves; ++w) {
+                const int c = wcnt[w];
+                off += w < wave ? c : 0;
+                tot += c;
+            }
+            if (v >= 0) sidx[off + below] = v;
+            nvalid += tot;
+            __syncthreads();                                       // wcnt reused
         }
-        if (lse != nullptr && g == 0)
-            lse[static_cast<int64_t>(row) * Hq + h] =
-                l_tot > 0.0f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
-    } else {
-        // partial block of (row, split, 16-head group): [t2][lane] 4 x bf16
-        const int nwg = (Hq + 15) / 16;
-        const int64_t blk = (static_cast<int64_t>(row) * nsplit + split) * nwg + wg;
-        uint16_t* wo = ws_o + blk * (kT2 * 64 * 4) + lane * 4;
-#pragma unroll
-        for (int t2 = 0; t2 < kT2; ++t2) {
-            const uint32_t lo = pack_bf16x2(acc[t2][0], acc[t2][1]);
-            const uint32_t hi = pack_bf16x2(acc[t2][2], acc[t2][3]);
-            // fewest rows: streamed past L2 (measured 0.2 us shorter for one
-            // row, slower for 32 rows)
-            if constexpr (PIPE && HPB == kHeadsPerBlockFew)
-                __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(wo + t2 * 256));
-            else
-                *reinterpret_cast<uint2*>(wo + t2 * 256) = make_uint2(lo, hi);
-        }
-        if (g == 0 && h < Hq)
-            *reinterpret_cast<float4*>(ws_ml + ((static_cast<int64_t>(row) * nsplit + split) * Hq + h) * 4) =
-                make_float4(m_run, lr_tot, l_tot, 0.0f);
     }
+    const int ntiles = (nvalid + kTile - 1) / kTile;
+    for (int i = nvalid + tid; i < ntiles * kTile; i += kThr) sidx[i] = -1;
+    bf16x8 qreg[kDq / 32];
+    {
+        const uint16_t* qh =
+            q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kDq / 32; ++ks) {
+            uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
+            if (h >= Hq) v = make_uint4(0u, 0u, 0u, 0u);
+            qreg[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    // q in registers before the ring's loads are issued: the compiler's own
+    // waits for the q loads would otherwise count the ring's loads too
+#pragma unroll
+    for (int ks = 0; ks < kDq / 32; ++ks) asm volatile("" : "+v"(qreg[ks]));
+    v4f acc[kT2];
+#pragma unroll
+    for (int t2 = 0; t2 < kT2; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
+    const uint64_t lat_b =
+        reinterpret_cast<uint64_t>(latent + (paged ? 0 : b * lat_bs));
+    const uint64_t rope_b = reinterpret_cast<uint64_t>(rope + (paged ? 0 : b * rope_bs));
+    const uint64_t zero = reinterpret_cast<uint64_t>(&mla_zero_kb[0]);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    __syncthreads();                               // sidx ready
+
+    auto issue = [&](int t) {
+        const uint32_t st = lds0 + (t % kRingStages) * kRingStageBytes;
+        // this wave's four rows: cache rows from one broadcast LDS read
+        const int4 p4 = *reinterpret_cast<const int4*>(sidx + t * kTile + 4 * wave_u);
+        const int pr[4] = {p4.x, p4.y, p4.z, p4.w};
+        // latent: row 4w + j, lane l reads bytes 16 l .. of the row
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = __builtin_amdgcn_readfirstlane(pr[j]);
+            const uint64_t base =
+                p >= 0 ? lat_b + static_cast<uint64_t>(static_cast<uint32_t>(p)) *
+                                     static_cast<uint64_t>(lat_rs * 2)
+                       : zero;
+            ring_load_s(base, 16u * static_cast<uint32_t>(ln),
+                        st + (4 * wave_u + j) * (kLatPitch * 2));
+        }
+        // rotary: lane l (and l + 32) fills chunk c = l % 8 of row 4w + j,
+        // j = (l / 8) % 4, from source chunk c ^ (row & 6)
+        {
+            const int j = (ln >> 3) & 3, c = ln & 7;
+            const int p = (j & 2) ? ((j & 1) ? pr[3] : pr[2]) : ((j & 1) ? pr[1] : pr[0]);
+            const int sc = c ^ ((4 * wave_u + j) & 6);
+            const uint64_t a =
+                p >= 0 ? rope_b + static_cast<uint64_t>(static_cast<uint32_t>(p)) *
+                                      static_cast<uint64_t>(rope_rs * 2) +
+                             16u * static_cast<uint32_t>(sc)
+                       : zero + 16u * static_cast<uint32_t>(c);
+            ring_load_v(a, st + kRingLatBytes + 1024 * wave_u);
+        }
+    };
+
+    // rotary operand offsets (bf16 within a stage) of k-steps 16 and 17 for
+    // row m: block m / 4, row m % 4, chunk (4 (ks - 16) + g) ^ (m & 6)
+    const int rbase = kRingLatBytes / 2 + (m >> 2) * 512 + (m & 3) * 64;
+    const int rope16 = rbase + 8 * (g ^ (m & 6));
+    const int rope17 = rbase + 8 * ((4 + g) ^ (m & 6));
+#ifndef DSA_RING_PIPE
+#define DSA_RING_PIPE 2, kPipeV = 4, kRingChains = 1
+#endif
+    constexpr int kPipe = DSA_RING_PIPE;
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) issue(1);
+    for (int t = 0; t < ntiles; ++t) {
+        // tile t has landed once only tile t + 1's loads are in flight; the
+        // barrier: every wave's loads, and tile t - 1 consumed
+        if (t + 1 < ntiles) ring_wait_barrier<kRingLoads>();
+        else ring_wait_barrier<0>();
+        if (t + 2 < ntiles) issue(t + 2);
+        if (active)
+            mla_tile_math<kPipe, kPipeV, kLatPitch, kRopeHalfRows, kRingChains>(
+                reinterpret_cast<const uint16_t*>(smem + (t % kRingStages) * kRingStageBytes),
+                rope16, rope17, sidx + t * kTile, lane, qreg, acc, scale_log2, m_run, l_run,
+                lr_run);
+    }
+
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    float lr_tot = lr_run + __shfl_xor(lr_run, 16);
+    lr_tot += __shfl_xor(lr_tot, 32);
+    if (!active) return;
+    mla_store_result<false>(acc, m_run, l_tot, lr_tot, lane, wg, Hq, row, split, nsplit, out, lse,
+                            ws_o, ws_ml);
 }
 
 // The build for the fewest blocks when every split holds at most 64
@@ -891,6 +1148,19 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
         e = launch_mla_kernel<true, kHeadsPerBlock>(
             dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs,
             lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out, lse, ws_o, ws_ml, cmap);
+    } else if (Hq > kHeadsPerBlock) {
+        // more than one block per CU and more than 64 heads: 128-head
+        // blocks, each row gathered once, the gather two tiles ahead
+        const int hg_ring = (Hq + kRingHeads - 1) / kRingHeads;
+        const int nb_ring = ((nitems + 7) / 8) * 8 * hg_ring;
+        e = set_dynamic_lds_limit(reinterpret_cast<const void*>(&sparse_mla_ring_kernel),
+                                  static_cast<int>(kRingLdsBytes));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sparse_mla_ring_kernel, dim3(nb_ring), dim3(64 * kRingWaves),
+                           kRingLdsBytes, stream, S, Hq, Lmax, K, sps, ns, nitems, hg_ring, q,
+                           latent, lat_rs, lat_bs, rope, rope_rs, rope_bs, idx, scale_log2, out,
+                           lse, ws_o, ws_ml, cmap);
+        e = hipGetLastError();
     } else {
         e = launch_mla_kernel<false, kHeadsPerBlock>(
             dim3(nblocks), stream, S, Hq, Lmax, K, sps, ns, nitems, hgroups, q, latent, lat_rs,
