@@ -80,25 +80,81 @@ constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 // (bf16 units). sk: the tile's cache rows (negative: unselected, scored
 // -inf). kPipe / kPipeV: LDS operand reads kept in flight ahead of the score
 // / value MFMAs.
-template <int kPipe, int kPipeV, int kPitch, int kRopeHalf, int kChains = 2>
-__device__ __forceinline__ void mla_tile_math(const uint16_t* Kt, int rope16, int rope17,
-                                              const int* sk, int lane,
-                                              const bf16x8 (&qreg)[kDq / 32], v4f (&acc)[kT2],
-                                              float scale_log2, float& m_run, float& l_run,
-                                              float& lr_run) {
+struct NoWork {
+    __device__ void operator()() const {}
+};
+
+// max over the four lanes l ^ 16 k (k = 0..3): lane-swap VALU moves, no LDS
+__device__ __forceinline__ float max_over_row_groups(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(v);
+    const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// sum over the four lanes l ^ 16 k (k = 0..3)
+__device__ __forceinline__ float sum_over_row_groups(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t w = __float_as_uint(v);
+    const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Q^T operand of one 16-head group: lane (head h, chunk g) holds
+// q[row][h][32 ks + 8 g .. +7]; heads past Hq read as zeros.
+__device__ __forceinline__ void mla_load_q(const uint16_t* __restrict__ q, int row, int Hq, int h,
+                                           int g, bf16x8 (&qreg)[kDq / 32]) {
+    const uint16_t* qh = q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDq / 32; ++ks) {
+        uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
+        if (h >= Hq) v = make_uint4(0u, 0u, 0u, 0u);
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// V^T operand of output tile t2 (16 latent features) for the 32 keys of the
+// tile at Kt (rows kPitch apart), by transposing reads: lane 4e+q of group g
+// reads features 4q.. of key 4g+e (k-step keys 0..15) and of key 16+4g+e
+// (keys 16..31)
+template <int kPitch>
+__device__ __forceinline__ bf16x8 mla_read_v(const uint16_t* Kt, int lane, int t2) {
+    const int tr_off = (4 * (lane >> 4) + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
+    // whole-register bit casts: element-wise 16-bit extraction here was
+    // mis-scheduled into a lane-mixing permute
+    const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
+    const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kPitch + 16 * t2));
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// The scores and online-softmax half of one 32-key tile for NG groups of 16
+// heads held by one wave: S^T = K Q^T (each score operand read from LDS
+// serves all NG groups), the running maximum, sums and (when the maximum
+// moves) the accumulator rescale; P^T of group j, as the bf16 MFMA operand,
+// goes to pv[j]. Kt: the tile, latent features of key row r at
+// Kt + r kPitch; the rotary part of the score operand (k-steps 16 and 17) at
+// Kt + rope16 / rope17 for row m = lane % 16, kRopeHalf further for row
+// 16 + m (bf16 units). sk: the tile's cache rows (negative: unselected,
+// scored -inf); with kCounted the rows are compacted and the first nk keys
+// of the tile are the selected ones (no LDS reads for the mask). kPipe:
+// score operand reads kept in flight ahead of the MFMAs; kChains: separate
+// accumulation chains per score output; the first kEarlyV value operands of
+// the tile are read into va while the softmax runs. mid(): work run once the
+// score MFMAs are issued, before the softmax waits for them.
+template <int NG, int kPipe, int kPipeV, int kEarlyV, int kPitch, int kRopeHalf, int kChains,
+          bool kCounted, typename Mid = NoWork>
+__device__ __forceinline__ void mla_scores(const uint16_t* Kt, int rope16, int rope17,
+                                           const int* sk, int nk, int lane,
+                                           const bf16x8 (&qreg)[NG][kDq / 32],
+                                           v4f (&acc)[NG][kT2], float scale_log2,
+                                           float (&m_run)[NG], float (&l_run)[NG],
+                                           float (&lr_run)[NG], bf16x8 (&va)[kPipeV],
+                                           bf16x8 (&pv)[NG], Mid mid = Mid()) {
     const int m = lane & 15, g = lane >> 4;
-    // transposing-read addresses (bf16 units within the tile): lane 4e+q of
-    // group g reads features 4q.. of key 4g+e (k-step keys 0..15) and of key
-    // 16+4g+e (keys 16..31)
-    const int tr_off = (4 * g + ((lane >> 2) & 3)) * kPitch + 4 * (lane & 3);
-    auto read_v = [&](int t2) -> bf16x8 {
-        // whole-register bit casts: element-wise 16-bit extraction here was
-        // mis-scheduled into a lane-mixing permute
-        const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * t2));
-        const uint2 hi =
-            __builtin_bit_cast(uint2, lds_read_tr16(Kt + tr_off + 16 * kPitch + 16 * t2));
-        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    };
     // score operand of k-step ks (compile-time) for keys m (h = 0) and 16 + m
     const int lat_off = m * kPitch + 8 * g;
     auto kop = [&](int ks, int hh) -> bf16x8 {
@@ -106,17 +162,18 @@ __device__ __forceinline__ void mla_tile_math(const uint16_t* Kt, int rope16, in
                                       : (ks == kDl / 32 ? rope16 : rope17) + hh * kRopeHalf;
         return *reinterpret_cast<const bf16x8*>(Kt + off);
     };
-
-    // S^T for keys 0..15 (s0) and 16..31 (s1); lane holds keys 4g+i.
-    // Even and odd k-steps accumulate separately (four MFMA chains).
-    v4f s0, s1;
+    // S^T for keys 0..15 (s0) and 16..31 (s1) of each group; lane holds keys
+    // 4g+i. Consecutive k-steps rotate over kChains accumulators.
+    v4f s0[NG], s1[NG];
     {
-        v4f c0[kChains], c1[kChains];
+        v4f c0[NG][kChains], c1[NG][kChains];
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) {
-            c0[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-            c1[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        for (int j = 0; j < NG; ++j)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                c0[j][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                c1[j][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
         bf16x8 a0[kPipe], a1[kPipe];
 #pragma unroll
         for (int d = 0; d < kPipe; ++d) {
@@ -126,80 +183,115 @@ __device__ __forceinline__ void mla_tile_math(const uint16_t* Kt, int rope16, in
         DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipe);
 #pragma unroll
         for (int ks = 0; ks < kDq / 32; ++ks) {
-            const int sl = ks % kPipe;
-            c0[ks % kChains] = mfma_bf16_16x16x32(a0[sl], qreg[ks], c0[ks % kChains]);
-            c1[ks % kChains] = mfma_bf16_16x16x32(a1[sl], qreg[ks], c1[ks % kChains]);
-            DSA_SCHED_GROUP(kSchedMfma, 2);
+            const int sl = ks % kPipe, ch = ks % kChains;
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                c0[j][ch] = mfma_bf16_16x16x32(a0[sl], qreg[j][ks], c0[j][ch]);
+                c1[j][ch] = mfma_bf16_16x16x32(a1[sl], qreg[j][ks], c1[j][ch]);
+            }
+            DSA_SCHED_GROUP(kSchedMfma, 2 * NG);
             if (ks + kPipe < kDq / 32) {
                 a0[sl] = kop(ks + kPipe, 0);
                 a1[sl] = kop(ks + kPipe, 1);
                 DSA_SCHED_GROUP(kSchedDsRead, 2);
             }
         }
-        s0 = c0[0];
-        s1 = c1[0];
+        mid();
 #pragma unroll
-        for (int c = 1; c < kChains; ++c) {
-            s0 += c0[c];
-            s1 += c1[c];
+        for (int j = 0; j < NG; ++j) {
+            s0[j] = c0[j][0];
+            s1[j] = c1[j][0];
+#pragma unroll
+            for (int c = 1; c < kChains; ++c) {
+                s0[j] += c0[j][c];
+                s1[j] += c1[j][c];
+            }
         }
     }
     // the first V^T operands are read while the softmax runs
-    bf16x8 va[kPipeV];
 #pragma unroll
-    for (int d = 0; d < kPipeV; ++d) va[d] = read_v(d);
-    DSA_SCHED_GROUP(kSchedDsRead, 2 * kPipeV);
+    for (int d = 0; d < kEarlyV; ++d) va[d] = mla_read_v<kPitch>(Kt, lane, d);
+    if constexpr (kEarlyV > 0) DSA_SCHED_GROUP(kSchedDsRead, 2 * kEarlyV);
 
-    float z[8];
-    float tmax = -INFINITY;
+    bool valid[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        z[i] = sk[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
-        z[4 + i] = sk[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
+        valid[i] = kCounted ? 4 * g + i < nk : sk[4 * g + i] >= 0;
+        valid[4 + i] = kCounted ? 16 + 4 * g + i < nk : sk[16 + 4 * g + i] >= 0;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // Lazy rescaling: probabilities are taken relative to a reference
-    // maximum m_run that only moves when the running maximum exceeds it
-    // by more than 8 (so p <= 2^8, exact enough in float and bf16).
-    if (tmax > m_run + 8.0f) {
-        const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - tmax);
-        l_run *= corr;
-        lr_run *= corr;
-        m_run = tmax;
-        if (__ballot(corr != 1.0f)) {
+    for (int j = 0; j < NG; ++j) {
+        float z[8];
+        float tmax = -INFINITY;
 #pragma unroll
-            for (int t2 = 0; t2 < kT2; ++t2) acc[t2] *= corr;
+        for (int i = 0; i < 4; ++i) {
+            z[i] = valid[i] ? s0[j][i] * scale_log2 : -INFINITY;
+            z[4 + i] = valid[4 + i] ? s1[j][i] * scale_log2 : -INFINITY;
         }
-    }
-    bf16x8 pv;
-    {
-        const bool live = m_run != -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+        tmax = max_over_row_groups(tmax);
+        // Lazy rescaling: probabilities are taken relative to a reference
+        // maximum m_run that only moves when the running maximum exceeds it
+        // by more than 8 (so p <= 2^8, exact enough in float and bf16).
+        if (tmax > m_run[j] + 8.0f) {
+            const float corr = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - tmax);
+            l_run[j] *= corr;
+            lr_run[j] *= corr;
+            m_run[j] = tmax;
+            if (__ballot(corr != 1.0f)) {
+#pragma unroll
+                for (int t2 = 0; t2 < kT2; ++t2) acc[j][t2] *= corr;
+            }
+        }
+        const bool live = m_run[j] != -INFINITY;
         float psum = 0.0f, prsum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run) : 0.0f;
+            const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run[j]) : 0.0f;
             const __bf16 pb = static_cast<__bf16>(pe);
-            pv[i] = pb;
+            pv[j][i] = pb;
             psum += pe;
             prsum += static_cast<float>(pb);
         }
-        l_run += psum;
-        lr_run += prsum;
+        l_run[j] += psum;
+        lr_run[j] += prsum;
     }
-    // O^T += V^T P^T, V^T operands by transposing reads of the K tile
+}
+
+// The value half: O^T += V^T P^T over the tile at Kt for the NG groups (each
+// V^T operand read from LDS serves all of them), the first kPipeV V^T
+// operands already in va, the rest read kPipeV steps ahead.
+template <int NG, int kPipeV, int kPitch>
+__device__ __forceinline__ void mla_values(const uint16_t* Kt, int lane, const bf16x8 (&pv)[NG],
+                                           bf16x8 (&va)[kPipeV], v4f (&acc)[NG][kT2]) {
 #pragma unroll
     for (int t2 = 0; t2 < kT2; ++t2) {
         const int sl = t2 % kPipeV;
-        acc[t2] = mfma_bf16_16x16x32(va[sl], pv, acc[t2]);
-        DSA_SCHED_GROUP(kSchedMfma, 1);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc[j][t2] = mfma_bf16_16x16x32(va[sl], pv[j], acc[j][t2]);
+        DSA_SCHED_GROUP(kSchedMfma, NG);
         if (t2 + kPipeV < kT2) {
-            va[sl] = read_v(t2 + kPipeV);
+            va[sl] = mla_read_v<kPitch>(Kt, lane, t2 + kPipeV);
             DSA_SCHED_GROUP(kSchedDsRead, 2);
         }
     }
+}
+
+// One whole tile: the scores half, then the value half.
+template <int NG, int kPipe, int kPipeV, int kPitch, int kRopeHalf, int kChains,
+          bool kCounted, typename Mid = NoWork>
+__device__ __forceinline__ void mla_tile_math(const uint16_t* Kt, int rope16, int rope17,
+                                              const int* sk, int nk, int lane,
+                                              const bf16x8 (&qreg)[NG][kDq / 32],
+                                              v4f (&acc)[NG][kT2], float scale_log2,
+                                              float (&m_run)[NG], float (&l_run)[NG],
+                                              float (&lr_run)[NG], Mid mid = Mid()) {
+    bf16x8 va[kPipeV], pv[NG];
+    mla_scores<NG, kPipe, kPipeV, kPipeV, kPitch, kRopeHalf, kChains, kCounted>(
+        Kt, rope16, rope17, sk, nk, lane, qreg, acc, scale_log2, m_run, l_run, lr_run, va, pv,
+        mid);
+    mla_values<NG, kPipeV, kPitch>(Kt, lane, pv, va, acc);
 }
 
 // A wave's result for its 16 heads (lane holds O^T[16 t2 + 4 g + i][h],
@@ -296,24 +388,14 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         }
     }
 
-    // Q^T operand: lane (head h, chunk g) holds q[h][32 ks + 8 g .. +7].
-    bf16x8 qreg[kDq / 32];
-    {
-        const uint16_t* qh =
-            q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+    bf16x8 qreg[1][kDq / 32];
+    mla_load_q(q, row, Hq, h, g, qreg[0]);
+    v4f acc[1][kT2];
 #pragma unroll
-        for (int ks = 0; ks < kDq / 32; ++ks) {
-            uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
-            if (h >= Hq) v = make_uint4(0u, 0u, 0u, 0u);
-            qreg[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    v4f acc[kT2];
-#pragma unroll
-    for (int t2 = 0; t2 < kT2; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t2 = 0; t2 < kT2; ++t2) acc[0][t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     // l_run sums the float32 probabilities (for lse); lr_run sums the bf16
     // values that actually weight the latent rows (for the normalisation).
-    float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
+    float m_run[1] = {-INFINITY}, l_run[1] = {0.0f}, lr_run[1] = {0.0f};
 
     const uint16_t* lat_b = latent + (paged ? 0 : b * lat_bs);
     const uint16_t* rope_b = rope + (paged ? 0 : b * rope_bs);
@@ -367,19 +449,18 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
         __syncthreads();
         if (PIPE && t + 1 < ntiles) fetch_tile(t + 1, G);
         if (!active) return;
-        mla_tile_math<kPipe, kPipeV, kKtStride, 16 * kKtStride>(
+        mla_tile_math<1, kPipe, kPipeV, kKtStride, 16 * kKtStride, 2, false>(
             Kt, m * kKtStride + 8 * g + kDl, m * kKtStride + 8 * g + kDl + 32, sidx + t * kTile,
-            lane, qreg, acc, scale_log2, m_run, l_run, lr_run);
+            0, lane, qreg, acc, scale_log2, m_run, l_run, lr_run);
     };
     for (int t = 0; t < ntiles; ++t) tile_step(t, GA);
 
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    float lr_tot = lr_run + __shfl_xor(lr_run, 16);
-    lr_tot += __shfl_xor(lr_tot, 32);
+    const float l_tot = sum_over_row_groups(l_run[0]);
+    const float lr_tot = sum_over_row_groups(lr_run[0]);
     if (!active) return;
-    mla_store_result<PIPE && HPB == kHeadsPerBlockFew>(acc, m_run, l_tot, lr_tot, lane, wg, Hq, row,
-                                                       split, nsplit, out, lse, ws_o, ws_ml);
+    mla_store_result<PIPE && HPB == kHeadsPerBlockFew>(acc[0], m_run[0], l_tot, lr_tot, lane, wg,
+                                                       Hq, row, split, nsplit, out, lse, ws_o,
+                                                       ws_ml);
 }
 
 // The build for grids of more than one block per CU with more than 64 heads
@@ -397,16 +478,20 @@ __global__ __launch_bounds__(4 * HPB, PIPE ? 1 : 2) void sparse_mla_kernel(
 //           filled by the first 32 lanes of one instruction (the other 32
 //           repeat them into the unused half).
 // Wave w loads rows 4w..4w+3: four latent instructions and one rotary, the
-// same five per wave and tile. Unselected rows read a block of zeros.
+// same five per wave and tile. Unselected rows read a block of zeros. The
+// split's selected rows are compacted first, so tiles of unselected slots
+// (a causal row shorter than the top-k count, say) cost nothing.
 constexpr int kRingWaves = 8;
-constexpr int kRingHeads = 16 * kRingWaves;
+constexpr int kRingGroups = 1;                                 // 16-head groups per wave
+constexpr int kRingHeads = 16 * kRingGroups * kRingWaves;
 constexpr int kRingStages = 3;
-constexpr int kRingLoads = 5;                                  // per wave and tile
+constexpr int kRingRows = kTile / kRingWaves;                  // rows loaded per wave
+constexpr int kRingLoads = kRingRows + 1;                      // per wave and tile
 constexpr int kLatPitch = kDl + 16;                            // bf16 (1056 B)
 constexpr int kRingLatBytes = kTile * kLatPitch * 2;           // 33,792
 constexpr int kRingStageBytes = kRingLatBytes + kRingWaves * 1024;
-constexpr int kRopeHalfRows = 16 / 4 * 512;                    // bf16 from row m to 16 + m
-static_assert(kRingWaves * 4 == kTile, "four rows per wave");
+constexpr int kRopeHalfRows = 16 / kRingRows * 512;            // bf16 from row m to 16 + m
+static_assert(kRingRows == 4, "one rotary instruction (4 rows of 128 B, twice) per wave");
 constexpr size_t kRingLdsBytes =
     static_cast<size_t>(kRingStages) * kRingStageBytes + sizeof(int) * (kMaxSlots + kRingWaves);
 
@@ -459,18 +544,15 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
     constexpr int kThr = 64 * kRingWaves;
-    const int wg = hg * kRingWaves + wave;                         // 16-head group
-    const int h = wg * 16 + m;
-    const bool active = wg * 16 < Hq;
+    const int wg0 = (hg * kRingWaves + wave) * kRingGroups;        // first 16-head group
+    const bool active = wg0 * 16 < Hq;
 
     const int j_begin = split * slots_per_split;
     const int j_end = min(K, j_begin + slots_per_split);
     const int count = j_end - j_begin;
     const bool paged = cmap.table != nullptr;
     // the split's cache rows, compacted: the selected, present rows first (in
-    // slot order), so tiles of unselected slots (a causal row shorter than
-    // the top-k count, say) are never loaded or computed; the tail of the
-    // last tile is -1
+    // slot order); the tail of the last tile is -1
     int nvalid = 0;
     {
         int* wcnt = sidx + kMaxSlots;                              // per-wave counts
@@ -499,25 +581,28 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     }
     const int ntiles = (nvalid + kTile - 1) / kTile;
     for (int i = nvalid + tid; i < ntiles * kTile; i += kThr) sidx[i] = -1;
-    bf16x8 qreg[kDq / 32];
-    {
-        const uint16_t* qh =
-            q + (static_cast<int64_t>(row) * Hq + (h < Hq ? h : 0)) * kDq + 8 * g;
+
+    bf16x8 qreg[kRingGroups][kDq / 32];
 #pragma unroll
-        for (int ks = 0; ks < kDq / 32; ++ks) {
-            uint4 v = *reinterpret_cast<const uint4*>(qh + ks * 32);
-            if (h >= Hq) v = make_uint4(0u, 0u, 0u, 0u);
-            qreg[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
+    for (int j = 0; j < kRingGroups; ++j) mla_load_q(q, row, Hq, (wg0 + j) * 16 + m, g, qreg[j]);
     // q in registers before the ring's loads are issued: the compiler's own
     // waits for the q loads would otherwise count the ring's loads too
 #pragma unroll
-    for (int ks = 0; ks < kDq / 32; ++ks) asm volatile("" : "+v"(qreg[ks]));
-    v4f acc[kT2];
+    for (int j = 0; j < kRingGroups; ++j)
 #pragma unroll
-    for (int t2 = 0; t2 < kT2; ++t2) acc[t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f, lr_run = 0.0f;
+        for (int ks = 0; ks < kDq / 32; ++ks) asm volatile("" : "+v"(qreg[j][ks]));
+    v4f acc[kRingGroups][kT2];
+#pragma unroll
+    for (int j = 0; j < kRingGroups; ++j)
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2) acc[j][t2] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run[kRingGroups], l_run[kRingGroups], lr_run[kRingGroups];
+#pragma unroll
+    for (int j = 0; j < kRingGroups; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.0f;
+        lr_run[j] = 0.0f;
+    }
     const uint64_t lat_b =
         reinterpret_cast<uint64_t>(latent + (paged ? 0 : b * lat_bs));
     const uint64_t rope_b = reinterpret_cast<uint64_t>(rope + (paged ? 0 : b * rope_bs));
@@ -529,32 +614,32 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     auto issue = [&](int t) {
         const uint32_t st = lds0 + (t % kRingStages) * kRingStageBytes;
         // this wave's four rows: cache rows from one broadcast LDS read
-        const int4 p4 = *reinterpret_cast<const int4*>(sidx + t * kTile + 4 * wave_u);
-        const int pr[4] = {p4.x, p4.y, p4.z, p4.w};
-        // latent: row 4w + j, lane l reads bytes 16 l .. of the row
+        const int4 pa = *reinterpret_cast<const int4*>(sidx + t * kTile + kRingRows * wave_u);
+        const int pr[4] = {pa.x, pa.y, pa.z, pa.w};
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        // latent: row 4w + j, lane l reads bytes 16 l .. of the row
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kRingRows; ++j) {
             const int p = __builtin_amdgcn_readfirstlane(pr[j]);
             const uint64_t base =
                 p >= 0 ? lat_b + static_cast<uint64_t>(static_cast<uint32_t>(p)) *
                                      static_cast<uint64_t>(lat_rs * 2)
                        : zero;
             ring_load_s(base, 16u * static_cast<uint32_t>(ln),
-                        st + (4 * wave_u + j) * (kLatPitch * 2));
+                        st + (kRingRows * wave_u + j) * (kLatPitch * 2));
         }
         // rotary: lane l (and l + 32) fills chunk c = l % 8 of row 4w + j,
         // j = (l / 8) % 4, from source chunk c ^ (row & 6)
         {
             const int j = (ln >> 3) & 3, c = ln & 7;
             const int p = (j & 2) ? ((j & 1) ? pr[3] : pr[2]) : ((j & 1) ? pr[1] : pr[0]);
-            const int sc = c ^ ((4 * wave_u + j) & 6);
+            const int sc = c ^ ((kRingRows * wave_u + j) & 6);
             const uint64_t a =
                 p >= 0 ? rope_b + static_cast<uint64_t>(static_cast<uint32_t>(p)) *
                                       static_cast<uint64_t>(rope_rs * 2) +
                              16u * static_cast<uint32_t>(sc)
-                       : zero + 16u * static_cast<uint32_t>(c);
+                       : zero + 16u * static_cast<uint32_t>(ln);
             ring_load_v(a, st + kRingLatBytes + 1024 * wave_u);
         }
     };
@@ -564,10 +649,8 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     const int rbase = kRingLatBytes / 2 + (m >> 2) * 512 + (m & 3) * 64;
     const int rope16 = rbase + 8 * (g ^ (m & 6));
     const int rope17 = rbase + 8 * ((4 + g) ^ (m & 6));
-#ifndef DSA_RING_PIPE
-#define DSA_RING_PIPE 2, kPipeV = 4, kRingChains = 1
-#endif
-    constexpr int kPipe = DSA_RING_PIPE;
+    // LDS operand reads in flight (the register budget of two waves per SIMD)
+    constexpr int kPipe = 2, kPipeV = 4;
     if (ntiles > 0) issue(0);
     if (ntiles > 1) issue(1);
     for (int t = 0; t < ntiles; ++t) {
@@ -575,21 +658,28 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
         // barrier: every wave's loads, and tile t - 1 consumed
         if (t + 1 < ntiles) ring_wait_barrier<kRingLoads>();
         else ring_wait_barrier<0>();
-        if (t + 2 < ntiles) issue(t + 2);
+        // the loads of tile t + 2 are issued while the score MFMAs run
+        auto ahead = [&]() {
+            if (t + 2 < ntiles) issue(t + 2);
+        };
         if (active)
-            mla_tile_math<kPipe, kPipeV, kLatPitch, kRopeHalfRows, kRingChains>(
+            mla_tile_math<kRingGroups, kPipe, kPipeV, kLatPitch, kRopeHalfRows, 1, true>(
                 reinterpret_cast<const uint16_t*>(smem + (t % kRingStages) * kRingStageBytes),
-                rope16, rope17, sidx + t * kTile, lane, qreg, acc, scale_log2, m_run, l_run,
-                lr_run);
+                rope16, rope17, sidx, nvalid - t * kTile, lane, qreg, acc, scale_log2, m_run,
+                l_run, lr_run, ahead);
+        else
+            ahead();
     }
 
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    float lr_tot = lr_run + __shfl_xor(lr_run, 16);
-    lr_tot += __shfl_xor(lr_tot, 32);
     if (!active) return;
-    mla_store_result<false>(acc, m_run, l_tot, lr_tot, lane, wg, Hq, row, split, nsplit, out, lse,
-                            ws_o, ws_ml);
+#pragma unroll
+    for (int j = 0; j < kRingGroups; ++j) {
+        const float l_tot = sum_over_row_groups(l_run[j]);
+        const float lr_tot = sum_over_row_groups(lr_run[j]);
+        if ((wg0 + j) * 16 < Hq)
+            mla_store_result<false>(acc[j], m_run[j], l_tot, lr_tot, lane, wg0 + j, Hq, row,
+                                    split, nsplit, out, lse, ws_o, ws_ml);
+    }
 }
 
 // The build for the fewest blocks when every split holds at most 64
