@@ -798,7 +798,11 @@ def cpu_baseline(wl, x, seconds):
     cores = oracle.num_threads()
     rec = dict(value=done / el, unit="queries/s", cores=cores, kind="oracle",
                sample=f"{done} single-query decode steps of {wl.name} (batch row 0, "
-                      f"L={n}, H=64, top-{wl.K}, 128 heads) in {el:.1f} s")
+                      f"L={n}, H=64, top-{wl.K}, 128 heads) in {el:.1f} s",
+               # threads each stage of one row can use: the oracle parallelises
+               # over independent rows, or over keys for a single row's scores
+               stage_threads={"prepare_q": min(64, cores), "dequantise": cores,
+                              "scores": cores, "topk": 1, "sparse_mla": min(128, cores)})
     # the same steps on one core, for a few seconds
     oracle.set_num_threads(1)
     try:
