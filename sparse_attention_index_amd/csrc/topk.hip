@@ -496,51 +496,58 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
     int64_t ob = 0;
     if constexpr (CAND_OUT) ob = (static_cast<int64_t>(row) * a.nparts + part) << kps;
     else out = a.idx + static_cast<int64_t>(row) * K;
-    // Per group of four items per lane (item order: lane, then q): the
-    // ballots of the taken items give each item's slot as the taken items
-    // at lower lanes (mbcnt) plus those before it in its lane; ties at T
-    // are ranked the same way among the equal items.
+    // Item order within a wave is (group, lane, element). Each lane turns its
+    // 16 items into bit masks (taken / equal to T), counts each group's
+    // nibble, and two DPP prefix sums over the lanes of the counts packed in
+    // 16-bit fields (at most 256 per field) give every lane its first slot
+    // in each group; the lane then stores its taken items in order. Ties at
+    // T (rare; wave-uniform test) are ranked the same way among the equal
+    // items before the taken counts are formed.
+    auto nib = [](uint32_t m, int g) { return __popc((m >> (4 * g)) & 0xFu); };
+    auto field = [](int lo, int hi, int g) {
+        const int x = g < 2 ? lo : hi;
+        return (g & 1) ? (x >> 16) : (x & 0xFFFF);
+    };
     auto compact = [&](auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
+        uint32_t tkm = 0u, eqm = 0u;
+#pragma unroll
+        for (int j = 0; j < kRegItems; ++j) {
+            const bool ok = FULL || valid(j);
+            tkm |= (ok && (take_all || v[j] > Tf)) ? (1u << j) : 0u;
+            eqm |= (ok && !take_all && v[j] == Tf) ? (1u << j) : 0u;
+        }
+        if (__ballot(eqm != 0u) != 0ull) {
+            const int lo = nib(eqm, 0) | (nib(eqm, 1) << 16), hi = nib(eqm, 2) | (nib(eqm, 3) << 16);
+            const int ilo = wave_incl_scan_add(lo), ihi = wave_incl_scan_add(hi);
+            const int tlo = __builtin_amdgcn_readlane(ilo, 63), thi = __builtin_amdgcn_readlane(ihi, 63);
+            int er = e;
+#pragma unroll
+            for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
+                int r = er + field(ilo - lo, ihi - hi, g4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int j = 4 * g4 + q;
+                    if ((eqm >> j) & 1u) {
+                        tkm |= r < eq_take ? (1u << j) : 0u;
+                        ++r;
+                    }
+                }
+                er += field(tlo, thi, g4);
+            }
+            e = er;
+        }
+        const int lo = nib(tkm, 0) | (nib(tkm, 1) << 16), hi = nib(tkm, 2) | (nib(tkm, 3) << 16);
+        const int ilo = wave_incl_scan_add(lo), ihi = wave_incl_scan_add(hi);
+        const int tlo = __builtin_amdgcn_readlane(ilo, 63), thi = __builtin_amdgcn_readlane(ihi, 63);
 #pragma unroll
         for (int g4 = 0; g4 < kRegItems / 4; ++g4) {
-            bool tk[4], eqv[4];
-            uint64_t E[4];
-            uint64_t any_eq = 0ull;
+            int slot = o + field(ilo - lo, ihi - hi, g4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int j = 4 * g4 + q;
-                const bool ok = FULL || valid(j);
-                tk[q] = ok && (take_all || v[j] > Tf);
-                eqv[q] = ok && !take_all && v[j] == Tf;
-                E[q] = __ballot(eqv[q]);
-                any_eq |= E[q];
-            }
-            if (any_eq != 0ull) {           // wave-uniform: ties at T are rare
-                int er = e;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) er += lanes_below(E[q]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (eqv[q]) {
-                        tk[q] = er < eq_take;
-                        ++er;
-                    }
-                    e += __popcll(E[q]);
-                }
-            }
-            int slot = o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint64_t tm = __ballot(tk[q]);
-                slot += lanes_below(tm);
-                o += __popcll(tm);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (tk[q]) {
+                if ((tkm >> j) & 1u) {
                     if (slot < keff) {
-                        const int j = 4 * g4 + q;
                         int32_t p;
                         if constexpr (CAND_IN) p = pv[j];
                         else p = start + item(j);
@@ -554,6 +561,7 @@ __global__ __launch_bounds__(kRegMaxThreads) void topk_select_kernel(SelectArgs 
                     ++slot;
                 }
             }
+            o += field(tlo, thi, g4);
         }
     };
     if (wave_full) compact(std::true_type{});
