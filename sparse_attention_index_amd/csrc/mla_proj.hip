@@ -80,12 +80,15 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
     // LDS tiles, filled straight from global memory (lane l of a wave
     // instruction writes bytes 16 l .. 16 l + 15 of that instruction's 1 KiB).
     //  - 128 x 32 tiles (A; B stored N x K): 64-byte rows of four 16-byte
-    //    chunks, chunk c of row r at position c ^ ((r >> 2) & 3), so the 16
-    //    rows of an MFMA operand read fall on distinct banks. Instruction j
-    //    of wave w fills rows 16 (4 j + w) .. +15.
+    //    chunks, chunk c of row r at position c ^ (2 ((r >> 2) & 1)).
+    //    Instruction j of wave w fills rows 16 (4 j + w) .. +15.
     //  - 32 x 128 tiles (B stored K x N): 256-byte rows of sixteen chunks,
-    //    chunk c of row r at position c ^ (2 (r & 3)); instruction j of wave
-    //    w fills rows 4 (4 j + w) .. +3.
+    //    chunk c of row r at position c ^ (2 (r & 3)) ^ (8 ((r >> 3) & 1));
+    //    instruction j of wave w fills rows 4 (4 j + w) .. +3.
+    //  Both keep every operand read free of LDS bank conflicts on gfx950
+    //  (the bank-conflict counter of a probe of each access pattern reads
+    //  zero; the earlier swizzles, c ^ ((r >> 2) & 3) and c ^ (2 (r & 3)),
+    //  cost one extra cycle per read).
     // Source addresses of this thread's four loads (k offset added per slice);
     // A rows past M load row M - 1 (their products are never stored).
     const uint16_t* srcA[2];
@@ -93,13 +96,14 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = 16 * (4 * j + wave) + (lane >> 2), p = lane & 3;
-        const int c = p ^ ((r >> 2) & 3);
+        const int c = p ^ (2 * ((r >> 2) & 1));
         srcA[j] = A + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.lda + 8 * c;
         if (!B_KN) {
             srcB[j] = B + static_cast<int64_t>(n0 + r) * a.ldb + 8 * c;
         } else {
             const int kr = 4 * (4 * j + wave) + (lane >> 4), pb = lane & 15;
-            srcB[j] = B + static_cast<int64_t>(kr) * a.ldb + n0 + 8 * (pb ^ (2 * (kr & 3)));
+            srcB[j] = B + static_cast<int64_t>(kr) * a.ldb + n0 +
+                      8 * (pb ^ (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)));
         }
     }
     auto issue = [&](int kt) {
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     // operand read offsets (bytes within a stage)
-    const int swzA = (m >> 2) & 3;
+    const int swzA = 2 * ((m >> 2) & 1);
     const int offA = (64 * wm + m) * 64 + 16 * (g ^ swzA);            // + 16 i rows: + 1024 i
     const int offBnt = kGTileBytes + (64 * wn + m) * 64 + 16 * (g ^ swzA);
     // K x N: lane 4e + q of group g reads row 8g + e (and 8g + 4 + e),
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
             if (!B_KN) {
                 bv[j] = *reinterpret_cast<const bf16x8*>(st + offBnt + 1024 * j);
             } else {
-                const int pos = (cBkn + 2 * j) ^ (2 * e);
+                const int pos = (cBkn + 2 * j) ^ (2 * e) ^ (8 * (g & 1));
                 const uint16_t* p = reinterpret_cast<const uint16_t*>(st + offBkn + 16 * pos);
                 const uint2 lo = __builtin_bit_cast(uint2, lds_read_tr16(p));
                 const uint2 hi = __builtin_bit_cast(uint2, lds_read_tr16(p + 4 * 128));
