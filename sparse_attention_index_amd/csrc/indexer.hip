@@ -336,13 +336,8 @@ __global__ __launch_bounds__(256) void score_rows_kernel(
 // are reused from that XCD's L2.
 // ---------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
-#ifndef DSA_TILE_KW
-#define DSA_TILE_KW 2
-#endif
-#ifndef DSA_TILE_OCC
-#define DSA_TILE_OCC 2
-#endif
-constexpr int kKW = DSA_TILE_KW;            // 32-key tiles per wave
+constexpr int kKW = 2;                      // 32-key tiles per wave
+constexpr int kTileBlocksPerCU = 2;         // occupancy the tile kernel is built for
 constexpr int kQT = 64, kKT = 64 * kKW;     // queries, keys per block tile
 constexpr int kQsStride = 128 + 8;          // bf16 per staged query row (bank stagger)
 
@@ -350,7 +345,7 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256, DSA_TILE_OCC) void score_tile_kernel(
+__global__ __launch_bounds__(256, kTileBlocksPerCU) void score_tile_kernel(
     int B, int S, int H, int Lmax, int P, int nqt, int nkt, const uint8_t* __restrict__ q8,
     const float* __restrict__ qscale, const float* __restrict__ w,
     const int32_t* __restrict__ pos, const uint8_t* __restrict__ kcache,
@@ -952,15 +947,11 @@ __global__ __launch_bounds__(NW * 64) void decode_score_kernel(
     }
 }
 
-// Looping decode grid: blocks of DSA_DEC_LOOP_NW waves scoring chunks of
-// DSA_DEC_LOOP_NW * 64 keys, about DSA_DEC_LOOP_BLOCKS blocks in all; used
+// Looping decode grid: blocks of kDecLoopWaves waves scoring chunks of
+// kDecLoopWaves * 64 keys, about kDecLoopBlocks blocks in all; used
 // when a call has more than that many chunks.
-#ifndef DSA_DEC_LOOP_BLOCKS
-#define DSA_DEC_LOOP_BLOCKS 256
-#endif
-#ifndef DSA_DEC_LOOP_NW
-#define DSA_DEC_LOOP_NW 8
-#endif
+constexpr int kDecLoopBlocks = 256;         // blocks of the looping decode grid, about
+constexpr int kDecLoopWaves = 8;            // waves per block of the looping grid
 
 hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, const void* q_raw,
                                const void* k_raw, const int32_t* pos, const float* cos_t,
@@ -968,15 +959,15 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                                float* kscale, uint8_t* q8_out, float* qs_out, float* scores,
                                int64_t ld, CacheMap cmap, bool hadamard, bool pow2,
                                hipStream_t stream) {
-    constexpr int kLoopChunk = DSA_DEC_LOOP_NW * 64;
+    constexpr int kLoopChunk = kDecLoopWaves * 64;
     const int chunksl = (Lmax + kLoopChunk - 1) / kLoopChunk;
-    const bool loop = static_cast<int64_t>(B) * chunksl > DSA_DEC_LOOP_BLOCKS;
+    const bool loop = static_cast<int64_t>(B) * chunksl > kDecLoopBlocks;
     int U = 4;
     unsigned gx, threads;
     if (loop) {
-        const int bpr = (DSA_DEC_LOOP_BLOCKS + B - 1) / B;
+        const int bpr = (kDecLoopBlocks + B - 1) / B;
         gx = static_cast<unsigned>(bpr < chunksl ? bpr : chunksl);
-        threads = DSA_DEC_LOOP_NW * 64;
+        threads = kDecLoopWaves * 64;
     } else {
         // one chunk of 64 U keys per block, U shrunk (down to 1) to give more blocks
         while (U > 1 && static_cast<int64_t>(B) * ((Lmax + 64 * U - 1) / (64 * U)) < 2048) U >>= 1;
@@ -989,12 +980,12 @@ hipError_t launch_decode_score(bool bf16_in, int B, int H, int Lmax, int P, cons
                        Lmax, P, q_raw, k_raw, pos, cos_t, sin_t, w, kcache, kscale, q8_out,    \
                        qs_out, scores, ld, cmap, hadamard ? 1 : 0, pow2 ? 1 : 0)
     if (bf16_in) {
-        if (loop) DSA_DEC(4, DSA_DEC_LOOP_NW, true, true);
+        if (loop) DSA_DEC(4, kDecLoopWaves, true, true);
         else if (U == 4) DSA_DEC(4, 4, false, true);
         else if (U == 2) DSA_DEC(2, 4, false, true);
         else DSA_DEC(1, 4, false, true);
     } else {
-        if (loop) DSA_DEC(4, DSA_DEC_LOOP_NW, true, false);
+        if (loop) DSA_DEC(4, kDecLoopWaves, true, false);
         else if (U == 4) DSA_DEC(4, 4, false, false);
         else if (U == 2) DSA_DEC(2, 4, false, false);
         else DSA_DEC(1, 4, false, false);

@@ -32,11 +32,8 @@
 
 namespace dsa {
 
-#ifndef DSA_GEMM_STAGES
-#define DSA_GEMM_STAGES 2
-#endif
 constexpr int kGM = 128, kGN = 128, kGK = 32;
-constexpr int kGStages = DSA_GEMM_STAGES;            // k-slices in the LDS ring
+constexpr int kGStages = 2;                          // k-slices in the LDS ring
 constexpr int kGThreads = 256;
 constexpr int kGTileBytes = 128 * kGK * 2;           // one 128 x 32 (or 32 x 128) bf16 tile
 constexpr int kGStageBytes = 2 * kGTileBytes;        // A tile + B tile

@@ -949,11 +949,8 @@ __device__ __forceinline__ float wave_incl_sum_f(float v) {
 // a wave is 512 consecutive bytes. Per head, wave w first turns the
 // (m, l, lr) triples of all splits (one split per lane) into weights
 // 2^(m_s - M) in LDS and the totals L, Lr.
-#ifndef DSA_COMBINE_CFG
-#define DSA_COMBINE_CFG 408                  // feature parts per 16-head group * 100 + unroll
-#endif
-constexpr int kCombineQuarters = DSA_COMBINE_CFG / 100;
-constexpr int kCombineUnroll = DSA_COMBINE_CFG % 100;
+constexpr int kCombineQuarters = 4;         // feature parts per 16-head group
+constexpr int kCombineUnroll = 8;           // splits whose loads are in flight together
 constexpr int kCombineT2 = kT2 / kCombineQuarters / 4;     // 16-feature tiles per wave
 
 __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
