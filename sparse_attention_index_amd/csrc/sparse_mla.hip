@@ -533,11 +533,14 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     int* sidx = reinterpret_cast<int*>(smem + kRingStages * kRingStageBytes);
 
-    // launch index -> (work item = row * nsplit + split, head group), as in
-    // the tile kernel
+    // launch index -> (work item = row * nsplit + split, head group): launch
+    // L runs on XCD L % 8; the nsplit splits of a row (and its head groups)
+    // go to one XCD, consecutive rows round the XCDs (one split: as in the
+    // tile kernel)
     const int L = blockIdx.x;
-    const int item = (L / (8 * hgroups)) * 8 + (L & 7);
-    const int hg = (L / 8) % hgroups;
+    const int jj = (L >> 3) / hgroups;
+    const int hg = (L >> 3) % hgroups;
+    const int item = ((jj / nsplit) * 8 + (L & 7)) * nsplit + jj % nsplit;
     if (item >= nitems) return;
     const int row = item / nsplit, split = item - row * nsplit;
     const int64_t b = row / S;
@@ -658,17 +661,15 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
         // barrier: every wave's loads, and tile t - 1 consumed
         if (t + 1 < ntiles) ring_wait_barrier<kRingLoads>();
         else ring_wait_barrier<0>();
-        // the loads of tile t + 2 are issued while the score MFMAs run
-        auto ahead = [&]() {
-            if (t + 2 < ntiles) issue(t + 2);
-        };
         if (active)
             mla_tile_math<kRingGroups, kPipe, kPipeV, kLatPitch, kRopeHalfRows, 1, true>(
                 reinterpret_cast<const uint16_t*>(smem + (t % kRingStages) * kRingStageBytes),
                 rope16, rope17, sidx, nvalid - t * kTile, lane, qreg, acc, scale_log2, m_run,
-                l_run, lr_run, ahead);
-        else
-            ahead();
+                l_run, lr_run);
+        // the loads of tile t + 2 (into tile t - 1's stage) are issued after
+        // the tile's math, where the wave would wait at the next barrier
+        // anyway: issued during the score MFMAs they held up the MFMA stream
+        if (t + 2 < ntiles) issue(t + 2);
     }
 
     if (!active) return;
@@ -1239,7 +1240,8 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
         // more than one block per CU and more than 64 heads: 128-head
         // blocks, each row gathered once, the gather two tiles ahead
         const int hg_ring = (Hq + kRingHeads - 1) / kRingHeads;
-        const int nb_ring = ((nitems + 7) / 8) * 8 * hg_ring;
+        // whole groups of 8 rows' splits (the launch-to-item map above)
+        const int nb_ring = ((nitems + 8 * ns - 1) / (8 * ns)) * 8 * ns * hg_ring;
         e = set_dynamic_lds_limit(reinterpret_cast<const void*>(&sparse_mla_ring_kernel),
                                   static_cast<int>(kRingLdsBytes));
         if (e != hipSuccess) return e;
