@@ -47,6 +47,8 @@
 // rounding, at most 2^-9 of the split's weighted |latent|, costs), and
 // combine_kernel (merge_few_kernel for the fewest rows) merges them in
 // float32 with the log-sum-exp rule.
+#include <type_traits>
+
 #include "dsa_common.h"
 
 namespace dsa {
@@ -213,49 +215,61 @@ __device__ __forceinline__ void mla_scores(const uint16_t* Kt, int rope16, int r
     for (int d = 0; d < kEarlyV; ++d) va[d] = mla_read_v<kPitch>(Kt, lane, d);
     if constexpr (kEarlyV > 0) DSA_SCHED_GROUP(kSchedDsRead, 2 * kEarlyV);
 
-    bool valid[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        valid[i] = kCounted ? 4 * g + i < nk : sk[4 * g + i] >= 0;
-        valid[4 + i] = kCounted ? 16 + 4 * g + i < nk : sk[16 + 4 * g + i] >= 0;
-    }
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-        float z[8];
-        float tmax = -INFINITY;
+    // kFull: a counted tile whose 32 keys are all selected (every tile of a
+    // split but its last) needs no mask
+    auto softmax = [&](auto full_c) {
+        constexpr bool kFull = decltype(full_c)::value;
+        bool valid[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = valid[i] ? s0[j][i] * scale_log2 : -INFINITY;
-            z[4 + i] = valid[4 + i] ? s1[j][i] * scale_log2 : -INFINITY;
+            valid[i] = kFull || (kCounted ? 4 * g + i < nk : sk[4 * g + i] >= 0);
+            valid[4 + i] = kFull || (kCounted ? 16 + 4 * g + i < nk : sk[16 + 4 * g + i] >= 0);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
-        tmax = max_over_row_groups(tmax);
-        // Lazy rescaling: probabilities are taken relative to a reference
-        // maximum m_run that only moves when the running maximum exceeds it
-        // by more than 8 (so p <= 2^8, exact enough in float and bf16).
-        if (tmax > m_run[j] + 8.0f) {
-            const float corr = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - tmax);
-            l_run[j] *= corr;
-            lr_run[j] *= corr;
-            m_run[j] = tmax;
-            if (__ballot(corr != 1.0f)) {
+        for (int j = 0; j < NG; ++j) {
+            float z[8];
+            float tmax = -INFINITY;
 #pragma unroll
-                for (int t2 = 0; t2 < kT2; ++t2) acc[j][t2] *= corr;
+            for (int i = 0; i < 4; ++i) {
+                z[i] = valid[i] ? s0[j][i] * scale_log2 : -INFINITY;
+                z[4 + i] = valid[4 + i] ? s1[j][i] * scale_log2 : -INFINITY;
             }
-        }
-        const bool live = m_run[j] != -INFINITY;
-        float psum = 0.0f, prsum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float pe = live ? __builtin_amdgcn_exp2f(z[i] - m_run[j]) : 0.0f;
-            const __bf16 pb = static_cast<__bf16>(pe);
-            pv[j][i] = pb;
-            psum += pe;
-            prsum += static_cast<float>(pb);
+            for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, z[i]);
+            tmax = max_over_row_groups(tmax);
+            // Lazy rescaling: probabilities are taken relative to a reference
+            // maximum m_run that only moves when the running maximum exceeds
+            // it by more than 8 (so p <= 2^8, exact enough in float and bf16).
+            if (tmax > m_run[j] + 8.0f) {
+                const float corr = (m_run[j] == -INFINITY) ? 0.0f : exp2f(m_run[j] - tmax);
+                l_run[j] *= corr;
+                lr_run[j] *= corr;
+                m_run[j] = tmax;
+                if (__ballot(corr != 1.0f)) {
+#pragma unroll
+                    for (int t2 = 0; t2 < kT2; ++t2) acc[j][t2] *= corr;
+                }
+            }
+            // while m_run is -inf every z is -inf too, and 2^(-inf - 0) = 0
+            const float mref = m_run[j] == -INFINITY ? 0.0f : m_run[j];
+            float psum = 0.0f, prsum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float pe = __builtin_amdgcn_exp2f(z[i] - mref);
+                const __bf16 pb = static_cast<__bf16>(pe);
+                pv[j][i] = pb;
+                psum += pe;
+                prsum += static_cast<float>(pb);
+            }
+            l_run[j] += psum;
+            lr_run[j] += prsum;
         }
-        l_run[j] += psum;
-        lr_run[j] += prsum;
+    };
+    if constexpr (kCounted) {
+        if (nk >= kTile) softmax(std::true_type{});
+        else softmax(std::false_type{});
+    } else {
+        softmax(std::false_type{});
     }
 }
 
@@ -657,6 +671,7 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     if (ntiles > 0) issue(0);
     if (ntiles > 1) issue(1);
     for (int t = 0; t < ntiles; ++t) {
+
         // tile t has landed once only tile t + 1's loads are in flight; the
         // barrier: every wave's loads, and tile t - 1 consumed
         if (t + 1 < ntiles) ring_wait_barrier<kRingLoads>();
