@@ -1038,6 +1038,78 @@ __global__ __launch_bounds__(256) void combine_kernel(int Hq, int nsplit,
     }
 }
 
+// The same merge for at most kS splits (the batched-decode plans): the
+// block and lane layout of combine_kernel, but each lane loads its head's
+// (m, lr, l) triples of every split and its partials of every split at
+// once and forms the weights itself, so the merge is one memory round trip
+// with no LDS and no barrier. Loads past nsplit repeat the last split and
+// are masked after arrival.
+template <int kS>
+__global__ __launch_bounds__(256) void combine_regs_kernel(int Hq, int nsplit,
+                                                           const uint16_t* __restrict__ ws_o,
+                                                           const float* __restrict__ ws_ml,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse) {
+    const int nwg = (Hq + 15) / 16;
+    const int quarter = blockIdx.x % kCombineQuarters;
+    const int wg = (blockIdx.x / kCombineQuarters) % nwg;
+    const int64_t row = blockIdx.x / (kCombineQuarters * nwg);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int h = wg * 16 + m;
+    const int hc = h < Hq ? h : Hq - 1;
+    const int t2a = quarter * (kT2 / kCombineQuarters) + kCombineT2 * wave;
+    const uint16_t* base = ws_o + (row * nsplit * nwg + wg) * (kT2 * 64 * 4) + lane * 4;
+    const int64_t sstride = static_cast<int64_t>(nwg) * kT2 * 64 * 4;
+    const float* mb = ws_ml + (row * nsplit * Hq + hc) * 4;
+    const int64_t ms = static_cast<int64_t>(Hq) * 4;
+
+    float4 ml[kS];
+    uint2 w[kS][kCombineT2];
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp) {
+        const int sc = min(sp, nsplit - 1);
+        ml[sp] = *reinterpret_cast<const float4*>(mb + sc * ms);
+#pragma unroll
+        for (int u = 0; u < kCombineT2; ++u)
+            w[sp][u] = *reinterpret_cast<const uint2*>(base + sc * sstride + (t2a + u) * 256);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp)
+        if (sp < nsplit) M = fmaxf(M, ml[sp].x);
+    float L = 0.0f, Lr = 0.0f;
+    float4 a[kCombineT2];
+#pragma unroll
+    for (int u = 0; u < kCombineT2; ++u) a[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp) {
+        if (sp < nsplit) {                                         // uniform
+            const float e = ml[sp].x == -INFINITY ? 0.0f : exp2f(ml[sp].x - M);
+            L += ml[sp].z * e;
+            Lr += ml[sp].y * e;
+#pragma unroll
+            for (int u = 0; u < kCombineT2; ++u) {
+                a[u].x += e * __uint_as_float(w[sp][u].x << 16);
+                a[u].y += e * __uint_as_float(w[sp][u].x & 0xFFFF0000u);
+                a[u].z += e * __uint_as_float(w[sp][u].y << 16);
+                a[u].w += e * __uint_as_float(w[sp][u].y & 0xFFFF0000u);
+            }
+        }
+    }
+    if (h >= Hq) return;
+    const float inv = Lr > 0.0f ? 1.0f / Lr : 0.0f;
+    uint16_t* oh = out + (row * Hq + h) * kDl + 4 * g;
+#pragma unroll
+    for (int u = 0; u < kCombineT2; ++u) {
+        const uint32_t lo = pack_bf16x2(a[u].x * inv, a[u].y * inv);
+        const uint32_t hi = pack_bf16x2(a[u].z * inv, a[u].w * inv);
+        *reinterpret_cast<uint2*>(oh + 16 * (t2a + u)) = make_uint2(lo, hi);
+    }
+    if (lse != nullptr && quarter == 0 && wave == 0 && g == 0)
+        lse[row * Hq + h] = L > 0.0f ? M * 0.69314718055994531f + logf(L) : -INFINITY;
+}
+
 // Merge for the fewest rows (the grid of the 32-head builds, at most 32
 // splits): one 64-thread block per (row, 16-head group, 16-feature tile t2),
 // so that even one row's merge spreads over the whole chip, with no barrier
@@ -1276,8 +1348,19 @@ hipError_t launch_sparse_mla(int B, int S, int Hq, int Lmax, int K, const uint16
         if (ns <= kMergeMaxSplits && merge_blocks <= 2048) {
             e = launch_merge_few(stream, rows, Hq, ns, ws_o, ws_ml, out, lse);
         } else {
-            hipLaunchKernelGGL(combine_kernel, dim3(rows * nwg * kCombineQuarters), dim3(256), 0,
-                               stream, Hq, ns, ws_o, ws_ml, out, lse);
+            const dim3 grid(rows * nwg * kCombineQuarters);
+            if (ns <= 4)
+                hipLaunchKernelGGL(combine_regs_kernel<4>, grid, dim3(256), 0, stream, Hq, ns,
+                                   ws_o, ws_ml, out, lse);
+            else if (ns <= 8)
+                hipLaunchKernelGGL(combine_regs_kernel<8>, grid, dim3(256), 0, stream, Hq, ns,
+                                   ws_o, ws_ml, out, lse);
+            else if (ns <= 16)
+                hipLaunchKernelGGL(combine_regs_kernel<16>, grid, dim3(256), 0, stream, Hq, ns,
+                                   ws_o, ws_ml, out, lse);
+            else
+                hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, Hq, ns, ws_o, ws_ml,
+                                   out, lse);
             e = hipGetLastError();
         }
     }
