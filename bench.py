@@ -77,7 +77,7 @@ KERNELS_OF_CALL = {
     "indexer": ["decode_score_kernel"],
     "topk": ["topk_select_kernel"],
     "sparse_mla": ["sparse_mla_kernel", "sparse_mla_pair_kernel", "sparse_mla_ring_kernel",
-                   "merge_few_kernel", "combine_kernel"],
+                   "merge_few_kernel", "combine_regs_kernel", "combine_kernel"],
 }
 
 
