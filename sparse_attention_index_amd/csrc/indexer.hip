@@ -339,7 +339,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kKW = 2;                      // 32-key tiles per wave
 constexpr int kTileBlocksPerCU = 2;         // occupancy the tile kernel is built for
 constexpr int kQT = 64, kKT = 64 * kKW;     // queries, keys per block tile
-constexpr int kQsStride = 128 + 8;          // bf16 per staged query row
+constexpr int kQsStride = 128 + 8;          // bf16 per staged query row (bank stagger)
 
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -423,11 +423,8 @@ __global__ __launch_bounds__(256, kTileBlocksPerCU) void score_tile_kernel(
             raw1 = src[1];
         }
     };
-    // 16-byte chunk c of query row r is stored at chunk c ^ 8 (r & 16): an
-    // A read serves lanes l and l + 16 (rows r and r + 16) together, which
-    // every 16-byte-aligned row stride maps to the same banks
     auto stage_q = [&](int buf) {
-        uint16_t* dst = &Qs[buf][sq][32 * (sc ^ (2 * ((sq >> 4) & 1)))];
+        uint16_t* dst = &Qs[buf][sq][32 * sc];
         *reinterpret_cast<bf16x8*>(dst + 0) = e4m3x8_to_bf16x8(raw0.x, raw0.y);
         *reinterpret_cast<bf16x8*>(dst + 8) = e4m3x8_to_bf16x8(raw0.z, raw0.w);
         *reinterpret_cast<bf16x8*>(dst + 16) = e4m3x8_to_bf16x8(raw1.x, raw1.y);
@@ -439,10 +436,7 @@ __global__ __launch_bounds__(256, kTileBlocksPerCU) void score_tile_kernel(
     for (int kt2 = 0; kt2 < kKW; ++kt2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) I[kt2][i] = 0.0f;
-    // k-steps 0..3 and 4..7 swap halves on rows with bit 4 set
-    const int swz = 64 * ((l32 >> 4) & 1);
-    const uint16_t* arow = &Qs[0][wq_i * 32 + l32][8 * hi32 + swz];
-    const uint16_t* arow_hi = &Qs[0][wq_i * 32 + l32][8 * hi32 - swz];
+    const uint16_t* arow = &Qs[0][wq_i * 32 + l32][8 * hi32];
     constexpr int kBufStride = kQT * kQsStride;
     fetch_q(0);
     for (int h = 0; h < H; ++h) {
@@ -457,8 +451,7 @@ __global__ __launch_bounds__(256, kTileBlocksPerCU) void score_tile_kernel(
             for (int i = 0; i < 16; ++i) sacc[kt2][i] = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>((ks < 4 ? arow : arow_hi) +
-                                                              buf * kBufStride + 16 * ks);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + buf * kBufStride + 16 * ks);
 #pragma unroll
             for (int kt2 = 0; kt2 < kKW; ++kt2)
                 sacc[kt2] = mfma_bf16_32x32x16(a, kb[kt2][ks], sacc[kt2]);
