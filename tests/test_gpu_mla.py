@@ -79,6 +79,12 @@ CASES = [
     ("few-split16", 1, 1, 128, 3000, 1024, 3000, 0.7),
     ("few-split25", 1, 1, 64, 4000, 1600, 4000, 0.5),
     ("few-short-rows", 1, 2, 128, 300, 2048, 300, 1.0),
+    # the split merges of the batched plans: 13 splits (register merge for up
+    # to 16, three masked), 7 splits (register merge for up to 8, one
+    # masked) and 22 splits (the LDS-weight merge)
+    ("merge-regs16", 1, 20, 128, 2500, 2048, 2500, 0.9),
+    ("merge-regs8-masked", 1, 40, 128, 2500, 2048, 2500, 0.9),
+    ("merge-lds", 1, 10, 128, 2500, 2048, 2500, 0.9),
 ]
 
 
