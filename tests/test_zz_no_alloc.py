@@ -50,6 +50,31 @@ def test_noalloc_matches_workspace_call_twice():
         assert np.allclose(host(lse), ol, rtol=0, atol=1e-3)
 
 
+def test_noalloc_batched_merges():
+    """The batched plans' split merges on the static scratch: 40 rows of 2048
+    keys (7 splits, the register merge for up to 8), then 20 rows (13 splits,
+    the register merge for up to 16), each bit-identical to the workspace
+    call and within the attention bar of the oracle."""
+    import torch
+    scale = 192 ** -0.5
+    for case, (S, L) in enumerate([(40, 2500), (20, 2200)]):
+        say(f"noalloc batched call {case}: S={S} Hq=128 L={L} K=2048")
+        q, lat, kpe, idx = inputs(960 + case, 1, S, 128, L, 2048, 0.9)
+        dq, dlat, dkpe, didx = dev_bf16(q), dev_bf16(lat), dev_bf16(kpe), dev(idx)
+        out = torch.full((1, S, 128, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((1, S, 128), float("nan"), dtype=torch.float32, device="cuda")
+        dsa.sparse_mla_noalloc(dq, dlat, dkpe, didx, scale, out, lse)
+        ref_out, ref_lse = dsa.sparse_mla(dq, dlat, dkpe, didx, scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out.view(torch.int16)), host(ref_out.view(torch.int16)))
+        assert np.array_equal(host(lse), host(ref_lse))
+        o, ol = oracle_on_selection(q, lat, kpe, idx, scale)
+        err = float(np.abs(host_bf16_as_f32(out) - o).max())
+        say(f"  bit-identical to dsa_sparse_mla; max abs err vs oracle {err:.3e}")
+        assert err <= MLA_ATOL
+        assert np.allclose(host(lse), ol, rtol=0, atol=1e-3)
+
+
 def test_noalloc_rejects_more_than_its_scratch():
     import torch
     B, Hq, L, K = 230, 128, 256, 2048                        # 230 rows: ~58 MiB of partials
