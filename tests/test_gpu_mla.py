@@ -35,7 +35,7 @@ def report(label, g, gl, o, ol):
     output, its ratio to the largest |output|, max-abs on the finite lse."""
     err = float(np.abs(g - o).max())
     fin = np.isfinite(ol)
-    lerr = float(np.abs(gl - ol)[fin].max(initial=0.0))
+    lerr = float(np.abs(gl[fin] - ol[fin]).max(initial=0.0))
     say(f"  {label}: max abs err {err:.3e} (largest |out| {np.abs(o).max():.3f}), "
         f"lse max abs err {lerr:.3e}")
     return err
@@ -124,6 +124,31 @@ def test_mla_empty_selection_and_out_of_range_indices():
     o, ol = oracle_on_selection(q, lat, kpe, ref_idx, 0.1)
     assert np.abs(out[0, 1:] - o[0, 1:]).max() <= MLA_ATOL
     assert np.allclose(out[0, 2], synth.bf16_bits_to_f32(lat[0, 63])[None], atol=1e-2)
+
+
+def test_mla_batched_empty_splits_and_rows():
+    """The batched path (128-head ring blocks, 7 key splits, register merge)
+    with a sparse selection, so that many splits hold no key at all, and two
+    rows with none: those rows give zeros and lse = -inf."""
+    import torch
+    B, S, Hq, L, K = 1, 40, 128, 3000, 2048
+    g = synth.rng(71)
+    q = synth.to_bf16_bits(g.standard_normal((B, S, Hq, 576), dtype=np.float32))
+    lat = synth.to_bf16_bits(g.standard_normal((B, L, 512), dtype=np.float32))
+    kpe = synth.to_bf16_bits(g.standard_normal((B, L, 64), dtype=np.float32))
+    idx = synth.random_selection(72, B * S, K, np.full(B * S, L), 0.005).reshape(B, S, K)
+    idx[0, 3] = -1
+    idx[0, 17] = -1
+    say("mla batched path, empty splits and rows")
+    out, lse = dsa.sparse_mla(dev_bf16(q), dev_bf16(lat), dev_bf16(kpe), dev(idx), 0.07,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    g_out, g_lse = host_bf16_as_f32(out), host(lse)
+    assert np.all(g_out[0, 3] == 0) and np.all(g_out[0, 17] == 0)
+    assert np.all(np.isneginf(g_lse[0, 3])) and np.all(np.isneginf(g_lse[0, 17]))
+    o, ol = oracle_on_selection(q, lat, kpe, idx, 0.07)
+    assert report("empty splits", g_out, g_lse, o, ol) <= MLA_ATOL
+    assert np.allclose(g_lse, ol, atol=1e-3, rtol=1e-4)
 
 
 def test_mla_decode128k_full_size():
