@@ -687,13 +687,52 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
         if (t + 2 < ntiles) issue(t + 2);
     }
 
-    if (!active) return;
+    // lane, head group and activity recomputed here (mbcnt, scalars) rather
+    // than kept live through the tile loop
+    const int lane_e = static_cast<int>(
+        __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+    const int m_e = lane_e & 15, g_e = lane_e >> 4;
+    const int wg0_e = (hg * kRingWaves + wave_u) * kRingGroups;
+    const bool active_e = wg0_e * 16 < Hq;
+    if (nsplit == 1) {
+        // one split: the normalised rows go out through LDS (the ring's
+        // stages are free now), each wave's 16 head rows at a 1,040-byte
+        // pitch, then one whole 1 KiB head row per store instruction
+        static_assert(kRingGroups == 1, "one 16-head group per wave");
+        constexpr int kOutPitch = kDl + 8;                        // bf16
+        static_assert(static_cast<size_t>(kRingWaves) * 16 * kOutPitch * 2 <= kRingLdsBytes,
+                      "output staging fits the ring's LDS");
+        __syncthreads();                                           // every wave past its last tile
+        if (!active_e) return;
+        const float l_tot = sum_over_row_groups(l_run[0]);
+        const float lr_tot = sum_over_row_groups(lr_run[0]);
+        const int h = wg0_e * 16 + m_e;
+        if (lse != nullptr && g_e == 0 && h < Hq)
+            lse[static_cast<int64_t>(row) * Hq + h] =
+                l_tot > 0.0f ? m_run[0] * 0.69314718055994531f + logf(l_tot) : -INFINITY;
+        const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+        uint16_t* stg = reinterpret_cast<uint16_t*>(smem) + wave_u * 16 * kOutPitch;
+#pragma unroll
+        for (int t2 = 0; t2 < kT2; ++t2)
+            *reinterpret_cast<uint2*>(stg + m_e * kOutPitch + 16 * t2 + 4 * g_e) =
+                make_uint2(pack_bf16x2(acc[0][t2][0] * inv, acc[0][t2][1] * inv),
+                           pack_bf16x2(acc[0][t2][2] * inv, acc[0][t2][3] * inv));
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (wg0_e * 16 + k >= Hq) break;                       // wave-uniform
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + k * kOutPitch + 8 * lane_e);
+            *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(row) * Hq + wg0_e * 16 + k) * kDl +
+                                      8 * lane_e) = v;
+        }
+        return;
+    }
+    if (!active_e) return;
 #pragma unroll
     for (int j = 0; j < kRingGroups; ++j) {
         const float l_tot = sum_over_row_groups(l_run[j]);
         const float lr_tot = sum_over_row_groups(lr_run[j]);
-        if ((wg0 + j) * 16 < Hq)
-            mla_store_result<false>(acc[j], m_run[j], l_tot, lr_tot, lane, wg0 + j, Hq, row,
+        if ((wg0_e + j) * 16 < Hq)
+            mla_store_result<false>(acc[j], m_run[j], l_tot, lr_tot, lane_e, wg0_e + j, Hq, row,
                                     split, nsplit, out, lse, ws_o, ws_ml);
     }
 }
