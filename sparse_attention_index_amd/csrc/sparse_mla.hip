@@ -572,13 +572,24 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     // slot order); the tail of the last tile is -1
     int nvalid = 0;
     {
+        // every index (and page-table) load of the split issued before the
+        // first is used: one memory round trip instead of one per 512 slots
+        constexpr int kRounds = kMaxSlots / kThr;
+        static_assert(kRounds * kThr == kMaxSlots, "slot rounds");
         int* wcnt = sidx + kMaxSlots;                              // per-wave counts
         const int32_t* irow = idx + static_cast<int64_t>(row) * K + j_begin;
-        for (int base = 0; base < count; base += kThr) {
-            const int i = base + tid;
-            const int p = i < count ? irow[i] : -1;
-            int v = -1;
-            if (p >= 0 && p < Lmax) v = paged ? static_cast<int>(cmap.row(b, p)) : p;
+        int vv[kRounds];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) vv[r] = irow[min(r * kThr + tid, count - 1)];
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int p = r * kThr + tid < count ? vv[r] : -1;
+            vv[r] = (p >= 0 && p < Lmax) ? (paged ? static_cast<int>(cmap.row(b, p)) : p) : -1;
+        }
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            if (r * kThr >= count) break;                          // uniform
+            const int v = vv[r];
             const uint64_t bal = __ballot(v >= 0);
             const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
