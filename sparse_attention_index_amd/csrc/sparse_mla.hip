@@ -549,13 +549,16 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
 
     // launch index -> (work item = row * nsplit + split, head group): launch
     // L runs on XCD L % 8; the nsplit splits of a row (and its head groups)
-    // go to one XCD, consecutive rows round the XCDs (one split: as in the
-    // tile kernel)
+    // go to one XCD, consecutive rows round the XCDs
     const int L = blockIdx.x;
     const int jj = (L >> 3) / hgroups;
     const int hg = (L >> 3) % hgroups;
-    const int item = ((jj / nsplit) * 8 + (L & 7)) * nsplit + jj % nsplit;
-    if (item >= nitems) return;
+    const int item_l = ((jj / nsplit) * 8 + (L & 7)) * nsplit + jj % nsplit;
+    if (item_l >= nitems) return;
+    // items in reverse: in a causal prefill the last rows select the most
+    // keys, so the longest blocks start first and the short ones fill the
+    // tail (a row's splits stay together)
+    const int item = nitems - 1 - item_l;
     const int row = item / nsplit, split = item - row * nsplit;
     const int64_t b = row / S;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
