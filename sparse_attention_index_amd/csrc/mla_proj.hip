@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
 
     // Epilogue through LDS: lane holds C[64 wm + 16 i + m][64 wn + 16 j + 4 g + 0..3];
     // the bf16 tile goes to LDS ([128][128 + 8]) and leaves in 16-byte
-    // pieces, 16 threads per 256-byte row (whole cache lines per store).
+    // pieces, 16 threads per 256-byte row (whole cache lines per store),
+    // streamed past L2 (query absorption: 224 -> 130 us for its 537 MB)
     constexpr int kCS = kGN + 8;
     static_assert(sizeof(uint16_t) * kGM * kCS <= kGemmLds, "output tile fits the LDS");
     __builtin_amdgcn_s_barrier();                  // every wave done with the ring
@@ -187,8 +188,8 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_bf16_kernel(GemmArgs a) {
         const int r = 16 * p + cr;
         const int row = m0 + r;
         if (row < a.M)
-            *reinterpret_cast<uint4*>(C + static_cast<int64_t>(row) * a.ldc + n0 + cc) =
-                *reinterpret_cast<const uint4*>(ct + r * kCS + cc);
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ct + r * kCS + cc),
+                                        reinterpret_cast<u32x4*>(C + static_cast<int64_t>(row) * a.ldc + n0 + cc));
     }
 }
 

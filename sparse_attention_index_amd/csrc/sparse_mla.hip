@@ -711,7 +711,8 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
     if (nsplit == 1) {
         // one split: the normalised rows go out through LDS (the ring's
         // stages are free now), each wave's 16 head rows at a 1,040-byte
-        // pitch, then one whole 1 KiB head row per store instruction
+        // pitch, then one whole 1 KiB head row per store instruction,
+        // streamed past L2 (which keeps the cache rows other blocks gather)
         static_assert(kRingGroups == 1, "one 16-head group per wave");
         constexpr int kOutPitch = kDl + 8;                        // bf16
         static_assert(static_cast<size_t>(kRingWaves) * 16 * kOutPitch * 2 <= kRingLdsBytes,
@@ -734,9 +735,10 @@ __global__ __launch_bounds__(64 * kRingWaves, 1) void sparse_mla_ring_kernel(
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             if (wg0_e * 16 + k >= Hq) break;                       // wave-uniform
-            const uint4 v = *reinterpret_cast<const uint4*>(stg + k * kOutPitch + 8 * lane_e);
-            *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(row) * Hq + wg0_e * 16 + k) * kDl +
-                                      8 * lane_e) = v;
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const u32x4*>(stg + k * kOutPitch + 8 * lane_e),
+                reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(row) * Hq + wg0_e * 16 + k) * kDl +
+                                         8 * lane_e));
         }
         return;
     }
